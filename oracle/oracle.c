@@ -1,0 +1,159 @@
+/*
+ * oracle.c -- the oracle for the KV-cache buffered-copy path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or helper with
+ * the HIP library: every index below is written out here from the
+ * definitions, in plain scalar loops, one 16-bit element at a time.
+ *
+ * What it computes (sources are the pages this project follows):
+ *
+ *  - "DejaVu: KV-Cache Streaming for Fast, Fault-Tolerant Generative LLM
+ *    Serving" (papercache.org summary), section "Method details":
+ *      * DejaVuLib implementation, Fig 6 -- the KV cache is preallocated at
+ *        the maximum sequence length, and each generated token updates a
+ *        small, non-contiguous part of the key cache;
+ *      * Buffered copies, Fig 7a -- the small updates are aggregated into one
+ *        contiguous temporary buffer in GPU memory, which is then copied out
+ *        once it is filled;
+ *      * Layer-by-layer prompt cache streaming, Fig 7b -- prompt KV is moved
+ *        one layer at a time;
+ *      * Table 1 -- scatter/gather break a non-contiguous KV region into
+ *        contiguous transfers;
+ *      * Microbatch swapping workflow, Fig 9 -- swap-out moves cache contents
+ *        to CPU memory and swap-in brings them back.
+ *  - lsln.cn article on decode-only inference, section "KV Cache capacity":
+ *    the KV bytes of B rows, S tokens, H heads of D dims, P bytes per element
+ *    and N layers are 2 x B x S x H x D x P x N.
+ *
+ * Readings taken where the pages are silent (each is also listed in the
+ * design notes):
+ *  - Cache layouts: key [L,B,H,D/8,Smax,8], value [L,B,H,Smax,D]; an element
+ *    is 16 bits (fp16 or bf16, moved as raw bits, never converted).
+ *  - Packed (staging) order: the selected elements in lexicographic order of
+ *    (layer, K before V, row b, head h, token t, dim d).  With
+ *    T = sum_b count_b and rowoff_b = sum_{b'<b} count_b', element
+ *    (l, kv, b, h, t, d) sits at
+ *        ((l-l0)*2 + kv)*(H*T*D) + (H*rowoff_b + h*count_b + t)*D + d.
+ *    The pages print no staged buffer, so this order is a reading; what pins
+ *    the oracle is this definition (brute-force coordinate decoding, numpy
+ *    transposes, the size closed form and round-trip identity in the tests).
+ *  - Prompt-layer range: row b moves tokens [tok_begin, tok_begin+tok_count)
+ *    clipped to [0, row_len_b).
+ *  - Ring restore: slots are unpacked in ascending step order, so a later
+ *    step wins when two steps name the same position.
+ *
+ * Every function here is plain C99, single-threaded.
+ */
+#include <stdint.h>
+#include <stddef.h>
+
+/* Element offset of K(l,b,h,s,d) in the key layout [L,B,H,D/8,Smax,8]. */
+int64_t oracle_key_offset(int64_t L, int64_t B, int64_t H, int64_t D, int64_t Smax,
+                          int64_t l, int64_t b, int64_t h, int64_t s, int64_t d)
+{
+    (void)L;
+    int64_t chunk = d / 8;   /* which 8-element (16-byte) vector of the head */
+    int64_t lane = d % 8;    /* element inside that vector */
+    return ((((l * B + b) * H + h) * (D / 8) + chunk) * Smax + s) * 8 + lane;
+}
+
+/* Element offset of V(l,b,h,s,d) in the value layout [L,B,H,Smax,D]. */
+int64_t oracle_value_offset(int64_t L, int64_t B, int64_t H, int64_t D, int64_t Smax,
+                            int64_t l, int64_t b, int64_t h, int64_t s, int64_t d)
+{
+    (void)L;
+    return (((l * B + b) * H + h) * Smax + s) * D + d;
+}
+
+/* Number of 16-bit elements moved by one pack over `layer_count` layers:
+ * 2 (K and V) * layer_count * H * D * sum_b count_b. */
+int64_t oracle_pack_elems(int64_t H, int64_t D, int64_t layer_count,
+                          int64_t B, const int32_t *count)
+{
+    int64_t tokens = 0;
+    for (int64_t b = 0; b < B; ++b)
+        tokens += count[b];
+    return 2 * layer_count * H * D * tokens;
+}
+
+/* Gather (pack): copy the selected region of both caches into `out` in the
+ * packed order.  Rows with count 0 contribute nothing. */
+void oracle_pack(int64_t L, int64_t B, int64_t H, int64_t D, int64_t Smax,
+                 const uint16_t *key, const uint16_t *value,
+                 int64_t layer_begin, int64_t layer_count,
+                 const int32_t *start, const int32_t *count,
+                 uint16_t *out)
+{
+    int64_t o = 0;
+    for (int64_t l = layer_begin; l < layer_begin + layer_count; ++l)
+        for (int kv = 0; kv < 2; ++kv)
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t h = 0; h < H; ++h)
+                    for (int64_t t = 0; t < count[b]; ++t)
+                        for (int64_t d = 0; d < D; ++d) {
+                            int64_t s = start[b] + t;
+                            if (kv == 0)
+                                out[o] = key[oracle_key_offset(L, B, H, D, Smax, l, b, h, s, d)];
+                            else
+                                out[o] = value[oracle_value_offset(L, B, H, D, Smax, l, b, h, s, d)];
+                            ++o;
+                        }
+}
+
+/* Scatter (unpack): the inverse of oracle_pack.  Writes exactly the selected
+ * elements of the caches from `in`; every other element is left as it was. */
+void oracle_unpack(int64_t L, int64_t B, int64_t H, int64_t D, int64_t Smax,
+                   uint16_t *key, uint16_t *value,
+                   int64_t layer_begin, int64_t layer_count,
+                   const int32_t *start, const int32_t *count,
+                   const uint16_t *in)
+{
+    int64_t o = 0;
+    for (int64_t l = layer_begin; l < layer_begin + layer_count; ++l)
+        for (int kv = 0; kv < 2; ++kv)
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t h = 0; h < H; ++h)
+                    for (int64_t t = 0; t < count[b]; ++t)
+                        for (int64_t d = 0; d < D; ++d) {
+                            int64_t s = start[b] + t;
+                            if (kv == 0)
+                                key[oracle_key_offset(L, B, H, D, Smax, l, b, h, s, d)] = in[o];
+                            else
+                                value[oracle_value_offset(L, B, H, D, Smax, l, b, h, s, d)] = in[o];
+                            ++o;
+                        }
+}
+
+/* Per-row token ranges of one prompt-layer pack: tokens
+ * [tok_begin, tok_begin + tok_count) clipped to [0, row_len_b).  A NULL
+ * row_len means no clipping. */
+void oracle_prompt_ranges(int64_t B, int32_t tok_begin, int32_t tok_count,
+                          const int32_t *row_len, int32_t *start, int32_t *count)
+{
+    for (int64_t b = 0; b < B; ++b) {
+        int32_t end = tok_begin + tok_count;
+        if (row_len != NULL && row_len[b] < end)
+            end = row_len[b];
+        start[b] = tok_begin;
+        count[b] = end > tok_begin ? end - tok_begin : 0;
+    }
+}
+
+/* Ring restore: `steps` slots, each one single-token pack of all L layers
+ * (one token per row at positions pos[j*B + b]), stored back to back in
+ * step order `slot_elems` apart.  They are unpacked in ascending step order,
+ * so the later of two steps that name the same position wins. */
+void oracle_ring_restore(int64_t L, int64_t B, int64_t H, int64_t D, int64_t Smax,
+                         uint16_t *key, uint16_t *value,
+                         int64_t steps, const int32_t *pos, int64_t slot_elems,
+                         const uint16_t *host)
+{
+    int32_t one[B > 0 ? B : 1];
+    for (int64_t b = 0; b < B; ++b)
+        one[b] = 1;
+    for (int64_t j = 0; j < steps; ++j)
+        oracle_unpack(L, B, H, D, Smax, key, value, 0, L, pos + j * B, one,
+                      host + j * slot_elems);
+}

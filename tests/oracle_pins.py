@@ -1,0 +1,240 @@
+"""Pins of the oracle against facts that do not come from the oracle itself.
+
+Each check raises AssertionError on a mismatch.  ``run_all(lib)`` runs every
+check against one compiled oracle library; the test suite runs it on the real
+oracle (must pass) and, in a subprocess, on mutated copies of ``oracle.c``
+(each must fail), so that a plausible mistake anywhere in the oracle -- a
+dropped term, a wrong index, transposed operands, a wrong loop order, an
+off-by-one, a missing clip, a reversed restore order -- trips at least one pin.
+
+The pins:
+
+* brute force with coordinate-encoding values: every 16-bit word of a tiny
+  cache encodes its own (l, b, h, s, d), so each packed word can be decoded;
+  the packed buffer must list exactly the selected elements, once each, in
+  lexicographic (layer, K-before-V, row, head, token, dim) order -- which is the
+  packed-order definition -- and its length must equal the closed form
+  2 x B x S x H x D x P x N (lsln.cn decode-only article, "KV Cache capacity");
+* numpy special cases: the tiny caches are built as numpy arrays of shape
+  [L,B,H,D/8,Smax,8] and [L,B,H,Smax,D] (numpy's C order realises the layouts
+  independently of the oracle's offset code), so a range pack equals
+  ``K[l,b,h,:,s0:s0+n,:].transpose(1,0,2)`` and ``V[l,b,h,s0:s0+n,:]`` blocks;
+* round trip: unpack(pack(C)) into a zero cache reproduces C on the selected
+  region and leaves 0 elsewhere; a sentinel cache keeps its sentinel outside;
+* pack leaves the source caches untouched;
+* prompt ranges: hand-worked clip cases;
+* ring restore: the final cache holds, at every position, the value of the
+  latest step that named it (last writer wins), written out per element.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+
+import oracle
+
+TINY = (2, 3, 2, 16, 8)     # L, B, H, D, Smax: 1536 words per tensor
+
+
+def coord_caches(dims):
+    """K and V whose words encode (l,b,h,s,d); V words are offset by the K count."""
+    L, B, H, D, S = dims
+    n = L * B * H * S * D
+    assert 2 * n <= 65536
+    l, b, h, c, s, e = np.indices((L, B, H, D // 8, S, 8))
+    d = c * 8 + e
+    code = (((l * B + b) * H + h) * S + s) * D + d
+    K = code.astype(np.uint16)                       # shape [L,B,H,D/8,S,8]
+    l, b, h, s, d = np.indices((L, B, H, S, D))
+    V = (n + ((((l * B + b) * H + h) * S + s) * D + d)).astype(np.uint16)  # [L,B,H,S,D]
+    return K, V, n
+
+
+def decode(words, dims, n):
+    L, B, H, D, S = dims
+    w = words.astype(np.int64)
+    kv = (w >= n).astype(np.int64)
+    code = w - kv * n
+    l, b, h, s, d = np.unravel_index(code, (L, B, H, S, D))
+    return np.stack([l, kv, b, h, s, d], axis=1)
+
+
+def selected(dims, l0, nl, start, count):
+    L, B, H, D, S = dims
+    rows = []
+    for l in range(l0, l0 + nl):
+        for kv in (0, 1):
+            for b in range(B):
+                for h in range(H):
+                    for s in range(start[b], start[b] + count[b]):
+                        for d in range(D):
+                            rows.append((l, kv, b, h, s, d))
+    return rows
+
+
+def check_brute_force(lib, dims=TINY, cases=None):
+    L, B, H, D, S = dims
+    K, V, n = coord_caches(dims)
+    Kf, Vf = K.ravel().copy(), V.ravel().copy()
+    rng = np.random.default_rng(7)
+    if cases is None:
+        cases = []
+        # every (start, count) per row for row 0, the others random incl. empty rows
+        for s0 in range(S):
+            for c0 in range(0, S - s0 + 1):
+                st = [s0] + list(rng.integers(0, S, size=B - 1))
+                ct = [c0] + [int(rng.integers(0, S - x + 1)) for x in st[1:]]
+                l0 = int(rng.integers(0, L))
+                nl = int(rng.integers(0, L - l0 + 1))
+                cases.append((l0, nl, st, ct))
+        cases.append((0, L, [0] * B, [S] * B))
+        cases.append((1, 1, [S - 1] * B, [1] * B))
+        cases.append((0, L, [0] * B, [0] * B))
+    for l0, nl, st, ct in cases:
+        out = oracle.pack(dims, Kf, Vf, l0, nl, st, ct, lib=lib)
+        # closed form 2 x B x S x H x D x P x N (P = 2 bytes), with B x S
+        # generalised to the sum of the rows' token counts for ragged rows
+        tokens = int(np.sum(ct))
+        assert out.size * 2 == 2 * tokens * H * D * 2 * nl, "size != closed form"
+        if len(set(ct)) == 1:
+            assert out.size * 2 == 2 * B * ct[0] * H * D * 2 * nl
+        got = decode(out, dims, n)
+        want = np.array(selected(dims, l0, nl, st, ct), dtype=np.int64).reshape(-1, 6)
+        assert got.shape == want.shape, "wrong number of packed words"
+        # lexicographic order of the selected set == the packed-order definition
+        assert np.array_equal(got, want), f"packed order/selection wrong for {(l0, nl, st, ct)}"
+    assert np.array_equal(Kf, K.ravel()) and np.array_equal(Vf, V.ravel()), "pack wrote its input"
+
+
+def numpy_pack(K6, V5, l0, nl, start, count):
+    parts = []
+    L, B, H = K6.shape[:3]
+    for l in range(l0, l0 + nl):
+        for b in range(B):
+            for h in range(H):
+                s0, c = start[b], count[b]
+                parts.append(K6[l, b, h, :, s0:s0 + c, :].transpose(1, 0, 2).ravel())
+        for b in range(B):
+            for h in range(H):
+                s0, c = start[b], count[b]
+                parts.append(V5[l, b, h, s0:s0 + c, :].ravel())
+    return np.concatenate(parts) if parts else np.zeros(0, np.uint16)
+
+
+def check_numpy(lib, dims=(3, 2, 3, 24, 11), seeds=range(12)):
+    L, B, H, D, S = dims
+    rng = np.random.default_rng(11)
+    K = rng.integers(0, 1 << 16, size=(L, B, H, D // 8, S, 8), dtype=np.uint32).astype(np.uint16)
+    V = rng.integers(0, 1 << 16, size=(L, B, H, S, D), dtype=np.uint32).astype(np.uint16)
+    Kf, Vf = K.ravel(), V.ravel()
+    for seed in seeds:
+        r = np.random.default_rng(seed)
+        st = r.integers(0, S, size=B).astype(np.int32)
+        ct = np.array([int(r.integers(0, S - x + 1)) for x in st], dtype=np.int32)
+        l0 = int(r.integers(0, L))
+        nl = int(r.integers(1, L - l0 + 1))
+        out = oracle.pack(dims, Kf, Vf, l0, nl, st, ct, lib=lib)
+        assert np.array_equal(out, numpy_pack(K, V, l0, nl, st, ct)), "pack != numpy transpose"
+    # full range of one layer = the layer's K transposed to token-major, then V
+    for l in range(L):
+        out = oracle.pack(dims, Kf, Vf, l, 1, [0] * B, [S] * B, lib=lib)
+        want = np.concatenate([K[l].transpose(0, 1, 3, 2, 4).ravel(), V[l].ravel()])
+        assert np.array_equal(out, want), "full-layer pack != transpose"
+    # decode step: one token per row
+    pos = [S - 1, 3]
+    out = oracle.pack(dims, Kf, Vf, 0, L, pos, [1] * B, lib=lib)
+    want = []
+    for l in range(L):
+        want += [K[l, b, h, :, pos[b], :].ravel() for b in range(B) for h in range(H)]
+        want += [V[l, b, h, pos[b], :] for b in range(B) for h in range(H)]
+    assert np.array_equal(out, np.concatenate(want)), "decode pack != numpy"
+
+
+def check_round_trip(lib, dims=(2, 3, 2, 32, 9)):
+    L, B, H, D, S = dims
+    rng = np.random.default_rng(5)
+    K = rng.integers(0, 1 << 16, size=(L, B, H, D // 8, S, 8), dtype=np.uint32).astype(np.uint16)
+    V = rng.integers(0, 1 << 16, size=(L, B, H, S, D), dtype=np.uint32).astype(np.uint16)
+    for seed in range(10):
+        r = np.random.default_rng(100 + seed)
+        st = r.integers(0, S, size=B).astype(np.int32)
+        ct = np.array([int(r.integers(0, S - x + 1)) for x in st], dtype=np.int32)
+        l0 = int(r.integers(0, L))
+        nl = int(r.integers(0, L - l0 + 1))
+        packed = oracle.pack(dims, K.ravel(), V.ravel(), l0, nl, st, ct, lib=lib)
+        mk = np.zeros(K.shape, bool)
+        mv = np.zeros(V.shape, bool)
+        for b in range(B):
+            mk[l0:l0 + nl, b, :, :, st[b]:st[b] + ct[b], :] = True
+            mv[l0:l0 + nl, b, :, st[b]:st[b] + ct[b], :] = True
+        for fill in (0, 0xBEEF):
+            K2 = np.full(K.shape, fill, np.uint16)
+            V2 = np.full(V.shape, fill, np.uint16)
+            k2, v2 = K2.reshape(-1), V2.reshape(-1)
+            oracle.unpack(dims, k2, v2, l0, nl, st, ct, packed, lib=lib)
+            assert np.array_equal(K2[mk], K[mk]) and np.array_equal(V2[mv], V[mv]), \
+                "round trip lost data"
+            assert np.all(K2[~mk] == fill) and np.all(V2[~mv] == fill), \
+                "unpack wrote outside the selected region"
+
+
+def check_prompt_ranges(lib):
+    # hand-worked: a 4096-token chunk starting at 4096 over rows of these lengths
+    st, ct = oracle.prompt_ranges(4, 4096, 4096, [3000, 5000, 9000, 8192], lib=lib)
+    assert list(st) == [4096] * 4 and list(ct) == [0, 904, 4096, 4096], (st, ct)
+    st, ct = oracle.prompt_ranges(3, 0, 1000, None, lib=lib)
+    assert list(ct) == [1000, 1000, 1000]
+    st, ct = oracle.prompt_ranges(3, 10, 5, [0, 12, 15], lib=lib)
+    assert list(ct) == [0, 2, 5]
+
+
+def check_ring(lib, dims=(2, 2, 2, 16, 6)):
+    L, B, H, D, S = dims
+    rng = np.random.default_rng(9)
+    steps = 7
+    pos = np.array([[j % S, (2 * j + 1) % S] for j in range(steps)], dtype=np.int32)
+    pos[5] = pos[1]                              # a later step names an earlier position
+    caches, slots = [], []
+    for j in range(steps):                      # the cache changes between steps
+        K = rng.integers(0, 1 << 16, size=(L, B, H, D // 8, S, 8), dtype=np.uint32).astype(np.uint16)
+        V = rng.integers(0, 1 << 16, size=(L, B, H, S, D), dtype=np.uint32).astype(np.uint16)
+        caches.append((K, V))
+        slots.append(oracle.pack(dims, K.ravel(), V.ravel(), 0, L, pos[j], [1] * B, lib=lib))
+    host = oracle.ring_host(slots)
+    K2 = np.zeros((L, B, H, D // 8, S, 8), np.uint16)
+    V2 = np.zeros((L, B, H, S, D), np.uint16)
+    oracle.ring_restore(dims, K2.reshape(-1), V2.reshape(-1), pos, host, lib=lib)
+    for b in range(B):
+        for p in range(S):
+            named = [j for j in range(steps) if pos[j, b] == p]
+            if not named:
+                assert not K2[:, b, :, :, p, :].any() and not V2[:, b, :, p, :].any()
+                continue
+            K, V = caches[max(named)]
+            assert np.array_equal(K2[:, b, :, :, p, :], K[:, b, :, :, p, :]), "ring: not last writer"
+            assert np.array_equal(V2[:, b, :, p, :], V[:, b, :, p, :]), "ring: not last writer"
+
+
+def check_offsets(lib, dims=(2, 3, 2, 16, 5)):
+    """The exported offset functions agree with numpy's C-order index of the layouts."""
+    L, B, H, D, S = dims
+    for l, b, h, s, d in itertools.product(range(L), range(B), range(H), range(S), range(D)):
+        k = oracle.key_offset(dims, l, b, h, s, d, lib=lib)
+        v = oracle.value_offset(dims, l, b, h, s, d, lib=lib)
+        assert k == np.ravel_multi_index((l, b, h, d // 8, s, d % 8), (L, B, H, D // 8, S, 8))
+        assert v == np.ravel_multi_index((l, b, h, s, d), (L, B, H, S, D))
+
+
+def run_all(lib):
+    check_offsets(lib)
+    check_brute_force(lib)
+    check_numpy(lib)
+    check_round_trip(lib)
+    check_prompt_ranges(lib)
+    check_ring(lib)
+
+
+if __name__ == "__main__":          # used by the mutant test: exit 0 iff every pin holds
+    import sys
+    run_all(oracle.load(sys.argv[1]))
