@@ -1,0 +1,287 @@
+/*
+ * kvstream.h -- C ABI of the MI355X KV-cache buffered-copy library.
+ *
+ * The library moves slices of a preallocated, maximum-length, strided K/V
+ * cache into a contiguous HBM staging buffer and back ("buffered copies"),
+ * and streams staged blocks to and from pinned host memory, layer by layer,
+ * for microbatch swapping, prompt-cache streaming and replication.
+ *
+ * Sources (cited by page title and section):
+ *   [DV]  "DejaVu: KV-Cache Streaming for Fast, Fault-Tolerant Generative LLM
+ *         Serving" (papercache.org summary), section "Method details":
+ *         DejaVuLib implementation (Fig 6), Buffered copies (Fig 7a),
+ *         Layer-by-layer prompt cache streaming (Fig 7b), Token computation
+ *         and streaming parallelization (Fig 7c), DejaVuLib primitives
+ *         (Table 1), Fast prompt KV transfer, Microbatch swapping workflow
+ *         (Fig 9), Failure detection and recovery (Fig 10).
+ *   [KV]  lsln.cn article on decode-only inference, section "KV Cache
+ *         capacity": KV bytes = 2 x B x S x H x D x P x N.
+ *
+ * ---------------------------------------------------------------------------
+ * Cache layouts (16-bit elements, fp16 or bf16, moved as raw bits):
+ *   key   K[L][B][H][D/8][Smax][8]   element (l,b,h,s,d) at
+ *         ((((l*B + b)*H + h)*(D/8) + d/8)*Smax + s)*8 + d%8
+ *   value V[L][B][H][Smax][D]        element (l,b,h,s,d) at
+ *         (((l*B + b)*H + h)*Smax + s)*D + d
+ * Both are preallocated at the maximum sequence length [DV, Fig 6].  In the
+ * key layout a token's D values of one head are D/8 separate 16-byte vectors
+ * Smax*16 bytes apart, which is why a decode step touches a small,
+ * non-contiguous part of the key cache [DV, Fig 6].
+ *
+ * Packed (staging) format -- the layout of every staging buffer and host
+ * image this library writes or reads.  For a layer range [l0, l0+nl) and
+ * per-row token ranges [start_b, start_b + count_b), let T = sum_b count_b
+ * and rowoff_b = sum_{b'<b} count_b'.  Element (l, kv, b, h, t, d), kv = 0
+ * for K and 1 for V, t in [0, count_b), comes from cache position
+ * s = start_b + t and sits at staging element
+ *     ((l - l0)*2 + kv)*(H*T*D) + (H*rowoff_b + h*count_b + t)*D + d.
+ * That is: layer-major; within a layer the K block then the V block; each
+ * block [b][h][t][d] with d contiguous.  Its size is
+ *     2 * nl * H * D * P * T bytes,
+ * which for uniform rows (T = B*S) is the closed form 2 x B x S x H x D x P x N
+ * of [KV].  The pages print no staged buffer; this order is the reading this
+ * library fixes.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions for every call:
+ *   - The caller owns all memory: caches, staging banks, pinned host buffers,
+ *     streams and events.  The library allocates only its handle structs
+ *     and the hipEvents inside them; it never allocates data memory.
+ *   - Device pointers (caches, staging, banks) must be device memory and
+ *     16-byte aligned; host images must be pinned host memory (e.g. from
+ *     hipHostMalloc).  Staging must not overlap either cache.
+ *   - Per-row arrays (start, count, pos, row_len) are host int32[B], read
+ *     during the call only.  B <= KV_MAX_ROWS.
+ *   - Every call validates synchronously.  On error it returns a negative
+ *     kv_status, enqueues nothing, and sets the thread-local kv_last_error().
+ *   - On success it returns once the work is enqueued (asynchronous).  Buffers
+ *     must stay alive until the stream (or the `done` event) passes them.
+ *   - No C++ exception crosses this ABI.  Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Handles are not thread-safe; distinct handles may be used concurrently.
+ */
+#ifndef KVSTREAM_H
+#define KVSTREAM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KV_VERSION 1
+#define KV_MAX_ROWS 256          /* rows per call: per-row ranges travel in kernel arguments */
+#define KV_MAX_HEAD_DIM 1024
+
+typedef enum kv_status {
+    KV_OK = 0,
+    KV_EINVAL = -1,   /* bad argument: dims, dtype, NULL, misaligned, not device / not pinned, overlap */
+    KV_ERANGE = -2,   /* layer outside [0,L) or a token range outside [0,Smax) */
+    KV_ESIZE = -3,    /* a destination or bank smaller than required */
+    KV_EHIP = -4,     /* a HIP runtime call failed; detail in kv_last_error() */
+    KV_EBUSY = -5     /* handle state does not allow the call (e.g. restore before flush) */
+} kv_status;
+
+typedef enum kv_dtype { KV_F16 = 0, KV_BF16 = 1 } kv_dtype;
+
+/* Cache-layout descriptor, filled by kv_layout_init [DV, Fig 6]. */
+typedef struct kv_layout {
+    int32_t L, B, H, D, Smax, dtype;
+    int32_t elem_bytes;        /* P = 2 */
+    int32_t vec_elems;         /* x = 8 elements per 16-byte key vector */
+    int64_t k_strides[6];      /* element strides of K [L,B,H,D/8,Smax,8] */
+    int64_t v_strides[5];      /* element strides of V [L,B,H,Smax,D] */
+    int64_t k_bytes, v_bytes;  /* bytes of each cache tensor */
+    uint32_t magic;            /* set by kv_layout_init; checked by every call */
+    uint32_t reserved;
+} kv_layout;
+
+/* Layout descriptor of a cache preallocated at the maximum sequence length
+ * [DV, Fig 6].  Pure host call.  Requires L, B, H, D, Smax > 0, D % 8 == 0,
+ * D <= KV_MAX_HEAD_DIM, B <= KV_MAX_ROWS, dtype a kv_dtype, byte sizes
+ * that fit int64, and B * Smax and Smax * D/8 below 2^31.  Returns KV_OK or
+ * KV_EINVAL. */
+int kv_layout_init(kv_layout *out, int32_t L, int32_t B, int32_t H, int32_t D,
+                   int32_t Smax, int32_t dtype);
+
+/* Bytes of one packed block over `layer_count` layers:
+ * 2 * layer_count * H * D * P * sum_b count_b -- the closed form
+ * 2 x B x S x H x D x P x N of [KV] for uniform rows.  `count` NULL means
+ * every row moves `uniform_count` tokens.  Pure host call; returns the byte
+ * count, or a negative kv_status on bad arguments. */
+int64_t kv_pack_bytes(const kv_layout *lay, int32_t layer_count,
+                      const int32_t *count, int32_t uniform_count);
+
+/* Gather ("buffered copy", [DV, Buffered copies, Fig 7a]; gather in Table 1):
+ * copy, for layers [layer_begin, layer_begin+layer_count) and each row b,
+ * tokens [start_b, start_b + count_b) of both caches into `staging` in the
+ * packed format.  `count` NULL means one token per row (a decode step,
+ * [DV, Fig 6]).  count_b = 0 skips a row.  Requires start_b >= 0 and
+ * start_b + count_b <= Smax (else KV_ERANGE), staging_bytes >=
+ * kv_pack_bytes (else KV_ESIZE).  Reads the caches, writes exactly
+ * kv_pack_bytes bytes of staging, on stream `s`. */
+int kv_pack_tokens(const kv_layout *lay, const void *k, const void *v,
+                   int32_t layer_begin, int32_t layer_count,
+                   const int32_t *start, const int32_t *count,
+                   void *staging, int64_t staging_bytes, hipStream_t s);
+
+/* Scatter (the destination side of a buffered copy, [DV, Fig 7a]; scatter in
+ * Table 1): the exact inverse of kv_pack_tokens.  Writes each packed element
+ * of `staging` to its cache position and writes no other cache element.
+ * Same arguments, checks and errors as kv_pack_tokens. */
+int kv_unpack_tokens(const kv_layout *lay, void *k, void *v,
+                     int32_t layer_begin, int32_t layer_count,
+                     const int32_t *start, const int32_t *count,
+                     const void *staging, int64_t staging_bytes, hipStream_t s);
+
+/* One prompt layer ([DV, Layer-by-layer prompt cache streaming, Fig 7b]):
+ * layer `layer`, every row, tokens [tok_begin, tok_begin + tok_count) clipped
+ * to [0, row_len_b) (`row_len` NULL: no clip).  Same packed format as
+ * kv_pack_tokens with layer_count = 1.  A chunked prompt (fixed-size token
+ * chunks) is a sequence of calls with advancing tok_begin.  Requires
+ * 0 <= tok_begin, tok_count >= 0, tok_begin + tok_count <= Smax and
+ * 0 <= row_len_b <= Smax (else KV_ERANGE). */
+int kv_pack_prompt_layer(const kv_layout *lay, const void *k, const void *v,
+                         int32_t layer, int32_t tok_begin, int32_t tok_count,
+                         const int32_t *row_len, void *staging, int64_t staging_bytes,
+                         hipStream_t s);
+
+/* Inverse of kv_pack_prompt_layer (loading a streamed prompt layer into the
+ * token-side cache, [DV, Fast prompt KV transfer]). */
+int kv_unpack_prompt_layer(const kv_layout *lay, void *k, void *v,
+                           int32_t layer, int32_t tok_begin, int32_t tok_count,
+                           const int32_t *row_len, const void *staging, int64_t staging_bytes,
+                           hipStream_t s);
+
+/* ---------------------------------------------------------------------------
+ * Swap engine: staged, layer-pipelined transfers between a cache and pinned
+ * host memory ([DV, Microbatch swapping workflow, Fig 9]; flush/fetch in
+ * Table 1, local leg).  Two caller-owned device banks alternate: the pack of
+ * chunk i+1 overlaps the device-to-host copy of chunk i; a bank is reused
+ * only after the copy that read it (or the unpack that read it) completes,
+ * enforced with events on the GPU, never by host waits.  Chunks are whole
+ * layers when a layer fits a bank (several layers per chunk when they fit),
+ * otherwise row ranges of one layer (the K part and the V part of a row
+ * range are then two copies).  A single (layer, row) block must fit a bank
+ * (else KV_ESIZE).  Copies run on the caller's `copy` stream.
+ */
+typedef struct kv_swap kv_swap;
+
+int kv_swap_create(kv_swap **out, const kv_layout *lay, void *bank0, void *bank1,
+                   int64_t bank_bytes, hipStream_t copy);
+int kv_swap_destroy(kv_swap *e);
+
+/* Swap-out: pack the selected region (kernels on `compute`, so they see the
+ * cache as of the call) and copy it to `host` (pinned) on the copy stream.
+ * The host bytes are identical to one kv_pack_tokens over the whole layer
+ * range.  `done` (nullable) is recorded on the copy stream after the last
+ * copy: the host image is valid once it completes.  Later work on `compute`
+ * may overwrite the cache as soon as it runs: the packs precede it there. */
+int kv_swap_out(kv_swap *e, const void *k, const void *v,
+                int32_t layer_begin, int32_t layer_count,
+                const int32_t *start, const int32_t *count,
+                void *host, int64_t host_bytes, hipStream_t compute, hipEvent_t done);
+
+/* Swap-in: copy `host` (pinned, packed format) to the banks on the copy
+ * stream, ordered after all work enqueued on `compute` before the call, and
+ * unpack it into the caches on `compute`.  `done` (nullable) is recorded on
+ * `compute` after the last unpack; later work on `compute` sees the restored
+ * cache. */
+int kv_swap_in(kv_swap *e, void *k, void *v,
+               int32_t layer_begin, int32_t layer_count,
+               const int32_t *start, const int32_t *count,
+               const void *host, int64_t host_bytes, hipStream_t compute, hipEvent_t done);
+
+/* Layer-by-layer prompt streaming ([DV, Fig 7b; Fast prompt KV transfer]):
+ * pack one prompt layer (as kv_pack_prompt_layer) into the next bank on
+ * `compute` and copy it to `host` on the copy stream, so that streaming layer
+ * l overlaps the computation of layer l+1.  `done` as in kv_swap_out. */
+int kv_stream_prompt_layer(kv_swap *e, const void *k, const void *v,
+                           int32_t layer, int32_t tok_begin, int32_t tok_count,
+                           const int32_t *row_len, void *host, int64_t host_bytes,
+                           hipStream_t compute, hipEvent_t done);
+
+/* Host-only view of the swap engine's chunking, for inspection and tests.
+ * Fills up to `max_chunks` entries and returns the number of chunks (may
+ * exceed max_chunks), or a negative kv_status. */
+typedef struct kv_chunk {
+    int32_t layer_begin, layer_count;  /* layers of this chunk */
+    int32_t row_begin, row_end;        /* rows [row_begin, row_end) */
+    int64_t staged_bytes;              /* bytes packed into the bank */
+    int32_t pieces;                    /* contiguous copies: 1 or 2 */
+    int32_t reserved;
+    int64_t host_off[2], bank_off[2], bytes[2];
+} kv_chunk;
+
+int64_t kv_swap_plan(const kv_layout *lay, int32_t layer_begin, int32_t layer_count,
+                     const int32_t *start, const int32_t *count, int64_t bank_bytes,
+                     kv_chunk *out, int64_t max_chunks);
+
+/* ---------------------------------------------------------------------------
+ * Staging ring for decode steps ([DV, Buffered copies, Fig 7a; Token
+ * computation and streaming parallelization, Fig 7c]).  Step j (0-based)
+ * packs one token per row, at pos[b], of all L layers into slot j mod R of
+ * bank (j / R) mod 2.  When a bank's R slots are filled the bank is copied
+ * to host offset j0 * slot_bytes (j0 = its first unflushed step) in one
+ * contiguous copy on the copy stream; the host image therefore holds the
+ * slots in step order.  A push that reuses a bank waits, on the GPU, for
+ * that bank's previous copy.  slot_bytes = 2 * L * H * D * P * B.
+ */
+typedef struct kv_ring kv_ring;
+
+/* bank_bytes must hold R slots; host_bytes bounds the steps that can be
+ * pushed (steps * slot_bytes). */
+int kv_ring_create(kv_ring **out, const kv_layout *lay, int32_t R,
+                   void *bank0, void *bank1, int64_t bank_bytes,
+                   void *host, int64_t host_bytes, hipStream_t copy);
+int kv_ring_destroy(kv_ring *r);
+
+/* One decode step: pos is int32[B], every pos_b in [0, Smax). */
+int kv_ring_push(kv_ring *r, const void *k, const void *v, const int32_t *pos,
+                 hipStream_t compute);
+
+/* Copy the filled but unflushed slots (a final partial bank) to the host.
+ * `done` (nullable) is recorded on the copy stream after every copy so far:
+ * the whole host image is valid once it completes. */
+int kv_ring_flush(kv_ring *r, hipStream_t compute, hipEvent_t done);
+
+/* Restore ([DV, Failure detection and recovery, Fig 10], data leg): copy the
+ * host image back through the banks and unpack every step into (k, v) in
+ * ascending step order (a later step wins where two name the same position).
+ * Requires every pushed step flushed (else KV_EBUSY).  `done` (nullable) is
+ * recorded on `compute` after the last unpack. */
+int kv_ring_restore(kv_ring *r, void *k, void *v, hipStream_t compute, hipEvent_t done);
+
+/* Steps pushed so far, or a negative kv_status. */
+int64_t kv_ring_steps(const kv_ring *r);
+
+/* Forget all steps (the host image and banks are reused from step 0). */
+int kv_ring_reset(kv_ring *r);
+
+/* ---------------------------------------------------------------------------
+ * Live kernel timing.  Between kv_profile_begin and kv_profile_end every pack
+ * and unpack kernel the library launches is bracketed by hipEvents on its
+ * own stream.  kv_profile_end waits for those events, fills up to `max`
+ * per-kernel entries and returns the number of distinct kernels.  `bytes`
+ * is the algorithmic HBM traffic: payload read plus payload written.
+ */
+typedef struct kv_kernel_stat {
+    char name[40];
+    int64_t launches;
+    double ms;          /* summed kernel duration */
+    int64_t bytes;      /* summed algorithmic bytes (read + write) */
+} kv_kernel_stat;
+
+int kv_profile_begin(void);
+int kv_profile_end(kv_kernel_stat *out, int32_t max);
+
+/* Thread-local text of the last error; never NULL. */
+const char *kv_last_error(void);
+int kv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSTREAM_H */

@@ -1,0 +1,405 @@
+"""Python binding of ``libkvstream.so``, the MI355X KV-cache buffered-copy library.
+
+Argument marshalling only: every function here forwards to the C entry point
+of the same name (declared in ``include/kvstream.h``); all data movement
+runs in the library's HIP kernels and copy streams.  Buffers may be passed as
+torch tensors (their ``data_ptr()`` is used), as raw integer addresses, or as
+numpy arrays for host-side per-row arguments.  Streams may be passed as
+``torch.cuda.Stream`` objects, raw ``hipStream_t`` integers, or ``None`` (the
+current torch stream).
+
+The library must be built (``kv_cache_streaming_amd._build.build()``); importing
+this package raises ``ImportError`` when it is missing -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvstream.so")
+
+KV_OK, KV_EINVAL, KV_ERANGE, KV_ESIZE, KV_EHIP, KV_EBUSY = 0, -1, -2, -3, -4, -5
+KV_F16, KV_BF16 = 0, 1
+KV_MAX_ROWS = 256
+STATUS_NAMES = {0: "KV_OK", -1: "KV_EINVAL", -2: "KV_ERANGE", -3: "KV_ESIZE",
+                -4: "KV_EHIP", -5: "KV_EBUSY"}
+
+
+class KvError(RuntimeError):
+    """A library call returned a negative kv_status."""
+
+    def __init__(self, status: int, func: str, message: str):
+        self.status = status
+        self.func = func
+        super().__init__(f"{func}: {STATUS_NAMES.get(status, status)}: {message}")
+
+
+class kv_layout(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int32), ("B", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("Smax", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("elem_bytes", ctypes.c_int32), ("vec_elems", ctypes.c_int32),
+                ("k_strides", ctypes.c_int64 * 6), ("v_strides", ctypes.c_int64 * 5),
+                ("k_bytes", ctypes.c_int64), ("v_bytes", ctypes.c_int64),
+                ("magic", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+    @property
+    def dims(self):
+        return (self.L, self.B, self.H, self.D, self.Smax)
+
+
+class kv_chunk(ctypes.Structure):
+    _fields_ = [("layer_begin", ctypes.c_int32), ("layer_count", ctypes.c_int32),
+                ("row_begin", ctypes.c_int32), ("row_end", ctypes.c_int32),
+                ("staged_bytes", ctypes.c_int64), ("pieces", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("host_off", ctypes.c_int64 * 2),
+                ("bank_off", ctypes.c_int64 * 2), ("bytes", ctypes.c_int64 * 2)]
+
+
+class kv_kernel_stat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 40), ("launches", ctypes.c_int64),
+                ("ms", ctypes.c_double), ("bytes", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_LAY = ctypes.POINTER(kv_layout)
+
+# name -> (restype, argtypes), mirroring include/kvstream.h
+_SIGNATURES = {
+    "kv_version": (ctypes.c_int, []),
+    "kv_last_error": (ctypes.c_char_p, []),
+    "kv_layout_init": (ctypes.c_int, [_LAY, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "kv_pack_bytes": (_I64, [_LAY, _I32, _P, _I32]),
+    "kv_pack_tokens": (ctypes.c_int, [_LAY, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P]),
+    "kv_unpack_tokens": (ctypes.c_int, [_LAY, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P]),
+    "kv_pack_prompt_layer": (ctypes.c_int, [_LAY, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P]),
+    "kv_unpack_prompt_layer": (ctypes.c_int, [_LAY, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P]),
+    "kv_swap_create": (ctypes.c_int, [ctypes.POINTER(_P), _LAY, _P, _P, _I64, _P]),
+    "kv_swap_destroy": (ctypes.c_int, [_P]),
+    "kv_swap_out": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
+    "kv_swap_in": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
+    "kv_stream_prompt_layer": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _P]),
+    "kv_swap_plan": (_I64, [_LAY, _I32, _I32, _P, _P, _I64, _P, _I64]),
+    "kv_ring_create": (ctypes.c_int, [ctypes.POINTER(_P), _LAY, _I32, _P, _P, _I64, _P, _I64, _P]),
+    "kv_ring_destroy": (ctypes.c_int, [_P]),
+    "kv_ring_push": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "kv_ring_flush": (ctypes.c_int, [_P, _P, _P]),
+    "kv_ring_restore": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "kv_ring_steps": (_I64, [_P]),
+    "kv_ring_reset": (ctypes.c_int, [_P]),
+    "kv_profile_begin": (ctypes.c_int, []),
+    "kv_profile_end": (ctypes.c_int, [ctypes.POINTER(kv_kernel_stat), _I32]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run kv_cache_streaming_amd._build.build() "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTED = tuple(_SIGNATURES)
+
+
+def _check(status: int, func: str) -> int:
+    if status < 0:
+        raise KvError(int(status), func, _lib.kv_last_error().decode(errors="replace"))
+    return status
+
+
+def _addr(x) -> int | None:
+    """Device/host address of a tensor, array or integer (None stays None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    raise TypeError(f"cannot take the address of {type(x).__name__}")
+
+
+def _nbytes(x) -> int:
+    if hasattr(x, "untyped_storage"):
+        return x.numel() * x.element_size()
+    if isinstance(x, np.ndarray):
+        return x.nbytes
+    raise TypeError("pass the byte count explicitly for raw addresses")
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _event(e) -> int | None:
+    if e is None:
+        return None
+    if isinstance(e, int):
+        return e
+    # torch.cuda.Event creates its hipEvent lazily, on first record: record it
+    # once so that a real handle exists (the library re-records it).
+    if not e.cuda_event:
+        e.record()
+    if not e.cuda_event:
+        raise ValueError("could not obtain a hipEvent from the torch event")
+    return e.cuda_event
+
+
+class _Rows:
+    """Keeps an int32 array alive for the duration of a call."""
+
+    def __init__(self, x, B: int, name: str):
+        if x is None:
+            self.arr, self.ptr = None, None
+            return
+        a = np.ascontiguousarray(np.asarray(x, dtype=np.int32).reshape(-1))
+        if a.size != B:
+            raise ValueError(f"{name} needs {B} per-row values, got {a.size}")
+        self.arr, self.ptr = a, a.ctypes.data
+
+
+# ---------------------------------------------------------------- layout
+
+def kv_version() -> int:
+    return _lib.kv_version()
+
+
+def kv_last_error() -> str:
+    return _lib.kv_last_error().decode(errors="replace")
+
+
+def kv_layout_init(L: int, B: int, H: int, D: int, Smax: int, dtype: int = KV_F16) -> kv_layout:
+    lay = kv_layout()
+    _check(_lib.kv_layout_init(ctypes.byref(lay), L, B, H, D, Smax, dtype), "kv_layout_init")
+    return lay
+
+
+def kv_pack_bytes(lay: kv_layout, layer_count: int, count=None, uniform_count: int = 0) -> int:
+    c = _Rows(count, lay.B, "count")
+    return _check(_lib.kv_pack_bytes(ctypes.byref(lay), layer_count, c.ptr, uniform_count),
+                  "kv_pack_bytes")
+
+
+# ---------------------------------------------------------------- pack / unpack
+
+def kv_pack_tokens(lay, k, v, layer_begin, layer_count, start, count, staging,
+                   staging_bytes=None, stream=None) -> None:
+    st, ct = _Rows(start, lay.B, "start"), _Rows(count, lay.B, "count")
+    nb = _nbytes(staging) if staging_bytes is None else staging_bytes
+    _check(_lib.kv_pack_tokens(ctypes.byref(lay), _addr(k), _addr(v), layer_begin, layer_count,
+                               st.ptr, ct.ptr, _addr(staging), nb, _stream(stream)),
+           "kv_pack_tokens")
+
+
+def kv_unpack_tokens(lay, k, v, layer_begin, layer_count, start, count, staging,
+                     staging_bytes=None, stream=None) -> None:
+    st, ct = _Rows(start, lay.B, "start"), _Rows(count, lay.B, "count")
+    nb = _nbytes(staging) if staging_bytes is None else staging_bytes
+    _check(_lib.kv_unpack_tokens(ctypes.byref(lay), _addr(k), _addr(v), layer_begin, layer_count,
+                                 st.ptr, ct.ptr, _addr(staging), nb, _stream(stream)),
+           "kv_unpack_tokens")
+
+
+def kv_pack_prompt_layer(lay, k, v, layer, tok_begin, tok_count, row_len, staging,
+                         staging_bytes=None, stream=None) -> None:
+    rl = _Rows(row_len, lay.B, "row_len")
+    nb = _nbytes(staging) if staging_bytes is None else staging_bytes
+    _check(_lib.kv_pack_prompt_layer(ctypes.byref(lay), _addr(k), _addr(v), layer, tok_begin,
+                                     tok_count, rl.ptr, _addr(staging), nb, _stream(stream)),
+           "kv_pack_prompt_layer")
+
+
+def kv_unpack_prompt_layer(lay, k, v, layer, tok_begin, tok_count, row_len, staging,
+                           staging_bytes=None, stream=None) -> None:
+    rl = _Rows(row_len, lay.B, "row_len")
+    nb = _nbytes(staging) if staging_bytes is None else staging_bytes
+    _check(_lib.kv_unpack_prompt_layer(ctypes.byref(lay), _addr(k), _addr(v), layer, tok_begin,
+                                       tok_count, rl.ptr, _addr(staging), nb, _stream(stream)),
+           "kv_unpack_prompt_layer")
+
+
+def kv_swap_plan(lay, layer_begin, layer_count, start, count, bank_bytes):
+    """Chunks the swap engine would use, as a list of dicts (host-only)."""
+    st, ct = _Rows(start, lay.B, "start"), _Rows(count, lay.B, "count")
+    n = _check(_lib.kv_swap_plan(ctypes.byref(lay), layer_begin, layer_count, st.ptr, ct.ptr,
+                                 bank_bytes, None, 0), "kv_swap_plan")
+    arr = (kv_chunk * max(n, 1))()
+    _check(_lib.kv_swap_plan(ctypes.byref(lay), layer_begin, layer_count, st.ptr, ct.ptr,
+                             bank_bytes, ctypes.cast(arr, _P), n), "kv_swap_plan")
+    out = []
+    for c in arr[:n]:
+        out.append(dict(layer_begin=c.layer_begin, layer_count=c.layer_count,
+                        row_begin=c.row_begin, row_end=c.row_end, staged_bytes=c.staged_bytes,
+                        pieces=[(c.host_off[p], c.bank_off[p], c.bytes[p]) for p in range(c.pieces)]))
+    return out
+
+
+# ---------------------------------------------------------------- swap engine
+
+class KvSwap:
+    """Handle of a swap engine (kv_swap_create / kv_swap_destroy)."""
+
+    def __init__(self, lay, bank0, bank1, bank_bytes=None, copy_stream=None):
+        self.lay = lay
+        self._keep = (bank0, bank1)
+        nb = min(_nbytes(bank0), _nbytes(bank1)) if bank_bytes is None else bank_bytes
+        h = _P()
+        _check(_lib.kv_swap_create(ctypes.byref(h), ctypes.byref(lay), _addr(bank0), _addr(bank1),
+                                   nb, _stream(copy_stream)), "kv_swap_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.kv_swap_destroy(self._h)
+            self._h = None
+
+    __del__ = close
+
+    def swap_out(self, k, v, layer_begin, layer_count, start, count, host, host_bytes=None,
+                 compute=None, done=None):
+        st, ct = _Rows(start, self.lay.B, "start"), _Rows(count, self.lay.B, "count")
+        nb = _nbytes(host) if host_bytes is None else host_bytes
+        _check(_lib.kv_swap_out(self._h, _addr(k), _addr(v), layer_begin, layer_count, st.ptr,
+                                ct.ptr, _addr(host), nb, _stream(compute), _event(done)),
+               "kv_swap_out")
+
+    def swap_in(self, k, v, layer_begin, layer_count, start, count, host, host_bytes=None,
+                compute=None, done=None):
+        st, ct = _Rows(start, self.lay.B, "start"), _Rows(count, self.lay.B, "count")
+        nb = _nbytes(host) if host_bytes is None else host_bytes
+        _check(_lib.kv_swap_in(self._h, _addr(k), _addr(v), layer_begin, layer_count, st.ptr,
+                               ct.ptr, _addr(host), nb, _stream(compute), _event(done)),
+               "kv_swap_in")
+
+    def stream_prompt_layer(self, k, v, layer, tok_begin, tok_count, row_len, host,
+                            host_bytes=None, compute=None, done=None):
+        rl = _Rows(row_len, self.lay.B, "row_len")
+        nb = _nbytes(host) if host_bytes is None else host_bytes
+        _check(_lib.kv_stream_prompt_layer(self._h, _addr(k), _addr(v), layer, tok_begin,
+                                           tok_count, rl.ptr, _addr(host), nb, _stream(compute),
+                                           _event(done)), "kv_stream_prompt_layer")
+
+
+def kv_swap_create(lay, bank0, bank1, bank_bytes=None, copy_stream=None) -> KvSwap:
+    return KvSwap(lay, bank0, bank1, bank_bytes, copy_stream)
+
+
+def kv_swap_destroy(e: KvSwap) -> None:
+    e.close()
+
+
+def kv_swap_out(e: KvSwap, *args, **kw) -> None:
+    e.swap_out(*args, **kw)
+
+
+def kv_swap_in(e: KvSwap, *args, **kw) -> None:
+    e.swap_in(*args, **kw)
+
+
+def kv_stream_prompt_layer(e: KvSwap, *args, **kw) -> None:
+    e.stream_prompt_layer(*args, **kw)
+
+
+# ---------------------------------------------------------------- staging ring
+
+class KvRing:
+    """Handle of a decode-step staging ring (kv_ring_create / kv_ring_destroy)."""
+
+    def __init__(self, lay, R, bank0, bank1, host, bank_bytes=None, host_bytes=None,
+                 copy_stream=None):
+        self.lay = lay
+        self.R = R
+        self._keep = (bank0, bank1, host)
+        nb = min(_nbytes(bank0), _nbytes(bank1)) if bank_bytes is None else bank_bytes
+        hb = _nbytes(host) if host_bytes is None else host_bytes
+        h = _P()
+        _check(_lib.kv_ring_create(ctypes.byref(h), ctypes.byref(lay), R, _addr(bank0),
+                                   _addr(bank1), nb, _addr(host), hb, _stream(copy_stream)),
+               "kv_ring_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.kv_ring_destroy(self._h)
+            self._h = None
+
+    __del__ = close
+
+    def push(self, k, v, pos, compute=None):
+        p = _Rows(pos, self.lay.B, "pos")
+        _check(_lib.kv_ring_push(self._h, _addr(k), _addr(v), p.ptr, _stream(compute)),
+               "kv_ring_push")
+
+    def flush(self, compute=None, done=None):
+        _check(_lib.kv_ring_flush(self._h, _stream(compute), _event(done)), "kv_ring_flush")
+
+    def restore(self, k, v, compute=None, done=None):
+        _check(_lib.kv_ring_restore(self._h, _addr(k), _addr(v), _stream(compute), _event(done)),
+               "kv_ring_restore")
+
+    @property
+    def steps(self) -> int:
+        return _check(_lib.kv_ring_steps(self._h), "kv_ring_steps")
+
+    def reset(self):
+        _check(_lib.kv_ring_reset(self._h), "kv_ring_reset")
+
+
+def kv_ring_create(lay, R, bank0, bank1, host, bank_bytes=None, host_bytes=None,
+                   copy_stream=None) -> KvRing:
+    return KvRing(lay, R, bank0, bank1, host, bank_bytes, host_bytes, copy_stream)
+
+
+def kv_ring_destroy(r: KvRing) -> None:
+    r.close()
+
+
+def kv_ring_push(r: KvRing, *args, **kw) -> None:
+    r.push(*args, **kw)
+
+
+def kv_ring_flush(r: KvRing, *args, **kw) -> None:
+    r.flush(*args, **kw)
+
+
+def kv_ring_restore(r: KvRing, *args, **kw) -> None:
+    r.restore(*args, **kw)
+
+
+def kv_ring_steps(r: KvRing) -> int:
+    return r.steps
+
+
+def kv_ring_reset(r: KvRing) -> None:
+    r.reset()
+
+
+# ---------------------------------------------------------------- live timing
+
+def kv_profile_begin() -> None:
+    _check(_lib.kv_profile_begin(), "kv_profile_begin")
+
+
+def kv_profile_end(max_entries: int = 16):
+    """Per-kernel {name: (launches, ms, bytes)} since kv_profile_begin."""
+    arr = (kv_kernel_stat * max_entries)()
+    n = _check(_lib.kv_profile_end(arr, max_entries), "kv_profile_end")
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].ms, arr[i].bytes)
+            for i in range(min(n, max_entries))}

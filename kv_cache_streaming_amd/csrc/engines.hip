@@ -1,0 +1,627 @@
+// Staged transfers between the cache and pinned host memory: the swap engine
+// (microbatch swap-out/in and the layer-by-layer prompt streamer) and the
+// decode-step staging ring with its flush policy and restore.
+//
+// "DejaVu: KV-Cache Streaming ...", Method details: Buffered copies (Fig 7a:
+// fill a reusable device buffer, copy it out once filled), Layer-by-layer
+// prompt cache streaming (Fig 7b), Token computation and streaming
+// parallelization (Fig 7c: streaming overlaps the next step's compute on a
+// separate stream), Microbatch swapping workflow (Fig 9), Failure detection
+// and recovery (Fig 10: the replica is copied back to a fresh worker).
+//
+// Ordering is carried entirely by hipEvents between the caller's compute
+// stream and the engine's copy stream; no call waits on the host.  Each of
+// the two banks has a "free" event (after it, the bank may be overwritten)
+// and a "filled" event (after it, the bank holds the data the other stream
+// needs).
+#include "kvs_internal.h"
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+using namespace kvs;
+
+namespace {
+
+struct Chunk {
+    int32_t l0, nl, b0, b1;
+    int64_t staged;
+    int32_t pieces;
+    int64_t host_off[2], bank_off[2], bytes[2];
+};
+
+// Chunking of one swap: whole layers (as many as fit a bank) when a layer
+// fits, otherwise row groups of one layer.  Returns KV_OK or KV_ESIZE.
+int plan_chunks(const kv_layout &lay, int32_t l0, int32_t nl, const RowTable &rt,
+                int64_t bank_bytes, std::vector<Chunk> *out)
+{
+    out->clear();
+    const int64_t T = rt.off[lay.B];
+    const int64_t per_tok = (int64_t)lay.H * lay.D * lay.elem_bytes;   // one K (or V) token of a row
+    const int64_t layer_bytes = 2 * per_tok * T;
+    if (nl == 0 || T == 0)
+        return KV_OK;
+    if (layer_bytes <= bank_bytes) {
+        const int32_t per = (int32_t)std::min<int64_t>(nl, bank_bytes / layer_bytes);
+        for (int32_t l = 0; l < nl; l += per) {
+            Chunk c;
+            c.l0 = l0 + l;
+            c.nl = std::min(per, nl - l);
+            c.b0 = 0;
+            c.b1 = lay.B;
+            c.staged = c.nl * layer_bytes;
+            c.pieces = 1;
+            c.host_off[0] = l * layer_bytes;
+            c.bank_off[0] = 0;
+            c.bytes[0] = c.staged;
+            c.host_off[1] = c.bank_off[1] = c.bytes[1] = 0;
+            out->push_back(c);
+        }
+        return KV_OK;
+    }
+    for (int32_t b = 0; b < lay.B; ++b) {
+        const int64_t rb = 2 * per_tok * (rt.off[b + 1] - rt.off[b]);
+        if (rb > bank_bytes)
+            return set_error(KV_ESIZE, "row %d of one layer needs %lld bytes; banks hold %lld", b,
+                             (long long)rb, (long long)bank_bytes);
+    }
+    for (int32_t l = 0; l < nl; ++l) {
+        int32_t b0 = 0;
+        while (b0 < lay.B) {
+            int32_t b1 = b0;
+            while (b1 < lay.B &&
+                   2 * per_tok * (rt.off[b1 + 1] - rt.off[b0]) <= bank_bytes)
+                ++b1;
+            const int64_t tok = rt.off[b1] - rt.off[b0];
+            if (tok > 0) {
+                Chunk c;
+                c.l0 = l0 + l;
+                c.nl = 1;
+                c.b0 = b0;
+                c.b1 = b1;
+                c.staged = 2 * per_tok * tok;
+                c.pieces = 2;
+                c.host_off[0] = l * layer_bytes + per_tok * rt.off[b0];
+                c.host_off[1] = l * layer_bytes + per_tok * T + per_tok * rt.off[b0];
+                c.bank_off[0] = 0;
+                c.bank_off[1] = per_tok * tok;
+                c.bytes[0] = c.bytes[1] = per_tok * tok;
+                out->push_back(c);
+            }
+            b0 = b1;
+        }
+    }
+    return KV_OK;
+}
+
+// Row table of one chunk: rows outside [b0, b1) move nothing.
+void chunk_rows(const kv_layout &lay, const RowTable &rt, const Chunk &c, RowTable *sub,
+                int32_t *max_count)
+{
+    int32_t off = 0, mx = 0;
+    for (int32_t b = 0; b < lay.B; ++b) {
+        const int32_t n = (b >= c.b0 && b < c.b1) ? rt.off[b + 1] - rt.off[b] : 0;
+        sub->start[b] = n ? rt.start[b] : 0;
+        sub->off[b] = off;
+        off += n;
+        mx = std::max(mx, n);
+    }
+    sub->off[lay.B] = off;
+    *max_count = mx;
+}
+
+int check_banks_apart(void *const bank[2], int64_t bank_bytes, const kv_layout &lay,
+                      const void *k, const void *v)
+{
+    for (int b = 0; b < 2; ++b)
+        if (overlaps(bank[b], bank_bytes, k, lay.k_bytes) || overlaps(bank[b], bank_bytes, v, lay.v_bytes))
+            return set_error(KV_EINVAL, "bank%d overlaps a cache", b);
+    return KV_OK;
+}
+
+int record(hipEvent_t e, hipStream_t s, const char *what)
+{
+    const hipError_t r = hipEventRecord(e, s);
+    return r == hipSuccess ? KV_OK : hip_fail(r, what);
+}
+
+int wait(hipStream_t s, hipEvent_t e, const char *what)
+{
+    const hipError_t r = hipStreamWaitEvent(s, e, 0);
+    return r == hipSuccess ? KV_OK : hip_fail(r, what);
+}
+
+int create_events(hipEvent_t *ev, int n)
+{
+    for (int i = 0; i < n; ++i) {
+        const hipError_t r = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+        if (r != hipSuccess) {
+            for (int j = 0; j < i; ++j)
+                (void)hipEventDestroy(ev[j]);
+            return hip_fail(r, "hipEventCreateWithFlags");
+        }
+    }
+    return KV_OK;
+}
+
+}  // namespace
+
+struct kv_swap {
+    kv_layout lay;
+    void *bank[2];
+    int64_t bank_bytes;
+    hipStream_t copy;
+    hipEvent_t ev[5];            // free0, free1, filled0, filled1, call
+    bool free_valid[2];
+    int next;
+    hipEvent_t free_ev(int b) const { return ev[b]; }
+    hipEvent_t filled_ev(int b) const { return ev[2 + b]; }
+    hipEvent_t call_ev() const { return ev[4]; }
+};
+
+struct kv_ring {
+    kv_layout lay;
+    int32_t R;
+    void *bank[2];
+    int64_t bank_bytes;
+    void *host;
+    int64_t host_bytes;
+    hipStream_t copy;
+    int64_t slot_bytes;
+    int64_t steps, flushed;
+    std::vector<int32_t> pos;    // steps * B positions, in step order
+    hipEvent_t ev[5];            // free0, free1, filled0, filled1, call
+    bool wait_needed[2];         // a push must wait on free_ev before writing the bank
+    bool free_valid[2];          // free_ev has been recorded at least once
+    hipEvent_t free_ev(int b) const { return ev[b]; }
+    hipEvent_t filled_ev(int b) const { return ev[2 + b]; }
+    hipEvent_t call_ev() const { return ev[4]; }
+};
+
+namespace {
+
+int swap_out_rows(kv_swap *e, const void *k, const void *v, int32_t l0, int32_t nl,
+                  const RowTable &rt, void *host, int64_t host_bytes, hipStream_t compute,
+                  hipEvent_t done)
+{
+    const kv_layout &lay = e->lay;
+    const int64_t need = packed_bytes(lay, nl, rt.off[lay.B]);
+    int st;
+    if (host_bytes < need)
+        return set_error(KV_ESIZE, "host holds %lld bytes, %lld needed", (long long)host_bytes,
+                         (long long)need);
+    if ((st = check_pinned_host(host, need, "host")))
+        return st;
+    if ((st = check_device_buffer(k, lay.k_bytes, "key cache")))
+        return st;
+    if ((st = check_device_buffer(v, lay.v_bytes, "value cache")))
+        return st;
+    if ((st = check_banks_apart(e->bank, e->bank_bytes, lay, k, v)))
+        return st;
+    std::vector<Chunk> chunks;
+    if ((st = plan_chunks(lay, l0, nl, rt, e->bank_bytes, &chunks)))
+        return st;
+    for (const Chunk &c : chunks) {
+        const int bk = e->next;
+        e->next ^= 1;
+        if (e->free_valid[bk] && (st = wait(compute, e->free_ev(bk), "swap-out bank wait")))
+            return st;
+        RowTable sub;
+        int32_t mx;
+        chunk_rows(lay, rt, c, &sub, &mx);
+        if ((st = enqueue_copy(true, lay, k, v, c.l0, c.nl, sub, mx, e->bank[bk], compute)))
+            return st;
+        if ((st = record(e->filled_ev(bk), compute, "swap-out packed")) ||
+            (st = wait(e->copy, e->filled_ev(bk), "swap-out copy wait")))
+            return st;
+        for (int p = 0; p < c.pieces; ++p) {
+            const hipError_t r = hipMemcpyAsync((char *)host + c.host_off[p],
+                                                (const char *)e->bank[bk] + c.bank_off[p],
+                                                (size_t)c.bytes[p], hipMemcpyDeviceToHost, e->copy);
+            if (r != hipSuccess)
+                return hip_fail(r, "swap-out hipMemcpyAsync");
+        }
+        if ((st = record(e->free_ev(bk), e->copy, "swap-out copied")))
+            return st;
+        e->free_valid[bk] = true;
+    }
+    if (done && (st = record(done, e->copy, "swap-out done")))
+        return st;
+    return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_swap_create(kv_swap **out, const kv_layout *lay, void *bank0, void *bank1,
+                   int64_t bank_bytes, hipStream_t copy)
+{
+    if (out == nullptr)
+        return set_error(KV_EINVAL, "output handle pointer is NULL");
+    *out = nullptr;
+    int st = check_layout(lay);
+    if (st)
+        return st;
+    if (bank_bytes <= 0)
+        return set_error(KV_ESIZE, "bank_bytes %lld must be positive", (long long)bank_bytes);
+    if ((st = check_device_buffer(bank0, bank_bytes, "bank0")) ||
+        (st = check_device_buffer(bank1, bank_bytes, "bank1")))
+        return st;
+    if (overlaps(bank0, bank_bytes, bank1, bank_bytes))
+        return set_error(KV_EINVAL, "the two banks overlap");
+    kv_swap *e = new (std::nothrow) kv_swap();
+    if (!e)
+        return set_error(KV_EINVAL, "out of host memory for the handle");
+    e->lay = *lay;
+    e->bank[0] = bank0;
+    e->bank[1] = bank1;
+    e->bank_bytes = bank_bytes;
+    e->copy = copy;
+    e->free_valid[0] = e->free_valid[1] = false;
+    e->next = 0;
+    if ((st = create_events(e->ev, 5))) {
+        delete e;
+        return st;
+    }
+    *out = e;
+    return KV_OK;
+}
+
+int kv_swap_destroy(kv_swap *e)
+{
+    if (!e)
+        return KV_OK;
+    for (hipEvent_t ev : e->ev)
+        (void)hipEventDestroy(ev);
+    delete e;
+    return KV_OK;
+}
+
+int kv_swap_out(kv_swap *e, const void *k, const void *v, int32_t layer_begin,
+                int32_t layer_count, const int32_t *start, const int32_t *count, void *host,
+                int64_t host_bytes, hipStream_t compute, hipEvent_t done)
+{
+    if (!e)
+        return set_error(KV_EINVAL, "swap handle is NULL");
+    int st;
+    if ((st = check_layers(e->lay, layer_begin, layer_count)))
+        return st;
+    RowTable rt;
+    int32_t mx;
+    if ((st = build_rows(e->lay, start, count, &rt, &mx)))
+        return st;
+    return swap_out_rows(e, k, v, layer_begin, layer_count, rt, host, host_bytes, compute, done);
+}
+
+int kv_stream_prompt_layer(kv_swap *e, const void *k, const void *v, int32_t layer,
+                           int32_t tok_begin, int32_t tok_count, const int32_t *row_len,
+                           void *host, int64_t host_bytes, hipStream_t compute, hipEvent_t done)
+{
+    if (!e)
+        return set_error(KV_EINVAL, "swap handle is NULL");
+    const kv_layout &lay = e->lay;
+    int st;
+    if ((st = check_layers(lay, layer, 1)))
+        return st;
+    int32_t start[KV_MAX_ROWS], count[KV_MAX_ROWS];
+    if ((st = prompt_rows(lay, tok_begin, tok_count, row_len, start, count)))
+        return st;
+    RowTable rt;
+    int32_t mx;
+    if ((st = build_rows(lay, start, count, &rt, &mx)))
+        return st;
+    return swap_out_rows(e, k, v, layer, 1, rt, host, host_bytes, compute, done);
+}
+
+int kv_swap_in(kv_swap *e, void *k, void *v, int32_t layer_begin, int32_t layer_count,
+               const int32_t *start, const int32_t *count, const void *host, int64_t host_bytes,
+               hipStream_t compute, hipEvent_t done)
+{
+    if (!e)
+        return set_error(KV_EINVAL, "swap handle is NULL");
+    const kv_layout &lay = e->lay;
+    int st;
+    if ((st = check_layers(lay, layer_begin, layer_count)))
+        return st;
+    RowTable rt;
+    int32_t mx;
+    if ((st = build_rows(lay, start, count, &rt, &mx)))
+        return st;
+    const int64_t need = packed_bytes(lay, layer_count, rt.off[lay.B]);
+    if (host_bytes < need)
+        return set_error(KV_ESIZE, "host holds %lld bytes, %lld needed", (long long)host_bytes,
+                         (long long)need);
+    if ((st = check_pinned_host(host, need, "host")))
+        return st;
+    if ((st = check_device_buffer(k, lay.k_bytes, "key cache")) ||
+        (st = check_device_buffer(v, lay.v_bytes, "value cache")))
+        return st;
+    if ((st = check_banks_apart(e->bank, e->bank_bytes, lay, k, v)))
+        return st;
+    std::vector<Chunk> chunks;
+    if ((st = plan_chunks(lay, layer_begin, layer_count, rt, e->bank_bytes, &chunks)))
+        return st;
+    if (!chunks.empty()) {
+        if ((st = record(e->call_ev(), compute, "swap-in call")) ||
+            (st = wait(e->copy, e->call_ev(), "swap-in call wait")))
+            return st;
+    }
+    for (const Chunk &c : chunks) {
+        const int bk = e->next;
+        e->next ^= 1;
+        if (e->free_valid[bk] && (st = wait(e->copy, e->free_ev(bk), "swap-in bank wait")))
+            return st;
+        for (int p = 0; p < c.pieces; ++p) {
+            const hipError_t r = hipMemcpyAsync((char *)e->bank[bk] + c.bank_off[p],
+                                                (const char *)host + c.host_off[p],
+                                                (size_t)c.bytes[p], hipMemcpyHostToDevice, e->copy);
+            if (r != hipSuccess)
+                return hip_fail(r, "swap-in hipMemcpyAsync");
+        }
+        if ((st = record(e->filled_ev(bk), e->copy, "swap-in loaded")) ||
+            (st = wait(compute, e->filled_ev(bk), "swap-in unpack wait")))
+            return st;
+        RowTable sub;
+        int32_t cmx;
+        chunk_rows(lay, rt, c, &sub, &cmx);
+        if ((st = enqueue_copy(false, lay, k, v, c.l0, c.nl, sub, cmx, e->bank[bk], compute)))
+            return st;
+        if ((st = record(e->free_ev(bk), compute, "swap-in unpacked")))
+            return st;
+        e->free_valid[bk] = true;
+    }
+    if (done && (st = record(done, compute, "swap-in done")))
+        return st;
+    return KV_OK;
+}
+
+int64_t kv_swap_plan(const kv_layout *lay, int32_t layer_begin, int32_t layer_count,
+                     const int32_t *start, const int32_t *count, int64_t bank_bytes,
+                     kv_chunk *out, int64_t max_chunks)
+{
+    int st = check_layout(lay);
+    if (st)
+        return st;
+    if ((st = check_layers(*lay, layer_begin, layer_count)))
+        return st;
+    if (bank_bytes <= 0)
+        return set_error(KV_ESIZE, "bank_bytes must be positive");
+    RowTable rt;
+    int32_t mx;
+    if ((st = build_rows(*lay, start, count, &rt, &mx)))
+        return st;
+    std::vector<Chunk> chunks;
+    if ((st = plan_chunks(*lay, layer_begin, layer_count, rt, bank_bytes, &chunks)))
+        return st;
+    for (int64_t i = 0; out && i < max_chunks && i < (int64_t)chunks.size(); ++i) {
+        const Chunk &c = chunks[i];
+        kv_chunk &o = out[i];
+        std::memset(&o, 0, sizeof o);
+        o.layer_begin = c.l0;
+        o.layer_count = c.nl;
+        o.row_begin = c.b0;
+        o.row_end = c.b1;
+        o.staged_bytes = c.staged;
+        o.pieces = c.pieces;
+        for (int p = 0; p < 2; ++p) {
+            o.host_off[p] = c.host_off[p];
+            o.bank_off[p] = c.bank_off[p];
+            o.bytes[p] = c.bytes[p];
+        }
+    }
+    return (int64_t)chunks.size();
+}
+
+// ---------------------------------------------------------------------------
+// staging ring
+
+int kv_ring_create(kv_ring **out, const kv_layout *lay, int32_t R, void *bank0, void *bank1,
+                   int64_t bank_bytes, void *host, int64_t host_bytes, hipStream_t copy)
+{
+    if (out == nullptr)
+        return set_error(KV_EINVAL, "output handle pointer is NULL");
+    *out = nullptr;
+    int st = check_layout(lay);
+    if (st)
+        return st;
+    if (R <= 0)
+        return set_error(KV_EINVAL, "R=%d must be positive", R);
+    const int64_t slot = packed_bytes(*lay, lay->L, lay->B);
+    if (bank_bytes < (int64_t)R * slot)
+        return set_error(KV_ESIZE, "banks hold %lld bytes; %d slots need %lld",
+                         (long long)bank_bytes, R, (long long)R * slot);
+    if (host_bytes < 0)
+        return set_error(KV_ESIZE, "host_bytes is negative");
+    if ((st = check_device_buffer(bank0, (int64_t)R * slot, "bank0")) ||
+        (st = check_device_buffer(bank1, (int64_t)R * slot, "bank1")))
+        return st;
+    if (overlaps(bank0, (int64_t)R * slot, bank1, (int64_t)R * slot))
+        return set_error(KV_EINVAL, "the two banks overlap");
+    if ((st = check_pinned_host(host, host_bytes, "host")))
+        return st;
+    kv_ring *r = new (std::nothrow) kv_ring();
+    if (!r)
+        return set_error(KV_EINVAL, "out of host memory for the handle");
+    r->lay = *lay;
+    r->R = R;
+    r->bank[0] = bank0;
+    r->bank[1] = bank1;
+    r->bank_bytes = bank_bytes;
+    r->host = host;
+    r->host_bytes = host_bytes;
+    r->copy = copy;
+    r->slot_bytes = slot;
+    r->steps = r->flushed = 0;
+    r->wait_needed[0] = r->wait_needed[1] = false;
+    r->free_valid[0] = r->free_valid[1] = false;
+    if ((st = create_events(r->ev, 5))) {
+        delete r;
+        return st;
+    }
+    *out = r;
+    return KV_OK;
+}
+
+int kv_ring_destroy(kv_ring *r)
+{
+    if (!r)
+        return KV_OK;
+    for (hipEvent_t ev : r->ev)
+        (void)hipEventDestroy(ev);
+    delete r;
+    return KV_OK;
+}
+
+namespace {
+
+// Copy steps [first, first+n) -- all in one bank -- to the host image.
+int ring_flush_range(kv_ring *r, int64_t first, int64_t n, hipStream_t compute)
+{
+    const int bk = (int)((first / r->R) & 1);
+    const int64_t off = (first % r->R) * r->slot_bytes;
+    int st;
+    if ((st = record(r->filled_ev(bk), compute, "ring filled")) ||
+        (st = wait(r->copy, r->filled_ev(bk), "ring flush wait")))
+        return st;
+    const hipError_t e = hipMemcpyAsync((char *)r->host + first * r->slot_bytes,
+                                        (const char *)r->bank[bk] + off,
+                                        (size_t)(n * r->slot_bytes), hipMemcpyDeviceToHost, r->copy);
+    if (e != hipSuccess)
+        return hip_fail(e, "ring flush hipMemcpyAsync");
+    if ((st = record(r->free_ev(bk), r->copy, "ring flushed")))
+        return st;
+    r->wait_needed[bk] = true;
+    r->free_valid[bk] = true;
+    r->flushed = first + n;
+    return KV_OK;
+}
+
+}  // namespace
+
+int kv_ring_push(kv_ring *r, const void *k, const void *v, const int32_t *pos,
+                 hipStream_t compute)
+{
+    if (!r)
+        return set_error(KV_EINVAL, "ring handle is NULL");
+    const kv_layout &lay = r->lay;
+    if (pos == nullptr)
+        return set_error(KV_EINVAL, "pos is NULL");
+    for (int32_t b = 0; b < lay.B; ++b)
+        if (pos[b] < 0 || pos[b] >= lay.Smax)
+            return set_error(KV_ERANGE, "row %d: position %d outside [0, %d)", b, pos[b],
+                             lay.Smax);
+    if ((r->steps + 1) * r->slot_bytes > r->host_bytes)
+        return set_error(KV_ESIZE, "host image full after %lld steps", (long long)r->steps);
+    int st;
+    if ((st = check_device_buffer(k, lay.k_bytes, "key cache")) ||
+        (st = check_device_buffer(v, lay.v_bytes, "value cache")))
+        return st;
+    if ((st = check_banks_apart(r->bank, r->bank_bytes, lay, k, v)))
+        return st;
+    RowTable rt;
+    int32_t mx;
+    if ((st = build_rows(lay, pos, nullptr, &rt, &mx)))
+        return st;
+    const int64_t j = r->steps;
+    const int bk = (int)((j / r->R) & 1);
+    if (r->wait_needed[bk]) {
+        if ((st = wait(compute, r->free_ev(bk), "ring bank wait")))
+            return st;
+        r->wait_needed[bk] = false;
+    }
+    void *slot = (char *)r->bank[bk] + (j % r->R) * r->slot_bytes;
+    if ((st = enqueue_copy(true, lay, k, v, 0, lay.L, rt, mx, slot, compute)))
+        return st;
+    r->pos.insert(r->pos.end(), pos, pos + lay.B);
+    r->steps = j + 1;
+    if (r->steps % r->R == 0)
+        return ring_flush_range(r, r->flushed, r->steps - r->flushed, compute);
+    return KV_OK;
+}
+
+int kv_ring_flush(kv_ring *r, hipStream_t compute, hipEvent_t done)
+{
+    if (!r)
+        return set_error(KV_EINVAL, "ring handle is NULL");
+    int st;
+    if (r->steps > r->flushed &&
+        (st = ring_flush_range(r, r->flushed, r->steps - r->flushed, compute)))
+        return st;
+    if (done && (st = record(done, r->copy, "ring flush done")))
+        return st;
+    return KV_OK;
+}
+
+int kv_ring_restore(kv_ring *r, void *k, void *v, hipStream_t compute, hipEvent_t done)
+{
+    if (!r)
+        return set_error(KV_EINVAL, "ring handle is NULL");
+    const kv_layout &lay = r->lay;
+    if (r->flushed != r->steps)
+        return set_error(KV_EBUSY, "%lld of %lld steps are not flushed; call kv_ring_flush",
+                         (long long)(r->steps - r->flushed), (long long)r->steps);
+    int st;
+    if ((st = check_device_buffer(k, lay.k_bytes, "key cache")) ||
+        (st = check_device_buffer(v, lay.v_bytes, "value cache")))
+        return st;
+    if ((st = check_banks_apart(r->bank, r->bank_bytes, lay, k, v)))
+        return st;
+    if (r->steps > 0) {
+        if ((st = record(r->call_ev(), compute, "ring restore call")) ||
+            (st = wait(r->copy, r->call_ev(), "ring restore call wait")))
+            return st;
+    }
+    for (int64_t j0 = 0, g = 0; j0 < r->steps; j0 += r->R, ++g) {
+        const int64_t n = std::min<int64_t>(r->R, r->steps - j0);
+        const int bk = (int)(g & 1);
+        if (r->free_valid[bk] && (st = wait(r->copy, r->free_ev(bk), "ring restore bank wait")))
+            return st;
+        const hipError_t e = hipMemcpyAsync(r->bank[bk], (const char *)r->host + j0 * r->slot_bytes,
+                                            (size_t)(n * r->slot_bytes), hipMemcpyHostToDevice,
+                                            r->copy);
+        if (e != hipSuccess)
+            return hip_fail(e, "ring restore hipMemcpyAsync");
+        if ((st = record(r->filled_ev(bk), r->copy, "ring restore loaded")) ||
+            (st = wait(compute, r->filled_ev(bk), "ring restore unpack wait")))
+            return st;
+        for (int64_t j = j0; j < j0 + n; ++j) {
+            RowTable rt;
+            int32_t mx;
+            if ((st = build_rows(lay, &r->pos[j * lay.B], nullptr, &rt, &mx)))
+                return st;
+            void *slot = (char *)r->bank[bk] + (j - j0) * r->slot_bytes;
+            if ((st = enqueue_copy(false, lay, k, v, 0, lay.L, rt, mx, slot, compute)))
+                return st;
+        }
+        if ((st = record(r->free_ev(bk), compute, "ring restore unpacked")))
+            return st;
+        r->wait_needed[bk] = true;
+        r->free_valid[bk] = true;
+    }
+    if (done && (st = record(done, compute, "ring restore done")))
+        return st;
+    return KV_OK;
+}
+
+int64_t kv_ring_steps(const kv_ring *r)
+{
+    if (!r)
+        return set_error(KV_EINVAL, "ring handle is NULL");
+    return r->steps;
+}
+
+int kv_ring_reset(kv_ring *r)
+{
+    if (!r)
+        return set_error(KV_EINVAL, "ring handle is NULL");
+    if (r->steps > r->flushed)
+        return set_error(KV_EBUSY, "unflushed steps; flush before reset");
+    r->steps = r->flushed = 0;
+    r->pos.clear();
+    return KV_OK;
+}
+
+}  // extern "C"

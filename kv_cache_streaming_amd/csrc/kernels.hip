@@ -1,0 +1,295 @@
+// Pack (gather) and unpack (scatter) kernels for gfx950.
+//
+// Pure data movement: 16-byte vectors (one key vector of 8 elements, or 8
+// value elements) are the unit everywhere, loaded and stored as uint4 and
+// never converted.  No MFMA, no arithmetic on the data.
+//
+// Buffered copies ("DejaVu: KV-Cache Streaming ...", Method details, Fig 7a)
+// gather the many small non-contiguous cache pieces of a step into one
+// contiguous buffer; these kernels are that gather and its inverse.
+//
+// Two kernels:
+//  * copy_rows_small -- few tokens per row (decode steps, Fig 6): one thread
+//    per (layer, row, head, key vector c); it moves K vector c and V vector c
+//    of each of the row's tokens.  A wave covers 64/C heads, so every store
+//    instruction writes contiguous runs of C*16 bytes of the packed buffer.
+//  * copy_tiles -- many tokens per row (prompt layers, chunks, swaps): one
+//    256-thread workgroup per (layer, row, head, token tile).  V is a
+//    straight contiguous copy.  K's token range is D/8 rows ("chunks") of
+//    tile*16 contiguous bytes each, which the packed format wants token-major;
+//    the tile is loaded chunk-major (each wave reads 1 KiB contiguous),
+//    transposed at 16-byte granularity through LDS, and stored token-major
+//    (contiguous).  Unpack is the mirror image.  The LDS index is XOR-swizzled
+//    so that both the chunk-major writes and the token-major reads spread a
+//    wave's 16-byte accesses over all banks.
+#include "kvs_internal.h"
+
+#include <algorithm>
+
+namespace kvs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTileVecs = 1024;           // 16 KiB of K per tile (and 16 KiB of V)
+constexpr int kPerThread = kTileVecs / kThreads;
+constexpr int kSmallMaxTokens = 8;        // rows with at most this many tokens use copy_rows_small
+
+template <bool kPack>
+__global__ __launch_bounds__(kThreads) void copy_rows_small(Geometry g, RowTable rt)
+{
+    // flat thread id over (layer, row, head, vector); the launcher keeps it < 2^31
+    const uint32_t gid = blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t C = (uint32_t)g.C;
+    uint32_t r = gid / C;
+    const uint32_t c = gid - r * C;
+    const uint32_t h = r % (uint32_t)g.H;
+    r /= (uint32_t)g.H;
+    const uint32_t b = r % (uint32_t)g.B;
+    r /= (uint32_t)g.B;
+    if (r >= (uint32_t)g.nl)
+        return;
+    const int32_t li = (int32_t)r;
+    const int32_t off = rt.off[b];
+    const int32_t cnt = rt.off[b + 1] - off;
+    if (cnt <= 0)
+        return;
+    const int32_t s0 = rt.start[b];
+    const int64_t unit = ((int64_t)(g.l0 + li) * g.B + b) * g.H + h;
+    uint4 *kc = g.k + (unit * C + c) * g.Smax + s0;       // token t: kc[t]
+    uint4 *vc = g.v + (unit * g.Smax + s0) * C + c;       // token t: vc[t*C]
+    const int64_t blk = (int64_t)g.H * g.T * C;           // one (layer, K|V) block
+    uint4 *ks = g.stage + 2 * (int64_t)li * blk + ((int64_t)g.H * off + (int64_t)h * cnt) * C + c;
+    uint4 *vs = ks + blk;                                 // token t: ks[t*C], vs[t*C]
+
+    int32_t t = 0;
+    for (; t + 2 <= cnt; t += 2) {
+        if (kPack) {
+            const uint4 a0 = kc[t], a1 = kc[t + 1];
+            const uint4 d0 = vc[t * C], d1 = vc[(t + 1) * C];
+            ks[t * C] = a0;
+            ks[(t + 1) * C] = a1;
+            vs[t * C] = d0;
+            vs[(t + 1) * C] = d1;
+        } else {
+            const uint4 a0 = ks[t * C], a1 = ks[(t + 1) * C];
+            const uint4 d0 = vs[t * C], d1 = vs[(t + 1) * C];
+            kc[t] = a0;
+            kc[t + 1] = a1;
+            vc[t * C] = d0;
+            vc[(t + 1) * C] = d1;
+        }
+    }
+    if (t < cnt) {
+        if (kPack) {
+            const uint4 a = kc[t];
+            const uint4 d = vc[t * C];
+            ks[t * C] = a;
+            vs[t * C] = d;
+        } else {
+            const uint4 a = ks[t * C];
+            const uint4 d = vs[t * C];
+            kc[t] = a;
+            vc[t * C] = d;
+        }
+    }
+}
+
+// LDS slot of (token i, chunk c) in a tile stored token-major.  For a
+// power-of-two CT the chunk index is XOR-ed with a function of the row so
+// that 16 consecutive tokens of one chunk (chunk-major access) land in 16
+// distinct 16-byte bank groups of a 256-byte window, while the C chunks of
+// one token (token-major access) stay a permutation of one row.
+template <int CT>
+__device__ __forceinline__ int lds_slot(int i, int c, int C)
+{
+    if constexpr (CT == 0) {
+        return i * C + c;
+    } else if constexpr (CT >= 16) {
+        return i * CT + (c ^ (i & 15));
+    } else {
+        constexpr int kRowsPer256 = 16 / CT;
+        return i * CT + (c ^ ((i / kRowsPer256) & (CT - 1)));
+    }
+}
+
+template <int CT, bool kPack>
+__global__ __launch_bounds__(kThreads) void copy_tiles(Geometry g, RowTable rt)
+{
+    static_assert(kPerThread == 4, "the unrolled body below moves four vectors per thread");
+    __shared__ uint4 lds[kTileVecs];
+    const int32_t C = CT ? CT : g.C;
+    const int32_t TT = CT ? kTileVecs / CT : g.tile_tokens;
+
+    int32_t bid = blockIdx.x;
+    const int32_t tile = bid % g.tiles_per_row;
+    bid /= g.tiles_per_row;
+    const int32_t h = bid % g.H;
+    bid /= g.H;
+    const int32_t b = bid % g.B;
+    const int32_t li = bid / g.B;
+
+    const int32_t off = rt.off[b];
+    const int32_t cnt = rt.off[b + 1] - off;
+    const int32_t t0 = tile * TT;
+    if (t0 >= cnt)
+        return;
+    const int32_t nt = min(TT, cnt - t0);
+    const int32_t nvec = nt * C;
+    const int32_t s0 = rt.start[b] + t0;
+
+    const int64_t unit = ((int64_t)(g.l0 + li) * g.B + b) * g.H + h;
+    uint4 *kc = g.k + unit * C * g.Smax + s0;           // chunk c, token i: kc[c*Smax + i]
+    uint4 *vc = g.v + (unit * g.Smax + s0) * C;         // nvec contiguous vectors
+    const int64_t blk = (int64_t)g.H * g.T * C;
+    uint4 *ks = g.stage + 2 * (int64_t)li * blk + ((int64_t)g.H * off + (int64_t)h * cnt + t0) * C;
+    uint4 *vs = ks + blk;                               // both nvec contiguous vectors
+    const int tid = threadIdx.x;
+
+    // Element e = tid + p*256 of the tile is read as (chunk e/TT, token e%TT)
+    // on the cache side (chunk-major) and as (token e/C, chunk e%C) on the
+    // packed side (token-major).  Four vectors of K and four of V per thread,
+    // kept in named registers (arrays here end up in scratch).
+    uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+#define KVS_CHUNK_OK(e, c, i) ((c) < C && (i) < nt)
+    if (kPack) {
+#define KVS_LOAD(p, kk, vv)                                               \
+    {                                                                     \
+        const int e = tid + (p) * kThreads, c = e / TT, i = e % TT;       \
+        if (KVS_CHUNK_OK(e, c, i))                                        \
+            kk = kc[(int64_t)c * g.Smax + i];                             \
+        if (e < nvec)                                                     \
+            vv = vc[e];                                                   \
+    }
+        KVS_LOAD(0, k0, v0) KVS_LOAD(1, k1, v1) KVS_LOAD(2, k2, v2) KVS_LOAD(3, k3, v3)
+#undef KVS_LOAD
+#define KVS_STAGE(p, kk, vv)                                              \
+    {                                                                     \
+        const int e = tid + (p) * kThreads, c = e / TT, i = e % TT;       \
+        if (KVS_CHUNK_OK(e, c, i))                                        \
+            lds[lds_slot<CT>(i, c, C)] = kk;                              \
+        if (e < nvec)                                                     \
+            vs[e] = vv;                                                   \
+    }
+        KVS_STAGE(0, k0, v0) KVS_STAGE(1, k1, v1) KVS_STAGE(2, k2, v2) KVS_STAGE(3, k3, v3)
+#undef KVS_STAGE
+        __syncthreads();
+#define KVS_STORE(p)                                                      \
+    {                                                                     \
+        const int e = tid + (p) * kThreads;                               \
+        if (e < nvec)                                                     \
+            ks[e] = lds[lds_slot<CT>(e / C, e % C, C)];                   \
+    }
+        KVS_STORE(0) KVS_STORE(1) KVS_STORE(2) KVS_STORE(3)
+#undef KVS_STORE
+    } else {
+#define KVS_LOAD(p, kk, vv)                                               \
+    {                                                                     \
+        const int e = tid + (p) * kThreads;                               \
+        if (e < nvec) {                                                   \
+            kk = ks[e];                                                   \
+            vv = vs[e];                                                   \
+        }                                                                 \
+    }
+        KVS_LOAD(0, k0, v0) KVS_LOAD(1, k1, v1) KVS_LOAD(2, k2, v2) KVS_LOAD(3, k3, v3)
+#undef KVS_LOAD
+#define KVS_STAGE(p, kk, vv)                                              \
+    {                                                                     \
+        const int e = tid + (p) * kThreads;                               \
+        if (e < nvec) {                                                   \
+            lds[lds_slot<CT>(e / C, e % C, C)] = kk;                      \
+            vc[e] = vv;                                                   \
+        }                                                                 \
+    }
+        KVS_STAGE(0, k0, v0) KVS_STAGE(1, k1, v1) KVS_STAGE(2, k2, v2) KVS_STAGE(3, k3, v3)
+#undef KVS_STAGE
+        __syncthreads();
+#define KVS_STORE(p)                                                      \
+    {                                                                     \
+        const int e = tid + (p) * kThreads, c = e / TT, i = e % TT;       \
+        if (KVS_CHUNK_OK(e, c, i))                                        \
+            kc[(int64_t)c * g.Smax + i] = lds[lds_slot<CT>(i, c, C)];     \
+    }
+        KVS_STORE(0) KVS_STORE(1) KVS_STORE(2) KVS_STORE(3)
+#undef KVS_STORE
+    }
+#undef KVS_CHUNK_OK
+}
+
+template <bool kPack>
+hipError_t launch_tiles_rt(const Geometry &g, const RowTable &rt, int64_t blocks, hipStream_t s)
+{
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    switch (g.C) {
+    case 1: copy_tiles<1, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 2: copy_tiles<2, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 4: copy_tiles<4, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 8: copy_tiles<8, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 16: copy_tiles<16, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 32: copy_tiles<32, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 64: copy_tiles<64, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 128: copy_tiles<128, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    default: copy_tiles<0, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    }
+    return hipGetLastError();
+}
+
+int tile_tokens_for(int32_t C)
+{
+    return C >= kTileVecs ? 1 : kTileVecs / C;
+}
+
+}  // namespace
+
+int launch_copy(bool pack, const Geometry &g0, const RowTable &rt, int32_t max_count,
+                hipStream_t s)
+{
+    if (max_count <= 0 || g0.nl <= 0 || g0.T <= 0)
+        return KV_OK;
+    const bool small = max_count <= kSmallMaxTokens;
+    Geometry g = g0;
+    int64_t per_layer;
+    if (small) {
+        per_layer = ((int64_t)g.B * g.H * g.C + kThreads - 1) / kThreads;
+    } else {
+        g.tile_tokens = tile_tokens_for(g.C);
+        g.tiles_per_row = (max_count + g.tile_tokens - 1) / g.tile_tokens;
+        per_layer = (int64_t)g.B * g.H * g.tiles_per_row;
+    }
+    // A launch covers whole layers.  Keep every grid within 2^31-1 blocks and,
+    // for the small kernel, its flat thread id within 2^31.
+    const int64_t max_blocks = small ? 0x7fffffffLL / kThreads : 0x7fffffffLL;
+    const int32_t layers_per_launch =
+        (int32_t)std::max<int64_t>(1, std::min<int64_t>(g.nl, max_blocks / per_layer));
+    const char *name = small ? (pack ? "pack_rows_small" : "unpack_rows_small")
+                             : (pack ? "pack_tiles" : "unpack_tiles");
+    const int64_t blk = (int64_t)g.H * g.T * g.C;  // vectors per (layer, K|V) block
+
+    for (int32_t done = 0; done < g0.nl; done += layers_per_launch) {
+        Geometry gl = g;
+        gl.l0 = g0.l0 + done;
+        gl.nl = std::min<int32_t>(layers_per_launch, g0.nl - done);
+        gl.stage = g0.stage + 2 * (int64_t)done * blk;
+        const int64_t payload = 2 * (int64_t)gl.nl * blk * 16;
+        void *tok = profiling_enabled() ? profile_start(s) : nullptr;
+        hipError_t e;
+        if (small) {
+            const int64_t threads = (int64_t)gl.nl * gl.B * gl.H * gl.C;
+            const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads)), block(kThreads);
+            if (pack)
+                copy_rows_small<true><<<grid, block, 0, s>>>(gl, rt);
+            else
+                copy_rows_small<false><<<grid, block, 0, s>>>(gl, rt);
+            e = hipGetLastError();
+        } else {
+            const int64_t blocks = (int64_t)gl.nl * per_layer;
+            e = pack ? launch_tiles_rt<true>(gl, rt, blocks, s) : launch_tiles_rt<false>(gl, rt, blocks, s);
+        }
+        if (tok)
+            profile_stop(tok, s, name, 2 * payload);
+        if (e != hipSuccess)
+            return hip_fail(e, name);
+    }
+    return KV_OK;
+}
+
+}  // namespace kvs

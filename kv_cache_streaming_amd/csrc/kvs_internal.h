@@ -1,0 +1,70 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kvstream.h"
+
+namespace kvs {
+
+constexpr uint32_t kLayoutMagic = 0x4b565354u;  // "KVST"
+constexpr int kMaxRows = KV_MAX_ROWS;
+
+// Per-call row metadata, passed by value in the kernel arguments so that it
+// is captured at launch and needs no device allocation.
+struct RowTable {
+    int32_t start[kMaxRows];    // first cache position of row b's range
+    int32_t off[kMaxRows + 1];  // prefix sums of the counts: row b's tokens are [off[b], off[b+1])
+};
+
+// Geometry of one pack/unpack launch, in 16-byte vectors.
+struct Geometry {
+    uint4 *k;        // key cache base
+    uint4 *v;        // value cache base
+    uint4 *stage;    // packed buffer base
+    int32_t B, H, C, Smax;  // C = D/8 vectors per head row
+    int32_t l0, nl;         // layer range
+    int32_t tiles_per_row;  // tile kernel: tiles per row (ceil(max count / tile tokens))
+    int32_t tile_tokens;    // tile kernel: tokens per tile
+    int64_t T;              // sum of counts
+};
+
+// ---- errors (api.hip) ----
+int set_error(int status, const char *fmt, ...);
+int hip_fail(hipError_t e, const char *what);
+
+// ---- validation helpers (api.hip) ----
+int check_layout(const kv_layout *lay);
+int check_device_buffer(const void *p, int64_t bytes, const char *name);
+int check_pinned_host(const void *p, int64_t bytes, const char *name);
+bool overlaps(const void *a, int64_t an, const void *b, int64_t bn);
+// Validates per-row ranges and fills `rt`; returns KV_OK or an error.  `count`
+// NULL means one token per row.
+int build_rows(const kv_layout &lay, const int32_t *start, const int32_t *count, RowTable *rt,
+               int32_t *max_count);
+int check_layers(const kv_layout &lay, int32_t layer_begin, int32_t layer_count);
+int64_t packed_bytes(const kv_layout &lay, int32_t nl, int64_t tokens);
+// Per-row ranges of a prompt-layer call: [tok_begin, tok_begin+tok_count)
+// clipped to [0, row_len_b) (row_len NULL: no clip).
+int prompt_rows(const kv_layout &lay, int32_t tok_begin, int32_t tok_count,
+                const int32_t *row_len, int32_t *start, int32_t *count);
+
+// Validated pack/unpack of a whole call (used by the public entry points and
+// the engines).  Buffers are assumed checked by the caller.
+int enqueue_copy(bool pack, const kv_layout &lay, const void *k, const void *v, int32_t l0,
+                 int32_t nl, const RowTable &rt, int32_t max_count, void *stage, hipStream_t s);
+
+// ---- kernels (kernels.hip) ----
+// Launches the pack (or unpack) kernels for one call; returns KV_OK or KV_EHIP.
+int launch_copy(bool pack, const Geometry &g, const RowTable &rt, int32_t max_count,
+                hipStream_t s);
+
+// ---- profiling (api.hip) ----
+bool profiling_enabled();
+// Begin/end a bracketed launch; `tok` is opaque state handed back to profile_end.
+void *profile_start(hipStream_t s);
+void profile_stop(void *tok, hipStream_t s, const char *name, int64_t bytes);
+
+}  // namespace kvs

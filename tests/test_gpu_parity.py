@@ -1,0 +1,387 @@
+"""HIP path vs the oracle, bit for bit, at sizes the oracle finishes in seconds.
+
+Every comparison is element by element (np.array_equal on raw 16-bit words).
+Shapes span several token tiles with ragged tails, every compiled head-dim
+variant (D/8 = 1, 2, 3 (generic), 4, 8, 16, 32, 64, 128), empty rows, rows at
+the end of the cache, random bit patterns (NaN payloads, Inf, +-0, subnormals)
+and both kernels (few tokens per row and tiled).  Canaries after every staging
+buffer and sentinels around every unpacked region check that nothing outside
+the defined bytes is written.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import dev, empty, host, note, pinned, pinned_host_view
+
+pytestmark = pytest.mark.gpu
+
+CANARY = 64   # words after every staging buffer
+
+
+@pytest.fixture(scope="module")
+def kv():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+    import kv_cache_streaming_amd as kv
+    return kv
+
+
+def random_ranges(rng, B, S, max_count=None):
+    start = rng.integers(0, S, size=B)
+    count = []
+    for s in start:
+        hi = S - int(s)
+        if max_count is not None:
+            hi = min(hi, max_count)
+        count.append(int(rng.integers(0, hi + 1)))
+    return [int(x) for x in start], count
+
+
+def check_pack_unpack(kv, dims, l0, nl, start, count, seed, bits=True, dtype=0):
+    import torch
+    L, B, H, D, S = dims
+    note(f"pack/unpack dims={dims} layers=[{l0},+{nl}) start={start} count={count} seed={seed}")
+    K, V = synth.cache_pair(dims, seed, dtype=dtype, bits=bits)
+    lay = kv.kv_layout_init(L, B, H, D, S, dtype)
+    dk, dv = dev(K), dev(V)
+    want = oracle.pack(dims, K, V, l0, nl, start, count)
+    assert kv.kv_pack_bytes(lay, nl, count) == want.nbytes
+    st = empty(want.size, CANARY)
+    kv.kv_pack_tokens(lay, dk, dv, l0, nl, start, count, st, want.nbytes)
+    torch.cuda.synchronize()
+    got = host(st)
+    assert np.array_equal(got[:want.size], want), "pack differs from the oracle"
+    assert np.all(got[want.size:] == 0x7A7A), "pack wrote past kv_pack_bytes"
+    assert np.array_equal(host(dk), K) and np.array_equal(host(dv), V), "pack wrote a cache"
+    # unpack into sentinel caches; the oracle does the same on host copies
+    sk = np.full(K.size, 0xC3C3, np.uint16)
+    sv = np.full(V.size, 0x3C3C, np.uint16)
+    ek, ev = sk.copy(), sv.copy()
+    oracle.unpack(dims, ek, ev, l0, nl, start, count, want)
+    dk2, dv2 = dev(sk), dev(sv)
+    kv.kv_unpack_tokens(lay, dk2, dv2, l0, nl, start, count, st, want.nbytes)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(dk2), ek) and np.array_equal(host(dv2), ev), "unpack differs"
+    assert np.array_equal(host(st)[:want.size], want), "unpack wrote its staging input"
+
+
+@pytest.mark.parametrize("D", [8, 16, 24, 32, 64, 128, 256, 512, 1024])
+def test_tiled_ranges_every_head_dim(kv, D):
+    """Multi-token ranges (tile kernel), several tiles and a ragged tail per row."""
+    rng = np.random.default_rng(D)
+    C = D // 8
+    tile = max(1, 1024 // C)
+    S = 2 * tile + 37 if D <= 256 else 3 * tile + 5
+    dims = (3, 3, 2, D, S)
+    start = [0, 5, S - (tile + 11)]
+    count = [S, min(tile + 29, S - 5), tile + 11]
+    check_pack_unpack(kv, dims, 1, 2, start, count, seed=D)
+    for it in range(3):
+        st, ct = random_ranges(rng, 3, S)
+        ct[0] = max(ct[0], 9)        # keep the tile kernel selected
+        st[0] = min(st[0], S - ct[0])
+        check_pack_unpack(kv, dims, 0, 3, st, ct, seed=D * 10 + it)
+
+
+@pytest.mark.parametrize("D", [8, 16, 24, 64, 128, 1024])
+def test_few_tokens_every_head_dim(kv, D):
+    """Decode-like ranges (at most 8 tokens per row: the small kernel)."""
+    rng = np.random.default_rng(100 + D)
+    dims = (4, 5, 3, D, 40)
+    for it in range(4):
+        st, ct = random_ranges(rng, 5, 40, max_count=8)
+        check_pack_unpack(kv, dims, 0, 4, st, ct, seed=200 + D + it)
+    # one token per row at the last position
+    check_pack_unpack(kv, dims, 0, 4, [39] * 5, [1] * 5, seed=7)
+
+
+def test_empty_and_degenerate(kv):
+    import torch
+    dims = (2, 3, 2, 16, 12)
+    check_pack_unpack(kv, dims, 0, 2, [0, 0, 0], [0, 12, 0], seed=1)
+    check_pack_unpack(kv, dims, 1, 1, [11, 0, 5], [1, 0, 7], seed=2)
+    # zero layers and zero tokens enqueue nothing and succeed
+    L, B, H, D, S = dims
+    lay = kv.kv_layout_init(L, B, H, D, S, 0)
+    K, V = synth.cache_pair(dims, 3)
+    dk, dv = dev(K), dev(V)
+    st = empty(16)
+    kv.kv_pack_tokens(lay, dk, dv, 0, 0, [0] * B, [1] * B, st, 32)
+    kv.kv_pack_tokens(lay, dk, dv, 0, 2, [0] * B, [0] * B, st, 32)
+    torch.cuda.synchronize()
+    assert np.all(host(st) == 0x7A7A)
+
+
+def test_fp16_and_bf16_values(kv):
+    dims = (2, 2, 3, 64, 300)
+    check_pack_unpack(kv, dims, 0, 2, [0, 17], [300, 250], seed=5, bits=False, dtype=0)
+    check_pack_unpack(kv, dims, 0, 2, [3, 0], [290, 300], seed=6, bits=False, dtype=1)
+
+
+def test_prompt_layer_chunks(kv):
+    import torch
+    dims = (3, 4, 2, 32, 700)
+    L, B, H, D, S = dims
+    note(f"prompt chunks dims={dims}")
+    K, V = synth.cache_pair(dims, 11)
+    lay = kv.kv_layout_init(L, B, H, D, S, 0)
+    dk, dv = dev(K), dev(V)
+    row_len = [700, 123, 0, 333]
+    chunk = 256
+    for layer in range(L):
+        for tb in range(0, S, chunk):
+            tc = min(chunk, S - tb)
+            start, count = oracle.prompt_ranges(B, tb, tc, row_len)
+            want = oracle.pack(dims, K, V, layer, 1, start, count)
+            st = empty(max(want.size, 1), CANARY)
+            kv.kv_pack_prompt_layer(lay, dk, dv, layer, tb, tc, row_len, st, want.nbytes)
+            torch.cuda.synchronize()
+            got = host(st)
+            assert np.array_equal(got[:want.size], want)
+            assert np.all(got[max(want.size, 1):] == 0x7A7A)
+            # unpack the chunk back into a sentinel cache
+            ek = np.full(K.size, 0x1111, np.uint16)
+            ev = np.full(V.size, 0x2222, np.uint16)
+            dk2, dv2 = dev(ek), dev(ev)
+            oracle.unpack(dims, ek, ev, layer, 1, start, count, want)
+            kv.kv_unpack_prompt_layer(lay, dk2, dv2, layer, tb, tc, row_len, st, want.nbytes)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(dk2), ek) and np.array_equal(host(dv2), ev)
+
+
+def test_error_paths(kv):
+    import torch
+    dims = (2, 2, 2, 16, 8)
+    L, B, H, D, S = dims
+    lay = kv.kv_layout_init(L, B, H, D, S, 0)
+    K, V = synth.cache_pair(dims, 1)
+    dk, dv = dev(K), dev(V)
+    st = empty(4096)
+    pageable = np.zeros(8192, np.uint16)
+    note("error paths")
+    with pytest.raises(kv.KvError) as e:                    # host array passed as a cache
+        kv.kv_pack_tokens(lay, pageable, dv, 0, 1, [0, 0], [1, 1], st, 8192)
+    assert e.value.status == kv.KV_EINVAL
+    with pytest.raises(kv.KvError) as e:                    # misaligned staging
+        kv.kv_pack_tokens(lay, dk, dv, 0, 1, [0, 0], [1, 1], st.data_ptr() + 2, 4096)
+    assert e.value.status == kv.KV_EINVAL
+    with pytest.raises(kv.KvError) as e:                    # staging overlapping the key cache
+        kv.kv_pack_tokens(lay, dk, dv, 0, 1, [0, 0], [1, 1], dk, 4096)
+    assert e.value.status == kv.KV_EINVAL
+    with pytest.raises(kv.KvError) as e:                    # short staging
+        kv.kv_pack_tokens(lay, dk, dv, 0, 1, [0, 0], [2, 2], st, 255)
+    assert e.value.status == kv.KV_ESIZE
+    with pytest.raises(kv.KvError) as e:                    # position >= Smax
+        kv.kv_pack_tokens(lay, dk, dv, 0, 1, [8, 0], None, st, 8192)
+    assert e.value.status == kv.KV_ERANGE
+    torch.cuda.synchronize()
+    assert np.all(host(st) == 0x7A7A), "a rejected call wrote staging"
+    # swap engine: pageable host image, short host image
+    b0, b1 = empty(512), empty(512)
+    eng = kv.KvSwap(lay, b0, b1, 1024)
+    with pytest.raises(kv.KvError) as e:
+        eng.swap_out(dk, dv, 0, 2, [0, 0], [4, 4], pageable, pageable.nbytes)
+    assert e.value.status == kv.KV_EINVAL
+    hp = pinned(64)
+    with pytest.raises(kv.KvError) as e:
+        eng.swap_out(dk, dv, 0, 2, [0, 0], [4, 4], hp, 128)
+    assert e.value.status == kv.KV_ESIZE
+    with pytest.raises(kv.KvError) as e:                    # a bank aliasing the cache
+        kv.KvSwap(lay, dk, b1, 512).swap_out(dk, dv, 0, 1, [0, 0], [1, 1], pinned(4096), 8192)
+    assert e.value.status == kv.KV_EINVAL
+    # ring: restore before flush, full host image, bad position
+    slot = kv.kv_pack_bytes(lay, L, None, 1)
+    rb0, rb1 = empty(2 * slot // 2), empty(2 * slot // 2)
+    rh = pinned(3 * slot // 2)
+    ring = kv.KvRing(lay, 2, rb0, rb1, rh)
+    ring.push(dk, dv, [0, 1])
+    with pytest.raises(kv.KvError) as e:
+        ring.restore(dk, dv)
+    assert e.value.status == kv.KV_EBUSY
+    with pytest.raises(kv.KvError) as e:
+        ring.push(dk, dv, [0, 8])
+    assert e.value.status == kv.KV_ERANGE
+    ring.push(dk, dv, [1, 2])
+    ring.push(dk, dv, [2, 3])
+    with pytest.raises(kv.KvError) as e:
+        ring.push(dk, dv, [3, 4])
+    assert e.value.status == kv.KV_ESIZE
+    ring.flush()
+    torch.cuda.synchronize()
+    assert ring.steps == 3
+
+
+def run_ring(kv, dims, R, positions, seed, bits=True, mutate=False, delay_cycles=0):
+    """Push every step, flush, restore into a zero cache; compare with the oracle."""
+    import torch
+    L, B, H, D, S = dims
+    note(f"ring dims={dims} R={R} steps={len(positions)} mutate={mutate} delay={delay_cycles}")
+    K, V = synth.cache_pair(dims, seed, bits=bits)
+    lay = kv.kv_layout_init(L, B, H, D, S, 0)
+    dk, dv = dev(K), dev(V)
+    slot = kv.kv_pack_bytes(lay, L, None, 1)
+    banks = [empty(R * slot // 2), empty(R * slot // 2)]
+    steps = len(positions)
+    hostbuf = pinned(steps * slot // 2 + CANARY)
+    copy = torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    ring = kv.KvRing(lay, R, banks[0], banks[1], hostbuf, host_bytes=steps * slot,
+                     copy_stream=copy)
+    slots = []
+    rng = np.random.default_rng(seed)
+    if delay_cycles:
+        with torch.cuda.stream(copy):
+            torch.cuda._sleep(delay_cycles)   # a bounded spin: makes every flush copy late
+    for j, pos in enumerate(positions):
+        slots.append(oracle.pack(dims, K, V, 0, L, pos, [1] * B))
+        ring.push(dk, dv, pos, compute)
+        if mutate:
+            # the cache changes between steps (new values at random places)
+            idx = rng.integers(0, K.size, size=64)
+            K[idx] = rng.integers(0, 1 << 16, size=64).astype(np.uint16)
+            V[idx] = rng.integers(0, 1 << 16, size=64).astype(np.uint16)
+            dk.copy_(torch.from_numpy(K.view(np.int16)).cuda(), non_blocking=False)
+            dv.copy_(torch.from_numpy(V.view(np.int16)).cuda(), non_blocking=False)
+    done = torch.cuda.Event()
+    ring.flush(compute, done)
+    done.synchronize()
+    want_host = oracle.ring_host(slots)
+    got_host = pinned_host_view(hostbuf)
+    assert np.array_equal(got_host[:want_host.size], want_host), "ring host image differs"
+    assert np.all(got_host[want_host.size:] == 0x5C5C), "ring wrote past its steps"
+    zk, zv = np.zeros(K.size, np.uint16), np.zeros(V.size, np.uint16)
+    rk, rv = dev(zk), dev(zv)
+    oracle.ring_restore(dims, zk, zv, positions, want_host)
+    ring.restore(rk, rv, compute)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(rk), zk) and np.array_equal(host(rv), zv), "restore differs"
+    ring.close()
+
+
+def test_ring_decode_flow(kv):
+    dims = (3, 4, 2, 64, 50)
+    pos = [[10 + j, 20 + j, 3 + j, 40 + (j % 9)] for j in range(19)]   # 2 full banks + a partial
+    run_ring(kv, dims, 8, pos, seed=21)
+
+
+def test_ring_duplicate_positions_last_writer_wins(kv):
+    dims = (2, 3, 3, 16, 6)
+    pos = [[j % 6, (2 * j) % 6, 5] for j in range(11)]
+    run_ring(kv, dims, 4, pos, seed=22, mutate=True)
+
+
+def test_ring_bank_reuse_waits_for_a_late_flush(kv):
+    """The copy stream is held back by a bounded spin; a push that reuses a bank
+    must still wait for that bank's copy (else the host image would differ)."""
+    dims = (2, 2, 2, 32, 64)
+    pos = [[j, 63 - j] for j in range(13)]
+    run_ring(kv, dims, 2, pos, seed=23, mutate=True, delay_cycles=200_000_000)
+
+
+def run_swap(kv, dims, l0, nl, start, count, bank_bytes, seed, delay_cycles=0):
+    import torch
+    L, B, H, D, S = dims
+    note(f"swap dims={dims} layers=[{l0},+{nl}) bank={bank_bytes} delay={delay_cycles}")
+    K, V = synth.cache_pair(dims, seed, bits=True)
+    lay = kv.kv_layout_init(L, B, H, D, S, 0)
+    dk, dv = dev(K), dev(V)
+    want = oracle.pack(dims, K, V, l0, nl, start, count)
+    b0, b1 = empty(bank_bytes // 2 + 8), empty(bank_bytes // 2 + 8)
+    copy = torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    eng = kv.KvSwap(lay, b0, b1, bank_bytes, copy)
+    hostbuf = pinned(want.size + CANARY)
+    if delay_cycles:
+        with torch.cuda.stream(copy):
+            torch.cuda._sleep(delay_cycles)
+    done = torch.cuda.Event()
+    eng.swap_out(dk, dv, l0, nl, start, count, hostbuf, want.nbytes, compute, done)
+    # overwrite the source cache right away on compute: the packs precede it there
+    dk.fill_(0)
+    dv.fill_(0)
+    done.synchronize()
+    got = pinned_host_view(hostbuf)
+    assert np.array_equal(got[:want.size], want), "swap-out host image differs"
+    assert np.all(got[want.size:] == 0x5C5C)
+    # swap-in into sentinel caches
+    ek = np.full(K.size, 0x4444, np.uint16)
+    ev = np.full(V.size, 0x5555, np.uint16)
+    dk2, dv2 = dev(ek), dev(ev)
+    oracle.unpack(dims, ek, ev, l0, nl, start, count, want)
+    if delay_cycles:
+        with torch.cuda.stream(copy):
+            torch.cuda._sleep(delay_cycles)
+    done2 = torch.cuda.Event()
+    eng.swap_in(dk2, dv2, l0, nl, start, count, hostbuf, want.nbytes, compute, done2)
+    done2.synchronize()
+    assert np.array_equal(host(dk2), ek) and np.array_equal(host(dv2), ev), "swap-in differs"
+    eng.close()
+
+
+def test_swap_whole_layer_chunks(kv):
+    dims = (6, 3, 2, 64, 300)
+    layer = 2 * 2 * 64 * 2 * (300 + 250 + 17)
+    run_swap(kv, dims, 1, 5, [0, 50, 283], [300, 250, 17], 2 * layer, seed=31)
+
+
+def test_swap_row_group_chunks(kv):
+    dims = (3, 5, 2, 128, 260)
+    count = [260, 0, 100, 255, 3]
+    start = [0, 0, 160, 5, 257]
+    per_row = [2 * 2 * 128 * 2 * c for c in count]
+    run_swap(kv, dims, 0, 3, start, count, max(per_row) + 4096, seed=32)
+
+
+def test_swap_waits_for_late_copies(kv):
+    dims = (8, 2, 2, 32, 128)
+    layer = 2 * 2 * 32 * 2 * 256
+    run_swap(kv, dims, 0, 8, [0, 0], [128, 128], layer, seed=33, delay_cycles=200_000_000)
+
+
+def test_stream_prompt_layers(kv):
+    import torch
+    dims = (4, 3, 2, 64, 200)
+    L, B, H, D, S = dims
+    note(f"prompt streamer dims={dims}")
+    K, V = synth.cache_pair(dims, 41)
+    lay = kv.kv_layout_init(L, B, H, D, S, 0)
+    dk, dv = dev(K), dev(V)
+    row_len = [200, 150, 77]
+    start, count = oracle.prompt_ranges(B, 0, 180, row_len)
+    per_layer = oracle.pack(dims, K, V, 0, 1, start, count).size
+    b0, b1 = empty(per_layer), empty(per_layer)
+    copy = torch.cuda.Stream()
+    eng = kv.KvSwap(lay, b0, b1, per_layer * 2, copy)
+    hostbuf = pinned(L * per_layer + CANARY)
+    hv = pinned_host_view(hostbuf)
+    done = torch.cuda.Event()
+    for layer in range(L):
+        dst = hostbuf.data_ptr() + layer * per_layer * 2
+        eng.stream_prompt_layer(dk, dv, layer, 0, 180, row_len, dst, per_layer * 2,
+                                torch.cuda.current_stream(), done)
+    done.synchronize()
+    for layer in range(L):
+        want = oracle.pack(dims, K, V, layer, 1, start, count)
+        assert np.array_equal(hv[layer * per_layer:(layer + 1) * per_layer], want)
+    assert np.all(hv[L * per_layer:] == 0x5C5C)
+
+
+def test_profiler_counts_launches(kv):
+    import torch
+    dims = (2, 2, 2, 64, 128)
+    K, V = synth.cache_pair(dims, 51)
+    lay = kv.kv_layout_init(*dims, 0)
+    dk, dv = dev(K), dev(V)
+    st = empty(2 * 2 * 2 * 64 * 256)
+    kv.kv_profile_begin()
+    kv.kv_pack_tokens(lay, dk, dv, 0, 2, [0, 0], [128, 128], st)
+    kv.kv_pack_tokens(lay, dk, dv, 0, 2, [5, 9], None, st)
+    kv.kv_unpack_tokens(lay, dk, dv, 0, 2, [0, 0], [128, 128], st)
+    stats = kv.kv_profile_end()
+    torch.cuda.synchronize()
+    assert stats["pack_tiles"][0] == 1 and stats["pack_rows_small"][0] == 1
+    assert stats["unpack_tiles"][0] == 1
+    assert stats["pack_tiles"][2] == 2 * 2 * (2 * 2 * 2 * 64 * 256)
+    assert all(v[1] > 0 for v in stats.values())
