@@ -1,0 +1,367 @@
+"""Benchmark of the KV buffered-copy path on one MI355X.
+
+One step is one pass of the whole path over one batch of the
+GPT-2-1.5B-shaped workload (L=48, B=8, H=25, D=64, Smax=1024, fp16; prompt
+length 1000; 24 decode steps; staging ring of 8 slots):
+
+  1. prompt streaming: the 48 prompt layers of cache A are packed layer by
+     layer and copied to pinned host memory (prompt streamer);
+  2. prompt load: each layer, once its copy has landed, is copied back
+     through the banks and unpacked into cache B (swap-in), so that host->GPU
+     copies of layer l run while GPU->host copies of layer l+1 are in flight;
+  3. decode: 24 single-token packs of cache B (positions 1000..1023) into the
+     staging ring, flushed to pinned host memory every 8 steps;
+  4. restore: the ring's host image is unpacked into cache C;
+  5. microbatch swap: cache B (all 1024 positions) is swapped out layer by
+     layer to pinned host memory and swapped in to cache C, again duplex.
+
+Inputs are resident in HBM before the timed region.  `value` is the KV
+payload the step moves across the host link (both directions) per second.
+`roofline` describes the kernel with the most GPU time: algorithmic bytes
+(payload read + payload written) per launch over its average duration, both
+measured live with hipEvents bracketing every launch on its own stream.
+`cpu_baseline` is the oracle on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# The step drives four streams (two compute, one copy stream per link
+# direction) besides the default one.  HIP maps streams onto a fixed number of
+# hardware queues per process; with fewer queues than busy streams, streams
+# share a queue and their work serialises, so the two link directions never
+# overlap.  Ask for eight (must happen before the HIP runtime starts).
+if int(os.environ.get("GPU_MAX_HW_QUEUES", "0") or 0) < 8:
+    os.environ["GPU_MAX_HW_QUEUES"] = "8"
+
+METRIC = "KV pack/unpack GB/s (% HBM peak) + swap host-link GB/s, 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+PCIE_PEAK_GBPS = 63.0          # PCIe 5.0 x16, per direction
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "traffic_gpt2-1.5b.txt")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="gpt2-1.5b")
+    ap.add_argument("--swap-bank-mib", type=int, default=256)
+    ap.add_argument("--transport", choices=("auto", "kernel", "runtime", "dma"), default="auto",
+                    help="bank<->host transfers (see kv_transport in include/kvstream.h)")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="do not bracket launches with events (for external profilers)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+class Step:
+    """All buffers and handles of one workload, and the step itself."""
+
+    def __init__(self, w, swap_bank_bytes, transport=0):
+        import torch
+
+        import kv_cache_streaming_amd as kv
+        import synth
+        self.kv, self.w, self.torch = kv, w, torch
+        L, B, H, D, S = w.dims
+        self.lay = kv.kv_layout_init(L, B, H, D, S, w.dtype)
+        n = L * B * H * D * S
+        dev = torch.device("cuda")
+        self.caches = {}
+        for i, name in enumerate("ABC"):
+            k = torch.empty(n, dtype=torch.int16, device=dev)
+            v = torch.empty(n, dtype=torch.int16, device=dev)
+            synth.fill_device_cache(k, w.value_seed + 100 * i, w.dtype)
+            synth.fill_device_cache(v, w.value_seed + 100 * i + 1, w.dtype)
+            self.caches[name] = (k, v)
+        self.prompt = int(w.prompt_len)
+        self.rows_start = [0] * B
+        self.rows_prompt = [self.prompt] * B
+        self.rows_full = [self.prompt + w.decode_steps] * B
+        self.layer_prompt = kv.kv_pack_bytes(self.lay, 1, self.rows_prompt)
+        self.layer_full = kv.kv_pack_bytes(self.lay, 1, self.rows_full)
+        self.slot = kv.kv_pack_bytes(self.lay, L, None, 1)
+
+        def bank(nbytes):
+            return torch.empty((nbytes + 1) // 2, dtype=torch.int16, device=dev)
+
+        def pinned(nbytes):
+            return torch.empty((nbytes + 1) // 2, dtype=torch.int16, pin_memory=True)
+
+        # four streams: prompt-side compute, token-side compute, and one copy
+        # stream per link direction (engines of one direction share it)
+        self.s = {name: torch.cuda.Stream() for name in ("p", "t", "d2h", "h2d")}
+        pb = max(self.layer_prompt, 1)
+        sb = swap_bank_bytes
+        x = transport
+        self.eng_p = kv.KvSwap(self.lay, bank(pb), bank(pb), pb, self.s["d2h"], x)
+        self.eng_t = kv.KvSwap(self.lay, bank(pb), bank(pb), pb, self.s["h2d"], x)
+        self.eng_o = kv.KvSwap(self.lay, bank(sb), bank(sb), sb, self.s["d2h"], x)
+        self.eng_i = kv.KvSwap(self.lay, bank(sb), bank(sb), sb, self.s["h2d"], x)
+        R = w.ring_slots
+        self.ring_host = pinned(w.decode_steps * self.slot)
+        self.ring = kv.KvRing(self.lay, R, bank(R * self.slot), bank(R * self.slot),
+                              self.ring_host, copy_stream=self.s["d2h"], transport=x)
+        self.host_p = pinned(L * self.layer_prompt)
+        self.host_s = pinned(L * self.layer_full)
+        self.ev_p = [torch.cuda.Event() for _ in range(L)]
+        self.ev_o = [torch.cuda.Event() for _ in range(L)]
+        for e in self.ev_p + self.ev_o:
+            e.record()            # materialise the hipEvents once, outside the timed region
+        self.positions = [[self.prompt + j] * B for j in range(w.decode_steps)]
+
+    def link_bytes(self):
+        L = self.w.L
+        return (2 * L * self.layer_prompt + 2 * self.w.decode_steps * self.slot
+                + 2 * L * self.layer_full)
+
+    def run(self):
+        torch, w = self.torch, self.w
+        L = w.L
+        A, Bc, Cc = self.caches["A"], self.caches["B"], self.caches["C"]
+        sp, st = self.s["p"], self.s["t"]
+        hp, hs = self.host_p.data_ptr(), self.host_s.data_ptr()
+        # 1+2: prompt streaming out of A, loaded into B as each layer lands
+        for l in range(L):
+            self.eng_p.stream_prompt_layer(A[0], A[1], l, 0, self.prompt, None,
+                                           hp + l * self.layer_prompt, self.layer_prompt,
+                                           sp, self.ev_p[l])
+            st.wait_event(self.ev_p[l])
+            self.eng_t.swap_in(Bc[0], Bc[1], l, 1, self.rows_start, self.rows_prompt,
+                               hp + l * self.layer_prompt, self.layer_prompt, st)
+        # 3: decode steps into the staging ring
+        self.ring.reset()
+        for pos in self.positions:
+            self.ring.push(Bc[0], Bc[1], pos, st)
+        self.ring.flush(st)
+        # 4: restore the ring into C
+        self.ring.restore(Cc[0], Cc[1], st)
+        # 5: microbatch swap of B: packs on st, unpacks into C on sp, duplex
+        for l in range(L):
+            self.eng_o.swap_out(Bc[0], Bc[1], l, 1, self.rows_start, self.rows_full,
+                                hs + l * self.layer_full, self.layer_full, st, self.ev_o[l])
+            sp.wait_event(self.ev_o[l])
+            self.eng_i.swap_in(Cc[0], Cc[1], l, 1, self.rows_start, self.rows_full,
+                               hs + l * self.layer_full, self.layer_full, sp)
+        torch.cuda.synchronize()
+
+
+def link_ceiling(torch, nbytes=1 << 30, reps=3):
+    """GB/s of one large contiguous pinned copy each way, and both at once."""
+    d = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
+    d2 = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
+    h = torch.empty(nbytes // 2, dtype=torch.int16, pin_memory=True)
+    h2 = torch.empty(nbytes // 2, dtype=torch.int16, pin_memory=True)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    out = {}
+    for name, fn in (("d2h", lambda: h.copy_(d, non_blocking=True)),
+                     ("h2d", lambda: d.copy_(h, non_blocking=True))):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        out[name] = reps * nbytes / (time.perf_counter() - t0) / 1e9
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        with torch.cuda.stream(s1):
+            h.copy_(d, non_blocking=True)
+        with torch.cuda.stream(s2):
+            d2.copy_(h2, non_blocking=True)
+    torch.cuda.synchronize()
+    out["duplex_total"] = 2 * reps * nbytes / (time.perf_counter() - t0) / 1e9
+    del d, d2, h, h2
+    return out
+
+
+def decode_push_us(step, reps=3):
+    torch = step.torch
+    st = step.s["t"]
+    Bc = step.caches["B"]
+    times = []
+    for _ in range(reps):
+        step.ring.reset()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for pos in step.positions:
+            step.ring.push(Bc[0], Bc[1], pos, st)
+        b.record(st)
+        step.ring.flush(st)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1000 / len(step.positions))
+    return min(times)
+
+
+def read_counters(kernel_name):
+    """Per-launch HBM traffic of `kernel_name` from the committed counter summary,
+    or None when absent or taken on a different kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    import hashlib
+    fields = {}
+    for line in open(COUNTERS_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "kv_cache_streaming_amd", "csrc", "kernels.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if fields.get("kernels_sha256_16") != digest or fields.get("kernel") != kernel_name:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(step, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same step."""
+    import numpy as np
+
+    import oracle
+    w = step.w
+    L, B, H, D, S = w.dims
+    A = [t.cpu().numpy().view(np.uint16) for t in step.caches["A"]]
+    Bh = [t.cpu().numpy().view(np.uint16).copy() for t in step.caches["B"]]
+    start, prompt, full = step.rows_start, step.rows_prompt, step.rows_full
+    ops = []
+    for l in range(L):
+        ops.append(("prompt pack", l, lambda l=l: oracle.pack(w.dims, A[0], A[1], l, 1, start, prompt)))
+        ops.append(("prompt unpack", l, None))
+        ops.append(("swap pack", l, lambda l=l: oracle.pack(w.dims, Bh[0], Bh[1], l, 1, start, full)))
+        ops.append(("swap unpack", l, None))
+        if l < w.decode_steps:
+            j = l
+            ops.append(("decode pack", j, lambda j=j: oracle.pack(w.dims, Bh[0], Bh[1], 0, L,
+                                                                  step.positions[j], [1] * B)))
+            ops.append(("restore unpack", j, None))
+    done_bytes, ran, last = 0, {}, None
+    t0 = time.perf_counter()
+    for name, idx, fn in ops:
+        if time.perf_counter() - t0 > budget_s:
+            break
+        if fn is not None:
+            last = fn()
+        elif name == "prompt unpack":   # each unpack consumes the pack just made
+            oracle.unpack(w.dims, Bh[0], Bh[1], idx, 1, start, prompt, last)
+        elif name == "swap unpack":
+            oracle.unpack(w.dims, Bh[0], Bh[1], idx, 1, start, full, last)
+        else:
+            oracle.unpack(w.dims, Bh[0], Bh[1], 0, L, step.positions[idx], [1] * B, last)
+        done_bytes += last.nbytes
+        ran[name] = ran.get(name, 0) + 1
+    elapsed = time.perf_counter() - t0
+    sample = ", ".join(f"{v} x {k}" for k, v in ran.items())
+    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{sample}: {done_bytes / 1e9:.3f} GB of KV payload in {elapsed:.1f} s "
+                      f"(single-threaded C oracle)"}
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the KV pack/unpack and swap path is measured on a single MI355X", flush=True)
+        sys.exit(2)
+    import torch
+
+    import kv_cache_streaming_amd as kv
+    import synth
+    w = synth.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    step = Step(w, args.swap_bank_mib << 20,
+                {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3}[args.transport])
+    torch.cuda.synchronize()
+
+    if args.calibrate_copy_mib:
+        n = (args.calibrate_copy_mib << 20) // 2
+        src = torch.empty(n, dtype=torch.int16, device="cuda").fill_(3)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    if not args.no_profile:
+        kv.kv_profile_begin()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.run()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stats = {} if args.no_profile else kv.kv_profile_end()
+    ms = elapsed / args.steps * 1000
+    link = step.link_bytes()
+    value = link / (ms / 1000) / 1e9
+
+    kernels = {}
+    for name, (launches, kms, kbytes) in stats.items():
+        if name.startswith("link_copy"):
+            # transfers: bytes are host-link bytes, not HBM traffic
+            kernels[name] = {"launches_per_step": launches / args.steps,
+                             "avg_us": round(kms / launches * 1000, 2),
+                             "link_bytes_per_launch": kbytes // launches,
+                             "link_GBps": round(kbytes / (kms / 1000) / 1e9, 1),
+                             "gpu_ms_per_step": round(kms / args.steps, 3)}
+            continue
+        avg_ms = kms / launches
+        kernels[name] = {"launches_per_step": launches / args.steps,
+                         "avg_us": round(avg_ms * 1000, 2),
+                         "algorithmic_bytes_per_launch": kbytes // launches,
+                         "GBps": round(kbytes / launches / (avg_ms / 1000) / 1e9, 1),
+                         "gpu_ms_per_step": round(kms / args.steps, 3)}
+    roofline = None
+    if any(not k.startswith("link_copy") for k in kernels):
+        hbm = [k for k in kernels if not k.startswith("link_copy")]
+        dom = max(hbm, key=lambda k: kernels[k]["gpu_ms_per_step"])
+        d = kernels[dom]
+        traffic = read_counters(dom)
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": d["GBps"], "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(d["GBps"] / HBM_PEAK_GBPS, 4),
+                    "traffic": traffic,
+                    "algorithmic_bytes_per_launch": d["algorithmic_bytes_per_launch"],
+                    "avg_us": d["avg_us"]}
+
+    detail = {"kernels": kernels, "link_bytes_per_step": link,
+              "link_peak_per_direction_GBps": PCIE_PEAK_GBPS}
+    if not args.no_profile:
+        detail["decode_push_us"] = round(decode_push_us(step), 2)
+        detail["link_ceiling_GBps"] = {k: round(v, 2) for k, v in link_ceiling(torch).items()}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(step, args.cpu_baseline_seconds)
+
+    line = {"metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u16",
+            "data": "synthetic",
+            "config": {"workload": w.name, "L": w.L, "B": w.B, "H": w.H, "D": w.D,
+                       "Smax": w.Smax, "kv_dtype": "fp16" if w.dtype == 0 else "bf16",
+                       "prompt_len": w.prompt_len, "decode_steps": w.decode_steps,
+                       "ring_slots": w.ring_slots, "swap_bank_mib": args.swap_bank_mib,
+                       "transport": args.transport,
+                       "hw_queues": int(os.environ["GPU_MAX_HW_QUEUES"])},
+            "roofline": roofline, "cpu_baseline": cpu, "detail": detail}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -168,8 +168,36 @@ int kv_unpack_prompt_layer(const kv_layout *lay, void *k, void *v,
  */
 typedef struct kv_swap kv_swap;
 
+/* How a bank reaches pinned host memory (flush/fetch, local leg, Table 1).
+ *   KV_XFER_AUTO    -- device->host by the link-copy kernel, host->device by
+ *                      hipMemcpyAsync (DMA).  The default.
+ *   KV_XFER_KERNEL  -- both directions by the library's link-copy kernel on
+ *                      the copy stream: the host buffer is mapped into the
+ *                      GPU's address space and the GPU's load/store units move
+ *                      16-byte vectors across the host link.
+ *   KV_XFER_RUNTIME -- both directions by hipMemcpyAsync with the ordinary
+ *                      host<->device kinds (the runtime picks the engine).
+ *   KV_XFER_DMA     -- both directions by hipMemcpyAsync between the bank and
+ *                      the host buffer's device-visible address with
+ *                      hipMemcpyDeviceToDeviceNoCU: the DMA engines, never the
+ *                      compute units.
+ * On MI355X a DMA copy that must wait for a kernel on another stream pays a
+ * long hand-off per dependency, which a layer-by-layer pipeline pays once per
+ * layer; a kernel copy waits through a queue barrier instead.  GPU-initiated
+ * reads of host memory, however, keep the two link directions from running
+ * at once, while DMA reads do not -- hence AUTO.  All three produce identical
+ * bytes. */
+typedef enum kv_transport {
+    KV_XFER_AUTO = 0,
+    KV_XFER_KERNEL = 1,
+    KV_XFER_RUNTIME = 2,
+    KV_XFER_DMA = 3
+} kv_transport;
+
+/* bank0/bank1: caller-owned device banks of bank_bytes each; `copy`: the
+ * stream that carries the transfers; `transport`: a kv_transport. */
 int kv_swap_create(kv_swap **out, const kv_layout *lay, void *bank0, void *bank1,
-                   int64_t bank_bytes, hipStream_t copy);
+                   int64_t bank_bytes, hipStream_t copy, int32_t transport);
 int kv_swap_destroy(kv_swap *e);
 
 /* Swap-out: pack the selected region (kernels on `compute`, so they see the
@@ -231,10 +259,10 @@ int64_t kv_swap_plan(const kv_layout *lay, int32_t layer_begin, int32_t layer_co
 typedef struct kv_ring kv_ring;
 
 /* bank_bytes must hold R slots; host_bytes bounds the steps that can be
- * pushed (steps * slot_bytes). */
+ * pushed (steps * slot_bytes); `transport` as for kv_swap_create. */
 int kv_ring_create(kv_ring **out, const kv_layout *lay, int32_t R,
                    void *bank0, void *bank1, int64_t bank_bytes,
-                   void *host, int64_t host_bytes, hipStream_t copy);
+                   void *host, int64_t host_bytes, hipStream_t copy, int32_t transport);
 int kv_ring_destroy(kv_ring *r);
 
 /* One decode step: pos is int32[B], every pos_b in [0, Smax). */

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libkvstream.so")
 
 KV_OK, KV_EINVAL, KV_ERANGE, KV_ESIZE, KV_EHIP, KV_EBUSY = 0, -1, -2, -3, -4, -5
 KV_F16, KV_BF16 = 0, 1
+KV_XFER_AUTO, KV_XFER_KERNEL, KV_XFER_RUNTIME, KV_XFER_DMA = 0, 1, 2, 3
 KV_MAX_ROWS = 256
 STATUS_NAMES = {0: "KV_OK", -1: "KV_EINVAL", -2: "KV_ERANGE", -3: "KV_ESIZE",
                 -4: "KV_EHIP", -5: "KV_EBUSY"}
@@ -78,13 +79,14 @@ _SIGNATURES = {
     "kv_unpack_tokens": (ctypes.c_int, [_LAY, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P]),
     "kv_pack_prompt_layer": (ctypes.c_int, [_LAY, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P]),
     "kv_unpack_prompt_layer": (ctypes.c_int, [_LAY, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P]),
-    "kv_swap_create": (ctypes.c_int, [ctypes.POINTER(_P), _LAY, _P, _P, _I64, _P]),
+    "kv_swap_create": (ctypes.c_int, [ctypes.POINTER(_P), _LAY, _P, _P, _I64, _P, _I32]),
     "kv_swap_destroy": (ctypes.c_int, [_P]),
     "kv_swap_out": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
     "kv_swap_in": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
     "kv_stream_prompt_layer": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _P]),
     "kv_swap_plan": (_I64, [_LAY, _I32, _I32, _P, _P, _I64, _P, _I64]),
-    "kv_ring_create": (ctypes.c_int, [ctypes.POINTER(_P), _LAY, _I32, _P, _P, _I64, _P, _I64, _P]),
+    "kv_ring_create": (ctypes.c_int, [ctypes.POINTER(_P), _LAY, _I32, _P, _P, _I64, _P, _I64, _P,
+                                      _I32]),
     "kv_ring_destroy": (ctypes.c_int, [_P]),
     "kv_ring_push": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "kv_ring_flush": (ctypes.c_int, [_P, _P, _P]),
@@ -256,18 +258,20 @@ def kv_swap_plan(lay, layer_begin, layer_count, start, count, bank_bytes):
 class KvSwap:
     """Handle of a swap engine (kv_swap_create / kv_swap_destroy)."""
 
-    def __init__(self, lay, bank0, bank1, bank_bytes=None, copy_stream=None):
+    def __init__(self, lay, bank0, bank1, bank_bytes=None, copy_stream=None,
+                 transport=KV_XFER_AUTO):
         self.lay = lay
         self._keep = (bank0, bank1)
+        self._destroy = _lib.kv_swap_destroy
         nb = min(_nbytes(bank0), _nbytes(bank1)) if bank_bytes is None else bank_bytes
         h = _P()
         _check(_lib.kv_swap_create(ctypes.byref(h), ctypes.byref(lay), _addr(bank0), _addr(bank1),
-                                   nb, _stream(copy_stream)), "kv_swap_create")
+                                   nb, _stream(copy_stream), transport), "kv_swap_create")
         self._h = h
 
     def close(self):
         if getattr(self, "_h", None):
-            _lib.kv_swap_destroy(self._h)
+            self._destroy(self._h)
             self._h = None
 
     __del__ = close
@@ -297,8 +301,9 @@ class KvSwap:
                                            _event(done)), "kv_stream_prompt_layer")
 
 
-def kv_swap_create(lay, bank0, bank1, bank_bytes=None, copy_stream=None) -> KvSwap:
-    return KvSwap(lay, bank0, bank1, bank_bytes, copy_stream)
+def kv_swap_create(lay, bank0, bank1, bank_bytes=None, copy_stream=None,
+                   transport=KV_XFER_AUTO) -> KvSwap:
+    return KvSwap(lay, bank0, bank1, bank_bytes, copy_stream, transport)
 
 
 def kv_swap_destroy(e: KvSwap) -> None:
@@ -323,21 +328,22 @@ class KvRing:
     """Handle of a decode-step staging ring (kv_ring_create / kv_ring_destroy)."""
 
     def __init__(self, lay, R, bank0, bank1, host, bank_bytes=None, host_bytes=None,
-                 copy_stream=None):
+                 copy_stream=None, transport=KV_XFER_AUTO):
         self.lay = lay
         self.R = R
         self._keep = (bank0, bank1, host)
+        self._destroy = _lib.kv_ring_destroy
         nb = min(_nbytes(bank0), _nbytes(bank1)) if bank_bytes is None else bank_bytes
         hb = _nbytes(host) if host_bytes is None else host_bytes
         h = _P()
         _check(_lib.kv_ring_create(ctypes.byref(h), ctypes.byref(lay), R, _addr(bank0),
-                                   _addr(bank1), nb, _addr(host), hb, _stream(copy_stream)),
-               "kv_ring_create")
+                                   _addr(bank1), nb, _addr(host), hb, _stream(copy_stream),
+                                   transport), "kv_ring_create")
         self._h = h
 
     def close(self):
         if getattr(self, "_h", None):
-            _lib.kv_ring_destroy(self._h)
+            self._destroy(self._h)
             self._h = None
 
     __del__ = close
@@ -363,8 +369,8 @@ class KvRing:
 
 
 def kv_ring_create(lay, R, bank0, bank1, host, bank_bytes=None, host_bytes=None,
-                   copy_stream=None) -> KvRing:
-    return KvRing(lay, R, bank0, bank1, host, bank_bytes, host_bytes, copy_stream)
+                   copy_stream=None, transport=KV_XFER_AUTO) -> KvRing:
+    return KvRing(lay, R, bank0, bank1, host, bank_bytes, host_bytes, copy_stream, transport)
 
 
 def kv_ring_destroy(r: KvRing) -> None:

@@ -94,6 +94,32 @@ int check_pinned_host(const void *p, int64_t bytes, const char *name)
     return KV_OK;
 }
 
+int host_device_address(const void *host, int64_t bytes, void **dev)
+{
+    hipPointerAttribute_t a;
+    std::memset(&a, 0, sizeof a);
+    if (hipPointerGetAttributes(&a, host) != hipSuccess || a.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return set_error(KV_EINVAL, "%p is not pinned host memory", host);
+    }
+    if (a.devicePointer == nullptr || a.hostPointer == nullptr)
+        return set_error(KV_EINVAL, "pinned host memory at %p is not mapped for the GPU", host);
+    char *d = (char *)a.devicePointer + ((const char *)host - (const char *)a.hostPointer);
+    if (bytes > 0) {
+        // the whole range must map with the same offset (one allocation)
+        hipPointerAttribute_t b;
+        std::memset(&b, 0, sizeof b);
+        const char *end = (const char *)host + (bytes - 1);
+        if (hipPointerGetAttributes(&b, end) != hipSuccess || b.devicePointer == nullptr ||
+            (char *)b.devicePointer + (end - (const char *)b.hostPointer) != d + (bytes - 1)) {
+            (void)hipGetLastError();
+            return set_error(KV_EINVAL, "pinned host range at %p does not map contiguously", host);
+        }
+    }
+    *dev = d;
+    return KV_OK;
+}
+
 int check_layers(const kv_layout &lay, int32_t layer_begin, int32_t layer_count)
 {
     if (layer_count < 0 || layer_begin < 0 || layer_begin > lay.L ||

@@ -146,6 +146,36 @@ int create_events(hipEvent_t *ev, int n)
     return KV_OK;
 }
 
+// One contiguous transfer between a bank and pinned host memory on `s`, with
+// the engine's transport.  `host_dev` is the device-visible address of the
+// host side (used by the link-copy kernel).
+int transfer(int32_t transport, void *bank, void *host, void *host_dev, int64_t bytes,
+             bool to_host, hipStream_t s)
+{
+    if (bytes <= 0)
+        return KV_OK;
+    const bool kernel = transport == KV_XFER_KERNEL || (transport == KV_XFER_AUTO && to_host);
+    if (kernel)
+        return to_host ? launch_link_copy(host_dev, bank, bytes, true, s)
+                       : launch_link_copy(bank, host_dev, bytes, false, s);
+    hipError_t r;
+    if (transport == KV_XFER_DMA)
+        r = to_host ? hipMemcpyAsync(host_dev, bank, (size_t)bytes, hipMemcpyDeviceToDeviceNoCU, s)
+                    : hipMemcpyAsync(bank, host_dev, (size_t)bytes, hipMemcpyDeviceToDeviceNoCU, s);
+    else
+        r = to_host ? hipMemcpyAsync(host, bank, (size_t)bytes, hipMemcpyDeviceToHost, s)
+                    : hipMemcpyAsync(bank, host, (size_t)bytes, hipMemcpyHostToDevice, s);
+    return r == hipSuccess ? KV_OK : hip_fail(r, "hipMemcpyAsync");
+}
+
+int check_transport(int32_t transport)
+{
+    if (transport != KV_XFER_AUTO && transport != KV_XFER_KERNEL && transport != KV_XFER_RUNTIME &&
+        transport != KV_XFER_DMA)
+        return set_error(KV_EINVAL, "transport %d is not a kv_transport", transport);
+    return KV_OK;
+}
+
 }  // namespace
 
 struct kv_swap {
@@ -153,6 +183,7 @@ struct kv_swap {
     void *bank[2];
     int64_t bank_bytes;
     hipStream_t copy;
+    int32_t transport;
     hipEvent_t ev[5];            // free0, free1, filled0, filled1, call
     bool free_valid[2];
     int next;
@@ -168,7 +199,9 @@ struct kv_ring {
     int64_t bank_bytes;
     void *host;
     int64_t host_bytes;
+    void *host_dev;              // device-visible address of `host`
     hipStream_t copy;
+    int32_t transport;
     int64_t slot_bytes;
     int64_t steps, flushed;
     std::vector<int32_t> pos;    // steps * B positions, in step order
@@ -194,6 +227,9 @@ int swap_out_rows(kv_swap *e, const void *k, const void *v, int32_t l0, int32_t 
                          (long long)need);
     if ((st = check_pinned_host(host, need, "host")))
         return st;
+    void *host_dev = nullptr;
+    if (need > 0 && (st = host_device_address(host, need, &host_dev)))
+        return st;
     if ((st = check_device_buffer(k, lay.k_bytes, "key cache")))
         return st;
     if ((st = check_device_buffer(v, lay.v_bytes, "value cache")))
@@ -216,13 +252,11 @@ int swap_out_rows(kv_swap *e, const void *k, const void *v, int32_t l0, int32_t 
         if ((st = record(e->filled_ev(bk), compute, "swap-out packed")) ||
             (st = wait(e->copy, e->filled_ev(bk), "swap-out copy wait")))
             return st;
-        for (int p = 0; p < c.pieces; ++p) {
-            const hipError_t r = hipMemcpyAsync((char *)host + c.host_off[p],
-                                                (const char *)e->bank[bk] + c.bank_off[p],
-                                                (size_t)c.bytes[p], hipMemcpyDeviceToHost, e->copy);
-            if (r != hipSuccess)
-                return hip_fail(r, "swap-out hipMemcpyAsync");
-        }
+        for (int p = 0; p < c.pieces; ++p)
+            if ((st = transfer(e->transport, (char *)e->bank[bk] + c.bank_off[p],
+                               (char *)host + c.host_off[p], (char *)host_dev + c.host_off[p],
+                               c.bytes[p], true, e->copy)))
+                return st;
         if ((st = record(e->free_ev(bk), e->copy, "swap-out copied")))
             return st;
         e->free_valid[bk] = true;
@@ -237,13 +271,15 @@ int swap_out_rows(kv_swap *e, const void *k, const void *v, int32_t l0, int32_t 
 extern "C" {
 
 int kv_swap_create(kv_swap **out, const kv_layout *lay, void *bank0, void *bank1,
-                   int64_t bank_bytes, hipStream_t copy)
+                   int64_t bank_bytes, hipStream_t copy, int32_t transport)
 {
     if (out == nullptr)
         return set_error(KV_EINVAL, "output handle pointer is NULL");
     *out = nullptr;
     int st = check_layout(lay);
     if (st)
+        return st;
+    if ((st = check_transport(transport)))
         return st;
     if (bank_bytes <= 0)
         return set_error(KV_ESIZE, "bank_bytes %lld must be positive", (long long)bank_bytes);
@@ -260,6 +296,7 @@ int kv_swap_create(kv_swap **out, const kv_layout *lay, void *bank0, void *bank1
     e->bank[1] = bank1;
     e->bank_bytes = bank_bytes;
     e->copy = copy;
+    e->transport = transport;
     e->free_valid[0] = e->free_valid[1] = false;
     e->next = 0;
     if ((st = create_events(e->ev, 5))) {
@@ -336,6 +373,9 @@ int kv_swap_in(kv_swap *e, void *k, void *v, int32_t layer_begin, int32_t layer_
                          (long long)need);
     if ((st = check_pinned_host(host, need, "host")))
         return st;
+    void *host_dev = nullptr;
+    if (need > 0 && (st = host_device_address(host, need, &host_dev)))
+        return st;
     if ((st = check_device_buffer(k, lay.k_bytes, "key cache")) ||
         (st = check_device_buffer(v, lay.v_bytes, "value cache")))
         return st;
@@ -354,13 +394,11 @@ int kv_swap_in(kv_swap *e, void *k, void *v, int32_t layer_begin, int32_t layer_
         e->next ^= 1;
         if (e->free_valid[bk] && (st = wait(e->copy, e->free_ev(bk), "swap-in bank wait")))
             return st;
-        for (int p = 0; p < c.pieces; ++p) {
-            const hipError_t r = hipMemcpyAsync((char *)e->bank[bk] + c.bank_off[p],
-                                                (const char *)host + c.host_off[p],
-                                                (size_t)c.bytes[p], hipMemcpyHostToDevice, e->copy);
-            if (r != hipSuccess)
-                return hip_fail(r, "swap-in hipMemcpyAsync");
-        }
+        for (int p = 0; p < c.pieces; ++p)
+            if ((st = transfer(e->transport, (char *)e->bank[bk] + c.bank_off[p],
+                               (char *)host + c.host_off[p], (char *)host_dev + c.host_off[p],
+                               c.bytes[p], false, e->copy)))
+                return st;
         if ((st = record(e->filled_ev(bk), e->copy, "swap-in loaded")) ||
             (st = wait(compute, e->filled_ev(bk), "swap-in unpack wait")))
             return st;
@@ -419,13 +457,16 @@ int64_t kv_swap_plan(const kv_layout *lay, int32_t layer_begin, int32_t layer_co
 // staging ring
 
 int kv_ring_create(kv_ring **out, const kv_layout *lay, int32_t R, void *bank0, void *bank1,
-                   int64_t bank_bytes, void *host, int64_t host_bytes, hipStream_t copy)
+                   int64_t bank_bytes, void *host, int64_t host_bytes, hipStream_t copy,
+                   int32_t transport)
 {
     if (out == nullptr)
         return set_error(KV_EINVAL, "output handle pointer is NULL");
     *out = nullptr;
     int st = check_layout(lay);
     if (st)
+        return st;
+    if ((st = check_transport(transport)))
         return st;
     if (R <= 0)
         return set_error(KV_EINVAL, "R=%d must be positive", R);
@@ -442,6 +483,9 @@ int kv_ring_create(kv_ring **out, const kv_layout *lay, int32_t R, void *bank0, 
         return set_error(KV_EINVAL, "the two banks overlap");
     if ((st = check_pinned_host(host, host_bytes, "host")))
         return st;
+    void *host_dev = nullptr;
+    if (host_bytes > 0 && (st = host_device_address(host, host_bytes, &host_dev)))
+        return st;
     kv_ring *r = new (std::nothrow) kv_ring();
     if (!r)
         return set_error(KV_EINVAL, "out of host memory for the handle");
@@ -452,7 +496,9 @@ int kv_ring_create(kv_ring **out, const kv_layout *lay, int32_t R, void *bank0, 
     r->bank_bytes = bank_bytes;
     r->host = host;
     r->host_bytes = host_bytes;
+    r->host_dev = host_dev;
     r->copy = copy;
+    r->transport = transport;
     r->slot_bytes = slot;
     r->steps = r->flushed = 0;
     r->wait_needed[0] = r->wait_needed[1] = false;
@@ -486,11 +532,11 @@ int ring_flush_range(kv_ring *r, int64_t first, int64_t n, hipStream_t compute)
     if ((st = record(r->filled_ev(bk), compute, "ring filled")) ||
         (st = wait(r->copy, r->filled_ev(bk), "ring flush wait")))
         return st;
-    const hipError_t e = hipMemcpyAsync((char *)r->host + first * r->slot_bytes,
-                                        (const char *)r->bank[bk] + off,
-                                        (size_t)(n * r->slot_bytes), hipMemcpyDeviceToHost, r->copy);
-    if (e != hipSuccess)
-        return hip_fail(e, "ring flush hipMemcpyAsync");
+    if ((st = transfer(r->transport, (char *)r->bank[bk] + off,
+                       (char *)r->host + first * r->slot_bytes,
+                       (char *)r->host_dev + first * r->slot_bytes, n * r->slot_bytes, true,
+                       r->copy)))
+        return st;
     if ((st = record(r->free_ev(bk), r->copy, "ring flushed")))
         return st;
     r->wait_needed[bk] = true;
@@ -579,11 +625,10 @@ int kv_ring_restore(kv_ring *r, void *k, void *v, hipStream_t compute, hipEvent_
         const int bk = (int)(g & 1);
         if (r->free_valid[bk] && (st = wait(r->copy, r->free_ev(bk), "ring restore bank wait")))
             return st;
-        const hipError_t e = hipMemcpyAsync(r->bank[bk], (const char *)r->host + j0 * r->slot_bytes,
-                                            (size_t)(n * r->slot_bytes), hipMemcpyHostToDevice,
-                                            r->copy);
-        if (e != hipSuccess)
-            return hip_fail(e, "ring restore hipMemcpyAsync");
+        if ((st = transfer(r->transport, r->bank[bk], (char *)r->host + j0 * r->slot_bytes,
+                           (char *)r->host_dev + j0 * r->slot_bytes, n * r->slot_bytes, false,
+                           r->copy)))
+            return st;
         if ((st = record(r->filled_ev(bk), r->copy, "ring restore loaded")) ||
             (st = wait(compute, r->filled_ev(bk), "ring restore unpack wait")))
             return st;

@@ -25,6 +25,7 @@
 #include "kvs_internal.h"
 
 #include <algorithm>
+#include <cstdlib>
 
 namespace kvs {
 namespace {
@@ -233,6 +234,62 @@ hipError_t launch_tiles_rt(const Geometry &g, const RowTable &rt, int64_t blocks
     return hipGetLastError();
 }
 
+// Transfer between a staging bank in HBM and pinned host memory, run by the
+// GPU's own load/store units instead of a DMA engine (the host buffer is
+// mapped into the GPU's address space).  Each thread keeps four 16-byte
+// vectors in flight; the grid is capped so that the copy occupies a fraction
+// of the compute units while it waits on the host link.  Loads from host
+// memory and stores to it are non-temporal (the data is touched once).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool kToHost>
+__global__ __launch_bounds__(kThreads) void link_copy(const u32x4 *__restrict__ src,
+                                                      u32x4 *__restrict__ dst, int64_t nvec)
+{
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; i + 3 * stride < nvec; i += 4 * stride) {
+        u32x4 a, b, c, d;
+        if (kToHost) {
+            a = src[i];
+            b = src[i + stride];
+            c = src[i + 2 * stride];
+            d = src[i + 3 * stride];
+            __builtin_nontemporal_store(a, dst + i);
+            __builtin_nontemporal_store(b, dst + i + stride);
+            __builtin_nontemporal_store(c, dst + i + 2 * stride);
+            __builtin_nontemporal_store(d, dst + i + 3 * stride);
+        } else {
+            a = __builtin_nontemporal_load(src + i);
+            b = __builtin_nontemporal_load(src + i + stride);
+            c = __builtin_nontemporal_load(src + i + 2 * stride);
+            d = __builtin_nontemporal_load(src + i + 3 * stride);
+            dst[i] = a;
+            dst[i + stride] = b;
+            dst[i + 2 * stride] = c;
+            dst[i + 3 * stride] = d;
+        }
+    }
+    for (; i < nvec; i += stride) {
+        if (kToHost)
+            __builtin_nontemporal_store(src[i], dst + i);
+        else
+            dst[i] = __builtin_nontemporal_load(src + i);
+    }
+    if (kToHost)
+        __threadfence_system();   // host-visible before the kernel completes
+}
+
+int link_blocks()
+{
+    static const int n = [] {
+        const char *e = std::getenv("KV_LINK_BLOCKS");
+        const int v = e ? std::atoi(e) : 0;
+        return v > 0 && v <= 65535 ? v : 128;
+    }();
+    return n;
+}
+
 int tile_tokens_for(int32_t C)
 {
     return C >= kTileVecs ? 1 : kTileVecs / C;
@@ -290,6 +347,28 @@ int launch_copy(bool pack, const Geometry &g0, const RowTable &rt, int32_t max_c
             return hip_fail(e, name);
     }
     return KV_OK;
+}
+
+int launch_link_copy(void *dst, const void *src, int64_t bytes, bool to_host, hipStream_t s)
+{
+    if (bytes <= 0)
+        return KV_OK;
+    if (bytes % 16 != 0 || ((uintptr_t)dst | (uintptr_t)src) % 16 != 0)
+        return set_error(KV_EINVAL, "link copy of %lld bytes is not in whole 16-byte vectors",
+                         (long long)bytes);
+    const int64_t nvec = bytes / 16;
+    const int64_t blocks = std::min<int64_t>(link_blocks(), (nvec + kThreads - 1) / kThreads);
+    const char *name = to_host ? "link_copy_d2h" : "link_copy_h2d";
+    void *tok = profiling_enabled() ? profile_start(s) : nullptr;
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    if (to_host)
+        link_copy<true><<<grid, block, 0, s>>>((const u32x4 *)src, (u32x4 *)dst, nvec);
+    else
+        link_copy<false><<<grid, block, 0, s>>>((const u32x4 *)src, (u32x4 *)dst, nvec);
+    const hipError_t e = hipGetLastError();
+    if (tok)
+        profile_stop(tok, s, name, bytes);
+    return e == hipSuccess ? KV_OK : hip_fail(e, name);
 }
 
 }  // namespace kvs

@@ -61,6 +61,15 @@ int enqueue_copy(bool pack, const kv_layout &lay, const void *k, const void *v, 
 int launch_copy(bool pack, const Geometry &g, const RowTable &rt, int32_t max_count,
                 hipStream_t s);
 
+// Copies `bytes` (a multiple of 16) between a device buffer and pinned host
+// memory with the link-copy kernel.  `dst`/`src` are device-visible
+// addresses (see host_device_address).
+int launch_link_copy(void *dst, const void *src, int64_t bytes, bool to_host, hipStream_t s);
+
+// Device-visible address of pinned host memory [host, host+bytes); returns
+// KV_OK or KV_EINVAL.
+int host_device_address(const void *host, int64_t bytes, void **dev);
+
 // ---- profiling (api.hip) ----
 bool profiling_enabled();
 // Begin/end a bracketed launch; `tok` is opaque state handed back to profile_end.

@@ -213,11 +213,15 @@ def test_error_paths(kv):
     assert ring.steps == 3
 
 
-def run_ring(kv, dims, R, positions, seed, bits=True, mutate=False, delay_cycles=0):
+TRANSPORTS = [0, 1, 2, 3]   # KV_XFER_AUTO, KV_XFER_KERNEL, KV_XFER_RUNTIME, KV_XFER_DMA
+
+
+def run_ring(kv, dims, R, positions, seed, bits=True, mutate=False, delay_cycles=0, transport=0):
     """Push every step, flush, restore into a zero cache; compare with the oracle."""
     import torch
     L, B, H, D, S = dims
-    note(f"ring dims={dims} R={R} steps={len(positions)} mutate={mutate} delay={delay_cycles}")
+    note(f"ring dims={dims} R={R} steps={len(positions)} mutate={mutate} delay={delay_cycles} "
+         f"transport={transport}")
     K, V = synth.cache_pair(dims, seed, bits=bits)
     lay = kv.kv_layout_init(L, B, H, D, S, 0)
     dk, dv = dev(K), dev(V)
@@ -228,7 +232,7 @@ def run_ring(kv, dims, R, positions, seed, bits=True, mutate=False, delay_cycles
     copy = torch.cuda.Stream()
     compute = torch.cuda.current_stream()
     ring = kv.KvRing(lay, R, banks[0], banks[1], hostbuf, host_bytes=steps * slot,
-                     copy_stream=copy)
+                     copy_stream=copy, transport=transport)
     slots = []
     rng = np.random.default_rng(seed)
     if delay_cycles:
@@ -260,30 +264,35 @@ def run_ring(kv, dims, R, positions, seed, bits=True, mutate=False, delay_cycles
     ring.close()
 
 
-def test_ring_decode_flow(kv):
+@pytest.mark.parametrize("transport", TRANSPORTS)
+def test_ring_decode_flow(kv, transport):
     dims = (3, 4, 2, 64, 50)
     pos = [[10 + j, 20 + j, 3 + j, 40 + (j % 9)] for j in range(19)]   # 2 full banks + a partial
-    run_ring(kv, dims, 8, pos, seed=21)
+    run_ring(kv, dims, 8, pos, seed=21, transport=transport)
 
 
-def test_ring_duplicate_positions_last_writer_wins(kv):
+@pytest.mark.parametrize("transport", TRANSPORTS)
+def test_ring_duplicate_positions_last_writer_wins(kv, transport):
     dims = (2, 3, 3, 16, 6)
     pos = [[j % 6, (2 * j) % 6, 5] for j in range(11)]
-    run_ring(kv, dims, 4, pos, seed=22, mutate=True)
+    run_ring(kv, dims, 4, pos, seed=22, mutate=True, transport=transport)
 
 
-def test_ring_bank_reuse_waits_for_a_late_flush(kv):
+@pytest.mark.parametrize("transport", TRANSPORTS)
+def test_ring_bank_reuse_waits_for_a_late_flush(kv, transport):
     """The copy stream is held back by a bounded spin; a push that reuses a bank
     must still wait for that bank's copy (else the host image would differ)."""
     dims = (2, 2, 2, 32, 64)
     pos = [[j, 63 - j] for j in range(13)]
-    run_ring(kv, dims, 2, pos, seed=23, mutate=True, delay_cycles=200_000_000)
+    run_ring(kv, dims, 2, pos, seed=23, mutate=True, delay_cycles=200_000_000,
+             transport=transport)
 
 
-def run_swap(kv, dims, l0, nl, start, count, bank_bytes, seed, delay_cycles=0):
+def run_swap(kv, dims, l0, nl, start, count, bank_bytes, seed, delay_cycles=0, transport=0):
     import torch
     L, B, H, D, S = dims
-    note(f"swap dims={dims} layers=[{l0},+{nl}) bank={bank_bytes} delay={delay_cycles}")
+    note(f"swap dims={dims} layers=[{l0},+{nl}) bank={bank_bytes} delay={delay_cycles} "
+         f"transport={transport}")
     K, V = synth.cache_pair(dims, seed, bits=True)
     lay = kv.kv_layout_init(L, B, H, D, S, 0)
     dk, dv = dev(K), dev(V)
@@ -291,7 +300,7 @@ def run_swap(kv, dims, l0, nl, start, count, bank_bytes, seed, delay_cycles=0):
     b0, b1 = empty(bank_bytes // 2 + 8), empty(bank_bytes // 2 + 8)
     copy = torch.cuda.Stream()
     compute = torch.cuda.current_stream()
-    eng = kv.KvSwap(lay, b0, b1, bank_bytes, copy)
+    eng = kv.KvSwap(lay, b0, b1, bank_bytes, copy, transport)
     hostbuf = pinned(want.size + CANARY)
     if delay_cycles:
         with torch.cuda.stream(copy):
@@ -320,27 +329,33 @@ def run_swap(kv, dims, l0, nl, start, count, bank_bytes, seed, delay_cycles=0):
     eng.close()
 
 
-def test_swap_whole_layer_chunks(kv):
+@pytest.mark.parametrize("transport", TRANSPORTS)
+def test_swap_whole_layer_chunks(kv, transport):
     dims = (6, 3, 2, 64, 300)
     layer = 2 * 2 * 64 * 2 * (300 + 250 + 17)
-    run_swap(kv, dims, 1, 5, [0, 50, 283], [300, 250, 17], 2 * layer, seed=31)
+    run_swap(kv, dims, 1, 5, [0, 50, 283], [300, 250, 17], 2 * layer, seed=31,
+             transport=transport)
 
 
-def test_swap_row_group_chunks(kv):
+@pytest.mark.parametrize("transport", TRANSPORTS)
+def test_swap_row_group_chunks(kv, transport):
     dims = (3, 5, 2, 128, 260)
     count = [260, 0, 100, 255, 3]
     start = [0, 0, 160, 5, 257]
     per_row = [2 * 2 * 128 * 2 * c for c in count]
-    run_swap(kv, dims, 0, 3, start, count, max(per_row) + 4096, seed=32)
+    run_swap(kv, dims, 0, 3, start, count, max(per_row) + 4096, seed=32, transport=transport)
 
 
-def test_swap_waits_for_late_copies(kv):
+@pytest.mark.parametrize("transport", TRANSPORTS)
+def test_swap_waits_for_late_copies(kv, transport):
     dims = (8, 2, 2, 32, 128)
     layer = 2 * 2 * 32 * 2 * 256
-    run_swap(kv, dims, 0, 8, [0, 0], [128, 128], layer, seed=33, delay_cycles=200_000_000)
+    run_swap(kv, dims, 0, 8, [0, 0], [128, 128], layer, seed=33, delay_cycles=200_000_000,
+             transport=transport)
 
 
-def test_stream_prompt_layers(kv):
+@pytest.mark.parametrize("transport", TRANSPORTS)
+def test_stream_prompt_layers(kv, transport):
     import torch
     dims = (4, 3, 2, 64, 200)
     L, B, H, D, S = dims
@@ -353,7 +368,7 @@ def test_stream_prompt_layers(kv):
     per_layer = oracle.pack(dims, K, V, 0, 1, start, count).size
     b0, b1 = empty(per_layer), empty(per_layer)
     copy = torch.cuda.Stream()
-    eng = kv.KvSwap(lay, b0, b1, per_layer * 2, copy)
+    eng = kv.KvSwap(lay, b0, b1, per_layer * 2, copy, transport)
     hostbuf = pinned(L * per_layer + CANARY)
     hv = pinned_host_view(hostbuf)
     done = torch.cuda.Event()
