@@ -2,25 +2,31 @@
 
 One step is one pass of the whole path over one batch of the
 GPT-2-1.5B-shaped workload (L=48, B=8, H=25, D=64, Smax=1024, fp16; prompt
-length 1000; 24 decode steps; staging ring of 8 slots):
+length 1000; 24 decode steps; staging ring of 8 slots).  It follows the
+dataflow of the DejaVu workers, emulated on one GPU:
 
-  1. prompt streaming: the 48 prompt layers of cache A are packed layer by
-     layer and copied to pinned host memory (prompt streamer);
-  2. prompt load: each layer, once its copy has landed, is copied back
-     through the banks and unpacked into cache B (swap-in), so that host->GPU
-     copies of layer l run while GPU->host copies of layer l+1 are in flight;
+  1. prompt streaming (prompt worker): the 48 prompt layers of cache A are
+     packed layer by layer and copied to pinned host memory;
+  2. prompt load (token worker): the prompt image streamed in the previous
+     step -- a different request, already in host memory -- is copied back
+     through the banks and unpacked into cache B layer by layer, while (1)
+     runs: the two link directions carry independent data;
   3. decode: 24 single-token packs of cache B (positions 1000..1023) into the
-     staging ring, flushed to pinned host memory every 8 steps;
-  4. restore: the ring's host image is unpacked into cache C;
-  5. microbatch swap: cache B (all 1024 positions) is swapped out layer by
-     layer to pinned host memory and swapped in to cache C, again duplex.
+     staging ring, flushed to pinned host memory every 8 steps (replication);
+  4. restore: the ring's host image is unpacked into cache D (recovery on a
+     fresh worker);
+  5. microbatch swap: cache B (microbatch x-1, all 1024 positions) is swapped
+     out layer by layer while microbatch x+1 is swapped in to cache C from
+     its host image, duplex.
 
-Inputs are resident in HBM before the timed region.  `value` is the KV
-payload the step moves across the host link (both directions) per second.
-`roofline` describes the kernel with the most GPU time: algorithmic bytes
-(payload read + payload written) per launch over its average duration, both
-measured live with hipEvents bracketing every launch on its own stream.
-`cpu_baseline` is the oracle on a bounded sample of the same step.
+Host images are double-buffered across steps, so each step's inbound
+transfers read what an earlier step wrote.  Inputs are resident in HBM
+before the timed region.  `value` is the KV payload the step moves across
+the host link (both directions) per second.  `roofline` describes the
+pack/unpack kernel with the most GPU time: algorithmic bytes (payload read +
+payload written) per launch over its average duration, both measured live
+with hipEvents bracketing every launch on its own stream.  `cpu_baseline`
+is the oracle on a bounded sample of the same step.
 """
 from __future__ import annotations
 
@@ -55,7 +61,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="gpt2-1.5b")
     ap.add_argument("--swap-bank-mib", type=int, default=256)
-    ap.add_argument("--transport", choices=("auto", "kernel", "runtime", "dma"), default="auto",
+    ap.add_argument("--transport", choices=("auto", "kernel", "runtime", "dma", "dma_out"), default="auto",
                     help="bank<->host transfers (see kv_transport in include/kvstream.h)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -80,7 +86,7 @@ class Step:
         n = L * B * H * D * S
         dev = torch.device("cuda")
         self.caches = {}
-        for i, name in enumerate("ABC"):
+        for i, name in enumerate("ABCD"):
             k = torch.empty(n, dtype=torch.int16, device=dev)
             v = torch.empty(n, dtype=torch.int16, device=dev)
             synth.fill_device_cache(k, w.value_seed + 100 * i, w.dtype)
@@ -114,12 +120,10 @@ class Step:
         self.ring_host = pinned(w.decode_steps * self.slot)
         self.ring = kv.KvRing(self.lay, R, bank(R * self.slot), bank(R * self.slot),
                               self.ring_host, copy_stream=self.s["d2h"], transport=x)
-        self.host_p = pinned(L * self.layer_prompt)
-        self.host_s = pinned(L * self.layer_full)
-        self.ev_p = [torch.cuda.Event() for _ in range(L)]
-        self.ev_o = [torch.cuda.Event() for _ in range(L)]
-        for e in self.ev_p + self.ev_o:
-            e.record()            # materialise the hipEvents once, outside the timed region
+        # double-buffered host images: one written this step, one read
+        self.host_p = [pinned(L * self.layer_prompt) for _ in range(2)]
+        self.host_s = [pinned(L * self.layer_full) for _ in range(2)]
+        self.k = 0
         self.positions = [[self.prompt + j] * B for j in range(w.decode_steps)]
 
     def link_bytes(self):
@@ -130,31 +134,32 @@ class Step:
     def run(self):
         torch, w = self.torch, self.w
         L = w.L
-        A, Bc, Cc = self.caches["A"], self.caches["B"], self.caches["C"]
+        A, Bc, Cc, Dc = (self.caches[n] for n in "ABCD")
         sp, st = self.s["p"], self.s["t"]
-        hp, hs = self.host_p.data_ptr(), self.host_s.data_ptr()
-        # 1+2: prompt streaming out of A, loaded into B as each layer lands
+        out, inn = self.k % 2, (self.k + 1) % 2
+        self.k += 1
+        hp_out, hp_in = self.host_p[out].data_ptr(), self.host_p[inn].data_ptr()
+        hs_out, hs_in = self.host_s[out].data_ptr(), self.host_s[inn].data_ptr()
+        lp, lf = self.layer_prompt, self.layer_full
+        # 1+2: prompt streaming out of A || loading an earlier prompt into B
         for l in range(L):
             self.eng_p.stream_prompt_layer(A[0], A[1], l, 0, self.prompt, None,
-                                           hp + l * self.layer_prompt, self.layer_prompt,
-                                           sp, self.ev_p[l])
-            st.wait_event(self.ev_p[l])
+                                           hp_out + l * lp, lp, sp)
             self.eng_t.swap_in(Bc[0], Bc[1], l, 1, self.rows_start, self.rows_prompt,
-                               hp + l * self.layer_prompt, self.layer_prompt, st)
-        # 3: decode steps into the staging ring
+                               hp_in + l * lp, lp, st)
+        # 3: decode steps of B into the staging ring
         self.ring.reset()
         for pos in self.positions:
             self.ring.push(Bc[0], Bc[1], pos, st)
         self.ring.flush(st)
-        # 4: restore the ring into C
-        self.ring.restore(Cc[0], Cc[1], st)
-        # 5: microbatch swap of B: packs on st, unpacks into C on sp, duplex
+        # 4: restore the ring into D
+        self.ring.restore(Dc[0], Dc[1], st)
+        # 5: swap out microbatch x-1 (B) || swap in microbatch x+1 (into C)
         for l in range(L):
             self.eng_o.swap_out(Bc[0], Bc[1], l, 1, self.rows_start, self.rows_full,
-                                hs + l * self.layer_full, self.layer_full, st, self.ev_o[l])
-            sp.wait_event(self.ev_o[l])
+                                hs_out + l * lf, lf, st)
             self.eng_i.swap_in(Cc[0], Cc[1], l, 1, self.rows_start, self.rows_full,
-                               hs + l * self.layer_full, self.layer_full, sp)
+                               hs_in + l * lf, lf, sp)
         torch.cuda.synchronize()
 
 
@@ -186,6 +191,24 @@ def link_ceiling(torch, nbytes=1 << 30, reps=3):
     out["duplex_total"] = 2 * reps * nbytes / (time.perf_counter() - t0) / 1e9
     del d, d2, h, h2
     return out
+
+
+def hbm_copy_ceiling(torch, nbytes=1 << 30, reps=4):
+    """GB/s (read + write) of a plain 1 GiB device-to-device copy."""
+    a = torch.empty(4 * nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    n = nbytes // 2
+    b[:n].copy_(a[:n])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r in range(reps):           # rotate over 4 GiB: more than the Infinity Cache
+        b[r % 4 * n:(r % 4 + 1) * n].copy_(a[r % 4 * n:(r % 4 + 1) * n])
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * reps * nbytes / (e0.elapsed_time(e1) / 1000) / 1e9
+    del a, b
+    return gbps
 
 
 def decode_push_us(step, reps=3):
@@ -286,14 +309,16 @@ def main():
     w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     step = Step(w, args.swap_bank_mib << 20,
-                {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3}[args.transport])
+                {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3, "dma_out": 4}[args.transport])
     torch.cuda.synchronize()
 
     if args.calibrate_copy_mib:
+        # a plain elementwise kernel that reads and writes exactly this many
+        # bytes: the scale for the hardware byte counters
         n = (args.calibrate_copy_mib << 20) // 2
         src = torch.empty(n, dtype=torch.int16, device="cuda").fill_(3)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -345,6 +370,7 @@ def main():
     if not args.no_profile:
         detail["decode_push_us"] = round(decode_push_us(step), 2)
         detail["link_ceiling_GBps"] = {k: round(v, 2) for k, v in link_ceiling(torch).items()}
+        detail["hbm_copy_ceiling_GBps"] = round(hbm_copy_ceiling(torch), 1)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(step, args.cpu_baseline_seconds)

@@ -181,6 +181,8 @@ typedef struct kv_swap kv_swap;
  *                      the host buffer's device-visible address with
  *                      hipMemcpyDeviceToDeviceNoCU: the DMA engines, never the
  *                      compute units.
+ *   KV_XFER_DMA_OUT -- device->host as KV_XFER_DMA, host->device as
+ *                      KV_XFER_RUNTIME.
  * On MI355X a DMA copy that must wait for a kernel on another stream pays a
  * long hand-off per dependency, which a layer-by-layer pipeline pays once per
  * layer; a kernel copy waits through a queue barrier instead.  GPU-initiated
@@ -191,7 +193,8 @@ typedef enum kv_transport {
     KV_XFER_AUTO = 0,
     KV_XFER_KERNEL = 1,
     KV_XFER_RUNTIME = 2,
-    KV_XFER_DMA = 3
+    KV_XFER_DMA = 3,
+    KV_XFER_DMA_OUT = 4
 } kv_transport;
 
 /* bank0/bank1: caller-owned device banks of bank_bytes each; `copy`: the

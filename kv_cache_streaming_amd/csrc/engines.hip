@@ -159,7 +159,7 @@ int transfer(int32_t transport, void *bank, void *host, void *host_dev, int64_t 
         return to_host ? launch_link_copy(host_dev, bank, bytes, true, s)
                        : launch_link_copy(bank, host_dev, bytes, false, s);
     hipError_t r;
-    if (transport == KV_XFER_DMA)
+    if (transport == KV_XFER_DMA || (transport == KV_XFER_DMA_OUT && to_host))
         r = to_host ? hipMemcpyAsync(host_dev, bank, (size_t)bytes, hipMemcpyDeviceToDeviceNoCU, s)
                     : hipMemcpyAsync(bank, host_dev, (size_t)bytes, hipMemcpyDeviceToDeviceNoCU, s);
     else
@@ -170,8 +170,7 @@ int transfer(int32_t transport, void *bank, void *host, void *host_dev, int64_t 
 
 int check_transport(int32_t transport)
 {
-    if (transport != KV_XFER_AUTO && transport != KV_XFER_KERNEL && transport != KV_XFER_RUNTIME &&
-        transport != KV_XFER_DMA)
+    if (transport < KV_XFER_AUTO || transport > KV_XFER_DMA_OUT)
         return set_error(KV_EINVAL, "transport %d is not a kv_transport", transport);
     return KV_OK;
 }

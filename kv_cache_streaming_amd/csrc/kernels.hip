@@ -31,8 +31,6 @@ namespace kvs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTileVecs = 1024;           // 16 KiB of K per tile (and 16 KiB of V)
-constexpr int kPerThread = kTileVecs / kThreads;
 constexpr int kSmallMaxTokens = 8;        // rows with at most this many tokens use copy_rows_small
 
 template <bool kPack>
@@ -113,13 +111,21 @@ __device__ __forceinline__ int lds_slot(int i, int c, int C)
     }
 }
 
-template <int CT, bool kPack>
+// Registers are a native 4 x 32-bit vector type: arrays of it stay in VGPRs
+// (arrays of the uint4 struct end up in scratch).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// One tile = kThreads * PER vectors of K (and as many of V); TT = tile / C
+// tokens.  Element e = tid + p*kThreads of the tile is read as (chunk e/TT,
+// token e%TT) on the cache side (chunk-major) and as (token e/C, chunk e%C)
+// on the packed side (token-major).
+template <int CT, int PER, bool kPack>
 __global__ __launch_bounds__(kThreads) void copy_tiles(Geometry g, RowTable rt)
 {
-    static_assert(kPerThread == 4, "the unrolled body below moves four vectors per thread");
-    __shared__ uint4 lds[kTileVecs];
+    constexpr int TV = kThreads * PER;
+    __shared__ u32x4 lds[TV];
     const int32_t C = CT ? CT : g.C;
-    const int32_t TT = CT ? kTileVecs / CT : g.tile_tokens;
+    const int32_t TT = CT ? TV / CT : g.tile_tokens;
 
     int32_t bid = blockIdx.x;
     const int32_t tile = bid % g.tiles_per_row;
@@ -139,160 +145,162 @@ __global__ __launch_bounds__(kThreads) void copy_tiles(Geometry g, RowTable rt)
     const int32_t s0 = rt.start[b] + t0;
 
     const int64_t unit = ((int64_t)(g.l0 + li) * g.B + b) * g.H + h;
-    uint4 *kc = g.k + unit * C * g.Smax + s0;           // chunk c, token i: kc[c*Smax + i]
-    uint4 *vc = g.v + (unit * g.Smax + s0) * C;         // nvec contiguous vectors
+    u32x4 *kc = (u32x4 *)(g.k + unit * C * g.Smax + s0);     // chunk c, token i: kc[c*Smax + i]
+    u32x4 *vc = (u32x4 *)(g.v + (unit * g.Smax + s0) * C);   // nvec contiguous vectors
     const int64_t blk = (int64_t)g.H * g.T * C;
-    uint4 *ks = g.stage + 2 * (int64_t)li * blk + ((int64_t)g.H * off + (int64_t)h * cnt + t0) * C;
-    uint4 *vs = ks + blk;                               // both nvec contiguous vectors
+    u32x4 *ks = (u32x4 *)(g.stage + 2 * (int64_t)li * blk +
+                          ((int64_t)g.H * off + (int64_t)h * cnt + t0) * C);
+    u32x4 *vs = ks + blk;                                    // both nvec contiguous vectors
     const int tid = threadIdx.x;
+    u32x4 kr[PER], vr[PER];
 
-    // Element e = tid + p*256 of the tile is read as (chunk e/TT, token e%TT)
-    // on the cache side (chunk-major) and as (token e/C, chunk e%C) on the
-    // packed side (token-major).  Four vectors of K and four of V per thread,
-    // kept in named registers (arrays here end up in scratch).
-    uint4 k0, k1, k2, k3, v0, v1, v2, v3;
-#define KVS_CHUNK_OK(e, c, i) ((c) < C && (i) < nt)
     if (kPack) {
-#define KVS_LOAD(p, kk, vv)                                               \
-    {                                                                     \
-        const int e = tid + (p) * kThreads, c = e / TT, i = e % TT;       \
-        if (KVS_CHUNK_OK(e, c, i))                                        \
-            kk = kc[(int64_t)c * g.Smax + i];                             \
-        if (e < nvec)                                                     \
-            vv = vc[e];                                                   \
-    }
-        KVS_LOAD(0, k0, v0) KVS_LOAD(1, k1, v1) KVS_LOAD(2, k2, v2) KVS_LOAD(3, k3, v3)
-#undef KVS_LOAD
-#define KVS_STAGE(p, kk, vv)                                              \
-    {                                                                     \
-        const int e = tid + (p) * kThreads, c = e / TT, i = e % TT;       \
-        if (KVS_CHUNK_OK(e, c, i))                                        \
-            lds[lds_slot<CT>(i, c, C)] = kk;                              \
-        if (e < nvec)                                                     \
-            vs[e] = vv;                                                   \
-    }
-        KVS_STAGE(0, k0, v0) KVS_STAGE(1, k1, v1) KVS_STAGE(2, k2, v2) KVS_STAGE(3, k3, v3)
-#undef KVS_STAGE
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + p * kThreads, c = e / TT, i = e % TT;
+            if (c < C && i < nt)
+                kr[p] = kc[(int64_t)c * g.Smax + i];
+            if (e < nvec)
+                vr[p] = vc[e];
+        }
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + p * kThreads, c = e / TT, i = e % TT;
+            if (c < C && i < nt)
+                lds[lds_slot<CT>(i, c, C)] = kr[p];
+            if (e < nvec)
+                vs[e] = vr[p];
+        }
         __syncthreads();
-#define KVS_STORE(p)                                                      \
-    {                                                                     \
-        const int e = tid + (p) * kThreads;                               \
-        if (e < nvec)                                                     \
-            ks[e] = lds[lds_slot<CT>(e / C, e % C, C)];                   \
-    }
-        KVS_STORE(0) KVS_STORE(1) KVS_STORE(2) KVS_STORE(3)
-#undef KVS_STORE
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + p * kThreads;
+            if (e < nvec)
+                ks[e] = lds[lds_slot<CT>(e / C, e % C, C)];
+        }
     } else {
-#define KVS_LOAD(p, kk, vv)                                               \
-    {                                                                     \
-        const int e = tid + (p) * kThreads;                               \
-        if (e < nvec) {                                                   \
-            kk = ks[e];                                                   \
-            vv = vs[e];                                                   \
-        }                                                                 \
-    }
-        KVS_LOAD(0, k0, v0) KVS_LOAD(1, k1, v1) KVS_LOAD(2, k2, v2) KVS_LOAD(3, k3, v3)
-#undef KVS_LOAD
-#define KVS_STAGE(p, kk, vv)                                              \
-    {                                                                     \
-        const int e = tid + (p) * kThreads;                               \
-        if (e < nvec) {                                                   \
-            lds[lds_slot<CT>(e / C, e % C, C)] = kk;                      \
-            vc[e] = vv;                                                   \
-        }                                                                 \
-    }
-        KVS_STAGE(0, k0, v0) KVS_STAGE(1, k1, v1) KVS_STAGE(2, k2, v2) KVS_STAGE(3, k3, v3)
-#undef KVS_STAGE
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + p * kThreads;
+            if (e < nvec) {
+                kr[p] = ks[e];
+                vr[p] = vs[e];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + p * kThreads;
+            if (e < nvec) {
+                lds[lds_slot<CT>(e / C, e % C, C)] = kr[p];
+                vc[e] = vr[p];
+            }
+        }
         __syncthreads();
-#define KVS_STORE(p)                                                      \
-    {                                                                     \
-        const int e = tid + (p) * kThreads, c = e / TT, i = e % TT;       \
-        if (KVS_CHUNK_OK(e, c, i))                                        \
-            kc[(int64_t)c * g.Smax + i] = lds[lds_slot<CT>(i, c, C)];     \
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + p * kThreads, c = e / TT, i = e % TT;
+            if (c < C && i < nt)
+                kc[(int64_t)c * g.Smax + i] = lds[lds_slot<CT>(i, c, C)];
+        }
     }
-        KVS_STORE(0) KVS_STORE(1) KVS_STORE(2) KVS_STORE(3)
-#undef KVS_STORE
-    }
-#undef KVS_CHUNK_OK
 }
+
+// Vectors per thread of the tile kernel: 512-vector tiles (two per thread)
+// for heads of up to 16 vectors -- more workgroups per launch, which fills
+// the 256 CUs better on the 50-70 MB slices of one layer -- and 1024-vector
+// tiles for wider heads, so that a tile still spans at least 8 tokens.
+constexpr int tile_per_thread(int32_t C) { return C <= 16 ? 2 : 4; }
 
 template <bool kPack>
 hipError_t launch_tiles_rt(const Geometry &g, const RowTable &rt, int64_t blocks, hipStream_t s)
 {
     const dim3 grid((unsigned)blocks), block(kThreads);
     switch (g.C) {
-    case 1: copy_tiles<1, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 2: copy_tiles<2, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 4: copy_tiles<4, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 8: copy_tiles<8, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 16: copy_tiles<16, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 32: copy_tiles<32, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 64: copy_tiles<64, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 128: copy_tiles<128, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    default: copy_tiles<0, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 1: copy_tiles<1, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 2: copy_tiles<2, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 4: copy_tiles<4, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 8: copy_tiles<8, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 16: copy_tiles<16, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 32: copy_tiles<32, 4, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 64: copy_tiles<64, 4, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 128: copy_tiles<128, 4, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    default:
+        if (tile_per_thread(g.C) == 2)
+            copy_tiles<0, 2, kPack><<<grid, block, 0, s>>>(g, rt);
+        else
+            copy_tiles<0, 4, kPack><<<grid, block, 0, s>>>(g, rt);
+        break;
     }
     return hipGetLastError();
+}
+
+int tile_tokens_for(int32_t C)
+{
+    const int tv = kThreads * tile_per_thread(C);
+    return C >= tv ? 1 : tv / C;
 }
 
 // Transfer between a staging bank in HBM and pinned host memory, run by the
 // GPU's own load/store units instead of a DMA engine (the host buffer is
 // mapped into the GPU's address space).  Each thread keeps four 16-byte
-// vectors in flight; the grid is capped so that the copy occupies a fraction
-// of the compute units while it waits on the host link.  Loads from host
-// memory and stores to it are non-temporal (the data is touched once).
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// vectors in flight.
+//
+// Device->host stores go through a bounds-checked buffer resource with the
+// system-coherent, non-temporal cache policy (sc0 sc1 nt), from a small grid
+// (8 workgroups by default).  Measured on MI355X: that keeps the host link at
+// ~56 GB/s while leaving co-running HBM kernels at their own speed; ordinary
+// stores to host memory from many workgroups hold up other kernels' HBM
+// traffic several-fold.  Host->device reads use non-temporal loads.
+constexpr int kHostStorePolicy = 1 | 2 | 16;   // sc0 | nt | sc1
 
 template <bool kToHost>
 __global__ __launch_bounds__(kThreads) void link_copy(const u32x4 *__restrict__ src,
-                                                      u32x4 *__restrict__ dst, int64_t nvec)
+                                                      u32x4 *__restrict__ dst, int32_t nvec)
 {
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    for (; i + 3 * stride < nvec; i += 4 * stride) {
-        u32x4 a, b, c, d;
-        if (kToHost) {
-            a = src[i];
-            b = src[i + stride];
-            c = src[i + 2 * stride];
-            d = src[i + 3 * stride];
-            __builtin_nontemporal_store(a, dst + i);
-            __builtin_nontemporal_store(b, dst + i + stride);
-            __builtin_nontemporal_store(c, dst + i + 2 * stride);
-            __builtin_nontemporal_store(d, dst + i + 3 * stride);
-        } else {
-            a = __builtin_nontemporal_load(src + i);
-            b = __builtin_nontemporal_load(src + i + stride);
-            c = __builtin_nontemporal_load(src + i + 2 * stride);
-            d = __builtin_nontemporal_load(src + i + 3 * stride);
+    const int32_t stride = (int32_t)gridDim.x * kThreads;
+    int32_t i = (int32_t)blockIdx.x * kThreads + threadIdx.x;
+    if (kToHost) {
+        // num_records = nvec * 16 bytes (< 2^31 per launch): out-of-range stores are dropped
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(dst, 0, nvec * 16, 0x00020000);
+        for (; i + 3 * stride < nvec; i += 4 * stride) {
+            const u32x4 a = src[i], b = src[i + stride];
+            const u32x4 c = src[i + 2 * stride], d = src[i + 3 * stride];
+            __builtin_amdgcn_raw_buffer_store_b128(a, r, i * 16, 0, kHostStorePolicy);
+            __builtin_amdgcn_raw_buffer_store_b128(b, r, (i + stride) * 16, 0, kHostStorePolicy);
+            __builtin_amdgcn_raw_buffer_store_b128(c, r, (i + 2 * stride) * 16, 0, kHostStorePolicy);
+            __builtin_amdgcn_raw_buffer_store_b128(d, r, (i + 3 * stride) * 16, 0, kHostStorePolicy);
+        }
+        for (; i < nvec; i += stride)
+            __builtin_amdgcn_raw_buffer_store_b128(src[i], r, i * 16, 0, kHostStorePolicy);
+        __threadfence_system();   // host-visible before the kernel completes
+    } else {
+        for (; i + 3 * stride < nvec; i += 4 * stride) {
+            const u32x4 a = __builtin_nontemporal_load(src + i);
+            const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+            const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+            const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
             dst[i] = a;
             dst[i + stride] = b;
             dst[i + 2 * stride] = c;
             dst[i + 3 * stride] = d;
         }
-    }
-    for (; i < nvec; i += stride) {
-        if (kToHost)
-            __builtin_nontemporal_store(src[i], dst + i);
-        else
+        for (; i < nvec; i += stride)
             dst[i] = __builtin_nontemporal_load(src + i);
     }
-    if (kToHost)
-        __threadfence_system();   // host-visible before the kernel completes
 }
 
-int link_blocks()
+// Workgroups of one link copy (KV_LINK_BLOCKS overrides, for tuning).
+int link_blocks(bool to_host)
 {
-    static const int n = [] {
+    static const int env = [] {
         const char *e = std::getenv("KV_LINK_BLOCKS");
         const int v = e ? std::atoi(e) : 0;
-        return v > 0 && v <= 65535 ? v : 128;
+        return v > 0 && v <= 65535 ? v : 0;
     }();
-    return n;
-}
-
-int tile_tokens_for(int32_t C)
-{
-    return C >= kTileVecs ? 1 : kTileVecs / C;
+    if (env)
+        return env;
+    return to_host ? 8 : 128;
 }
 
 }  // namespace
@@ -356,19 +364,29 @@ int launch_link_copy(void *dst, const void *src, int64_t bytes, bool to_host, hi
     if (bytes % 16 != 0 || ((uintptr_t)dst | (uintptr_t)src) % 16 != 0)
         return set_error(KV_EINVAL, "link copy of %lld bytes is not in whole 16-byte vectors",
                          (long long)bytes);
-    const int64_t nvec = bytes / 16;
-    const int64_t blocks = std::min<int64_t>(link_blocks(), (nvec + kThreads - 1) / kThreads);
     const char *name = to_host ? "link_copy_d2h" : "link_copy_h2d";
-    void *tok = profiling_enabled() ? profile_start(s) : nullptr;
-    const dim3 grid((unsigned)blocks), block(kThreads);
-    if (to_host)
-        link_copy<true><<<grid, block, 0, s>>>((const u32x4 *)src, (u32x4 *)dst, nvec);
-    else
-        link_copy<false><<<grid, block, 0, s>>>((const u32x4 *)src, (u32x4 *)dst, nvec);
-    const hipError_t e = hipGetLastError();
-    if (tok)
-        profile_stop(tok, s, name, bytes);
-    return e == hipSuccess ? KV_OK : hip_fail(e, name);
+    // one launch per piece of at most 1 GiB: 32-bit offsets inside a launch
+    constexpr int64_t kPiece = int64_t(1) << 30;
+    for (int64_t done = 0; done < bytes; done += kPiece) {
+        const int64_t n = std::min(kPiece, bytes - done);
+        const int32_t nvec = (int32_t)(n / 16);
+        const int64_t blocks =
+            std::min<int64_t>(link_blocks(to_host), (nvec + kThreads - 1) / kThreads);
+        const u32x4 *from = (const u32x4 *)((const char *)src + done);
+        u32x4 *to = (u32x4 *)((char *)dst + done);
+        void *tok = profiling_enabled() ? profile_start(s) : nullptr;
+        const dim3 grid((unsigned)blocks), block(kThreads);
+        if (to_host)
+            link_copy<true><<<grid, block, 0, s>>>(from, to, nvec);
+        else
+            link_copy<false><<<grid, block, 0, s>>>(from, to, nvec);
+        const hipError_t e = hipGetLastError();
+        if (tok)
+            profile_stop(tok, s, name, n);
+        if (e != hipSuccess)
+            return hip_fail(e, name);
+    }
+    return KV_OK;
 }
 
 }  // namespace kvs
