@@ -1,0 +1,362 @@
+"""The five workloads at full size, in the bench's launch configuration.
+
+Each test runs a workload's call sequence on its real shape (transport
+KV_XFER_AUTO, two staging banks, the ring sizes of the workload) and compares
+with the oracle bit for bit: whole buffers where the host can hold the
+oracle's inputs, otherwise complete layers or chunks sampled from every part of
+the flow (the oracle on one layer of the cache, a property the pins fix: a
+multi-layer pack is the concatenation of its per-layer packs).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import note, pinned, pinned_host_view
+
+pytestmark = pytest.mark.gpu
+
+MiB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def kv():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+    import kv_cache_streaming_amd as kv
+    return kv
+
+
+@pytest.fixture(autouse=True)
+def free_memory():
+    """Give device memory and cached pinned host memory back after each test
+    (the workloads pin tens of GB of host memory each)."""
+    import gc
+
+    import torch
+    yield
+    torch.cuda.synchronize()
+    gc.collect()
+    torch.cuda.empty_cache()
+    torch._C._host_emptyCache()
+
+
+def device_cache(w, seed):
+    import torch
+    n = w.L * w.B * w.H * w.D * w.Smax
+    k = torch.empty(n, dtype=torch.int16, device="cuda")
+    v = torch.empty(n, dtype=torch.int16, device="cuda")
+    synth.fill_device_cache(k, seed, w.dtype)
+    synth.fill_device_cache(v, seed + 1, w.dtype)
+    return k, v
+
+
+def layer_host(t, w, l):
+    """uint16 host copy of layer l of a flat device cache tensor."""
+    return t.view(w.L, -1)[l].cpu().numpy().view(np.uint16).copy()
+
+
+def one_layer(w):
+    return (1, w.B, w.H, w.D, w.Smax)
+
+
+def bank(nbytes):
+    import torch
+    return torch.empty((nbytes + 15) // 16 * 8, dtype=torch.int16, device="cuda")
+
+
+def test_gpt2_small_tiny_full_flow(kv):
+    """12 prompt-layer packs of 32 tokens, 16 decode steps into a ring of 8, restore
+    into a fresh zeroed cache (round-trip identity on the decode region)."""
+    import torch
+    w = synth.WORKLOADS["gpt2-small-tiny"]
+    note(f"workload {w.name} dims={w.dims}")
+    K, V = synth.cache_pair(w.dims, w.value_seed, w.dtype)
+    lay = kv.kv_layout_init(*w.dims, w.dtype)
+    dk = torch.from_numpy(K.view(np.int16)).cuda()
+    dv = torch.from_numpy(V.view(np.int16)).cuda()
+    lens = synth.row_lengths(w)
+    for l in range(w.L):
+        want = oracle.pack(w.dims, K, V, l, 1, [0] * w.B, lens)
+        st = torch.empty(want.size, dtype=torch.int16, device="cuda")
+        kv.kv_pack_prompt_layer(lay, dk, dv, l, 0, w.prompt_len, None, st)
+        torch.cuda.synchronize()
+        assert np.array_equal(st.cpu().numpy().view(np.uint16), want), f"prompt layer {l}"
+    pos = synth.decode_positions(w)
+    slot = kv.kv_pack_bytes(lay, w.L, None, 1)
+    R = w.ring_slots
+    host = pinned(w.decode_steps * slot // 2)
+    ring = kv.KvRing(lay, R, bank(R * slot), bank(R * slot), host, copy_stream=torch.cuda.Stream())
+    for p in pos:
+        ring.push(dk, dv, p)
+    done = torch.cuda.Event()
+    ring.flush(None, done)
+    done.synchronize()
+    want = oracle.ring_host([oracle.pack(w.dims, K, V, 0, w.L, p, [1] * w.B) for p in pos])
+    assert np.array_equal(pinned_host_view(host), want), "ring host image"
+    zk, zv = torch.zeros_like(dk), torch.zeros_like(dv)
+    ring.restore(zk, zv)
+    ek, ev = np.zeros_like(K), np.zeros_like(V)
+    oracle.ring_restore(w.dims, ek, ev, pos, want)
+    torch.cuda.synchronize()
+    assert np.array_equal(zk.cpu().numpy().view(np.uint16), ek)
+    assert np.array_equal(zv.cpu().numpy().view(np.uint16), ev)
+    ring.close()
+
+
+def test_gpt2_1p5b_full_flow(kv):
+    """48 streamed prompt layers (1000 tokens), 24 decode steps flushed every 8,
+    restore into a zeroed cache, microbatch swap-out/in of all 1024 positions."""
+    import torch
+    w = synth.WORKLOADS["gpt2-1.5b"]
+    note(f"workload {w.name} dims={w.dims}")
+    lay = kv.kv_layout_init(*w.dims, w.dtype)
+    dk, dv = device_cache(w, w.value_seed)
+    K = dk.cpu().numpy().view(np.uint16)
+    V = dv.cpu().numpy().view(np.uint16)
+    B = w.B
+    prompt = [w.prompt_len] * B
+    layer_bytes = kv.kv_pack_bytes(lay, 1, prompt)
+    copy_out, copy_in = torch.cuda.Stream(), torch.cuda.Stream()
+    eng = kv.KvSwap(lay, bank(layer_bytes), bank(layer_bytes), layer_bytes, copy_out)
+    host = pinned(w.L * layer_bytes // 2)
+    done = torch.cuda.Event()
+    for l in range(w.L):
+        eng.stream_prompt_layer(dk, dv, l, 0, w.prompt_len, None,
+                                host.data_ptr() + l * layer_bytes, layer_bytes, None, done)
+    done.synchronize()
+    hv = pinned_host_view(host)
+    for l in range(w.L):
+        want = oracle.pack(w.dims, K, V, l, 1, [0] * B, prompt)
+        assert np.array_equal(hv[l * want.size:(l + 1) * want.size], want), f"prompt layer {l}"
+    # decode ring
+    pos = synth.decode_positions(w)
+    slot = kv.kv_pack_bytes(lay, w.L, None, 1)
+    R = w.ring_slots
+    rhost = pinned(w.decode_steps * slot // 2)
+    ring = kv.KvRing(lay, R, bank(R * slot), bank(R * slot), rhost, copy_stream=copy_out)
+    for p in pos:
+        ring.push(dk, dv, p)
+    ring.flush(None, done)
+    done.synchronize()
+    want = oracle.ring_host([oracle.pack(w.dims, K, V, 0, w.L, p, [1] * B) for p in pos])
+    assert np.array_equal(pinned_host_view(rhost), want), "ring host image"
+    rk, rv = torch.zeros_like(dk), torch.zeros_like(dv)
+    ring.restore(rk, rv)
+    ek, ev = np.zeros_like(K), np.zeros_like(V)
+    oracle.ring_restore(w.dims, ek, ev, pos, want)
+    torch.cuda.synchronize()
+    assert np.array_equal(rk.cpu().numpy().view(np.uint16), ek), "restored K"
+    assert np.array_equal(rv.cpu().numpy().view(np.uint16), ev), "restored V"
+    del rk, rv, ek, ev
+    # microbatch swap-out of all 1024 positions, swap-in to a sentinel cache
+    full = [w.Smax] * B
+    total = kv.kv_pack_bytes(lay, w.L, full)
+    sb = 256 * MiB
+    eo = kv.KvSwap(lay, bank(sb), bank(sb), sb, copy_out)
+    ei = kv.KvSwap(lay, bank(sb), bank(sb), sb, copy_in)
+    shost = pinned(total // 2)
+    eo.swap_out(dk, dv, 0, w.L, [0] * B, full, shost, total, None, done)
+    done.synchronize()
+    sv = pinned_host_view(shost)
+    per = total // 2 // w.L
+    for l in range(w.L):
+        want = oracle.pack(w.dims, K, V, l, 1, [0] * B, full)
+        assert np.array_equal(sv[l * per:(l + 1) * per], want), f"swap-out layer {l}"
+    sk = torch.full_like(dk, 0x1357)
+    svv = torch.full_like(dv, 0x2468)
+    ei.swap_in(sk, svv, 0, w.L, [0] * B, full, shost, total)
+    torch.cuda.synchronize()
+    assert torch.equal(sk, dk) and torch.equal(svv, dv), "swap-in of every position restores the cache"
+    ring.close()
+    eng.close()
+    eo.close()
+    ei.close()
+
+
+def test_opt66b_slice_decode_ring(kv):
+    """Ragged decode positions (len_b + j), 64 steps into a ring of 16 flushed to
+    pinned host memory, restored into a second, zeroed cache."""
+    import torch
+    w = synth.WORKLOADS["opt-66b-16l"]
+    note(f"workload {w.name} dims={w.dims}")
+    lay = kv.kv_layout_init(*w.dims, w.dtype)
+    dk, dv = device_cache(w, w.value_seed)
+    K = dk.cpu().numpy().view(np.uint16)
+    V = dv.cpu().numpy().view(np.uint16)
+    pos = synth.decode_positions(w)
+    assert pos.max() < w.Smax
+    slot = kv.kv_pack_bytes(lay, w.L, None, 1)
+    assert slot == 4_718_592
+    R = w.ring_slots
+    host = pinned(w.decode_steps * slot // 2)
+    ring = kv.KvRing(lay, R, bank(R * slot), bank(R * slot), host, copy_stream=torch.cuda.Stream())
+    for p in pos:
+        ring.push(dk, dv, p)
+    done = torch.cuda.Event()
+    ring.flush(None, done)
+    done.synchronize()
+    want = oracle.ring_host([oracle.pack(w.dims, K, V, 0, w.L, p, [1] * w.B) for p in pos])
+    assert np.array_equal(pinned_host_view(host), want), "ring host image"
+    rk, rv = torch.zeros_like(dk), torch.zeros_like(dv)
+    ring.restore(rk, rv)
+    ek, ev = np.zeros_like(K), np.zeros_like(V)
+    oracle.ring_restore(w.dims, ek, ev, pos, want)
+    torch.cuda.synchronize()
+    assert np.array_equal(rk.cpu().numpy().view(np.uint16), ek), "restored K"
+    assert np.array_equal(rv.cpu().numpy().view(np.uint16), ev), "restored V"
+    ring.close()
+
+
+def test_bloom_slice_microbatch_swap(kv):
+    """Two device slots: swap out microbatch x-1 from slot B while microbatch x+1
+    is swapped in to slot A from its host image (layer-pipelined, duplex), then
+    the reverse; full 1500-token microbatches of 13.76 GB."""
+    import torch
+    w = synth.WORKLOADS["bloom-176b-10l"]
+    note(f"workload {w.name} dims={w.dims}")
+    lay = kv.kv_layout_init(*w.dims, w.dtype)
+    B = w.B
+    rows = [w.prompt_len] * B
+    total = kv.kv_pack_bytes(lay, w.L, rows)
+    assert total == 13_762_560_000
+    slot_a = device_cache(w, w.value_seed)          # microbatch 0 lives in slot A
+    slot_b = device_cache(w, w.value_seed + 40)     # microbatch 1 lives in slot B
+    sb = 256 * MiB
+    copy_out, copy_in = torch.cuda.Stream(), torch.cuda.Stream()
+    eo = kv.KvSwap(lay, bank(sb), bank(sb), sb, copy_out)
+    ei = kv.KvSwap(lay, bank(sb), bank(sb), sb, copy_in)
+    host = [pinned(total // 2) for _ in range(2)]
+    per = total // 2 // w.L
+    s_a, s_b = torch.cuda.Stream(), torch.cuda.Stream()
+    # initial swap-out of microbatch 0 (slot A) to host[0]
+    done = torch.cuda.Event()
+    eo.swap_out(slot_a[0], slot_a[1], 0, w.L, [0] * B, rows, host[0], total, s_a, done)
+    done.synchronize()
+    samples = (0, 7)
+    ref_a = {l: (layer_host(slot_a[0], w, l), layer_host(slot_a[1], w, l)) for l in samples}
+    hv0 = pinned_host_view(host[0])
+    for l in samples:
+        want = oracle.pack(one_layer(w), ref_a[l][0], ref_a[l][1], 0, 1, [0] * B, rows)
+        assert np.array_equal(hv0[l * per:(l + 1) * per], want), f"swap-out mb0 layer {l}"
+    ref_b = {l: (layer_host(slot_b[0], w, l), layer_host(slot_b[1], w, l)) for l in samples}
+    # duplex round: swap out microbatch 1 from slot B to host[1] while microbatch 0
+    # comes back into slot A (overwritten first with a sentinel) from host[0]
+    slot_a[0].fill_(0x0BAD)
+    slot_a[1].fill_(0x0BAD)
+    torch.cuda.synchronize()
+    d_out, d_in = torch.cuda.Event(), torch.cuda.Event()
+    for l in range(w.L):
+        eo.swap_out(slot_b[0], slot_b[1], l, 1, [0] * B, rows, host[1].data_ptr() + l * per * 2,
+                    per * 2, s_b, d_out)
+        ei.swap_in(slot_a[0], slot_a[1], l, 1, [0] * B, rows, host[0].data_ptr() + l * per * 2,
+                   per * 2, s_a, d_in)
+    d_out.synchronize()
+    d_in.synchronize()
+    torch.cuda.synchronize()
+    hv1 = pinned_host_view(host[1])
+    for l in samples:
+        want = oracle.pack(one_layer(w), ref_b[l][0], ref_b[l][1], 0, 1, [0] * B, rows)
+        assert np.array_equal(hv1[l * per:(l + 1) * per], want), f"swap-out mb1 layer {l}"
+        ek = np.full_like(ref_a[l][0], 0x0BAD)
+        ev = np.full_like(ref_a[l][1], 0x0BAD)
+        oracle.unpack(one_layer(w), ek, ev, 0, 1, [0] * B, rows, hv0[l * per:(l + 1) * per])
+        assert np.array_equal(layer_host(slot_a[0], w, l), ek), f"swap-in mb0 K layer {l}"
+        assert np.array_equal(layer_host(slot_a[1], w, l), ev), f"swap-in mb0 V layer {l}"
+    eo.close()
+    ei.close()
+
+
+def test_gqa_100k_long_context(kv):
+    """bf16, Smax = 100000, ragged rows: 4096-token prompt chunks per layer, 64
+    ragged decode steps into a ring of 16, swap-out/in of the longest row."""
+    import torch
+    w = synth.WORKLOADS["gqa-100k"]
+    note(f"workload {w.name} dims={w.dims}")
+    lay = kv.kv_layout_init(*w.dims, w.dtype)
+    B = w.B
+    lens = synth.row_lengths(w)
+    dk, dv = device_cache(w, w.value_seed)
+    lk, lv = {}, {}
+
+    def host_layer(l):
+        if l not in lk:
+            lk[l], lv[l] = layer_host(dk, w, l), layer_host(dv, w, l)
+        return lk[l], lv[l]
+
+    # chunked prompt packs: every chunk of layer 0, first and last chunks of two others
+    chunk = w.chunk_tokens
+    nchunks = (int(lens.max()) + chunk - 1) // chunk
+    st = bank(kv.kv_pack_bytes(lay, 1, None, chunk))
+    cases = [(0, c) for c in range(nchunks)] + [(59, 0), (59, nchunks - 1), (31, 0),
+                                                 (31, nchunks // 2), (31, nchunks - 1)]
+    for l, c in cases:
+        tb = c * chunk
+        tc = min(chunk, w.Smax - tb)
+        start, count = oracle.prompt_ranges(B, tb, tc, lens)
+        need = kv.kv_pack_bytes(lay, 1, count)
+        if need == 0:
+            continue
+        kv.kv_pack_prompt_layer(lay, dk, dv, l, tb, tc, lens, st, need)
+        torch.cuda.synchronize()
+        K1, V1 = host_layer(l)
+        want = oracle.pack(one_layer(w), K1, V1, 0, 1, start, count)
+        got = st.cpu().numpy().view(np.uint16)[:want.size]
+        assert np.array_equal(got, want), f"prompt chunk layer {l} chunk {c}"
+    # decode ring, ragged positions
+    pos = synth.decode_positions(w)
+    assert pos.max() < w.Smax
+    slot = kv.kv_pack_bytes(lay, w.L, None, 1)
+    assert slot == 983_040
+    R = w.ring_slots
+    host = pinned(w.decode_steps * slot // 2)
+    ring = kv.KvRing(lay, R, bank(R * slot), bank(R * slot), host, copy_stream=torch.cuda.Stream())
+    for p in pos:
+        ring.push(dk, dv, p)
+    done = torch.cuda.Event()
+    ring.flush(None, done)
+    done.synchronize()
+    hv = pinned_host_view(host)
+    per_layer = slot // 2 // w.L
+    for l in (0, 31, 59):
+        K1, V1 = host_layer(l)
+        for j, p in enumerate(pos):
+            want = oracle.pack(one_layer(w), K1, V1, 0, 1, p, [1] * B)
+            got = hv[j * (slot // 2) + l * per_layer:j * (slot // 2) + (l + 1) * per_layer]
+            assert np.array_equal(got, want), f"ring step {j} layer {l}"
+    ring.close()
+    # swap-out of the longest row over all 60 layers, then swap-in after the row is
+    # overwritten with a sentinel
+    bstar = int(np.argmax(lens))
+    count = [0] * B
+    count[bstar] = int(lens[bstar])
+    total = kv.kv_pack_bytes(lay, w.L, count)
+    per = total // 2 // w.L
+    sb = 512 * MiB
+    copy_out, copy_in = torch.cuda.Stream(), torch.cuda.Stream()
+    eo = kv.KvSwap(lay, bank(sb), bank(sb), sb, copy_out)
+    ei = kv.KvSwap(lay, bank(sb), bank(sb), sb, copy_in)
+    shost = pinned(total // 2)
+    eo.swap_out(dk, dv, 0, w.L, [0] * B, count, shost, total, None, done)
+    done.synchronize()
+    sv = pinned_host_view(shost)
+    for l in (0, 31, 59):
+        K1, V1 = host_layer(l)
+        want = oracle.pack(one_layer(w), K1, V1, 0, 1, [0] * B, count)
+        assert np.array_equal(sv[l * per:(l + 1) * per], want), f"row swap-out layer {l}"
+    dk.view(w.L, B, -1)[:, bstar, :].fill_(0x7E7E)
+    dv.view(w.L, B, -1)[:, bstar, :].fill_(0x7E7E)
+    ei.swap_in(dk, dv, 0, w.L, [0] * B, count, shost, total)
+    torch.cuda.synchronize()
+    for l in (0, 31, 59):
+        K1, V1 = host_layer(l)
+        ek = K1.copy().reshape(B, -1)
+        ev = V1.copy().reshape(B, -1)
+        ek[bstar] = 0x7E7E
+        ev[bstar] = 0x7E7E
+        ek, ev = ek.reshape(-1), ev.reshape(-1)
+        oracle.unpack(one_layer(w), ek, ev, 0, 1, [0] * B, count, sv[l * per:(l + 1) * per])
+        assert np.array_equal(layer_host(dk, w, l), ek), f"row swap-in K layer {l}"
+        assert np.array_equal(layer_host(dv, w, l), ev), f"row swap-in V layer {l}"
+    eo.close()
+    ei.close()
