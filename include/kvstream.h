@@ -215,10 +215,12 @@ int kv_swap_out(kv_swap *e, const void *k, const void *v,
                 void *host, int64_t host_bytes, hipStream_t compute, hipEvent_t done);
 
 /* Swap-in: copy `host` (pinned, packed format) to the banks on the copy
- * stream, ordered after all work enqueued on `compute` before the call, and
- * unpack it into the caches on `compute`.  `done` (nullable) is recorded on
- * `compute` after the last unpack; later work on `compute` sees the restored
- * cache. */
+ * stream and unpack it into the caches on `compute`.  The copies wait only for
+ * the bank they overwrite to be free; the host image must already be complete
+ * when they run -- order its producer before the call on the copy stream (for
+ * instance hipStreamWaitEvent(copy, done of the swap-out that wrote it)) or on
+ * the host.  `done` (nullable) is recorded on `compute` after the last unpack;
+ * later work on `compute` sees the restored cache. */
 int kv_swap_in(kv_swap *e, void *k, void *v,
                int32_t layer_begin, int32_t layer_count,
                const int32_t *start, const int32_t *count,
@@ -280,8 +282,9 @@ int kv_ring_flush(kv_ring *r, hipStream_t compute, hipEvent_t done);
 /* Restore ([DV, Failure detection and recovery, Fig 10], data leg): copy the
  * host image back through the banks and unpack every step into (k, v) in
  * ascending step order (a later step wins where two name the same position).
- * Requires every pushed step flushed (else KV_EBUSY).  `done` (nullable) is
- * recorded on `compute` after the last unpack. */
+ * Requires every pushed step flushed (else KV_EBUSY).  The copies follow the
+ * ring's own flushes on the copy stream.  `done` (nullable) is recorded on
+ * `compute` after the last unpack. */
 int kv_ring_restore(kv_ring *r, void *k, void *v, hipStream_t compute, hipEvent_t done);
 
 /* Steps pushed so far, or a negative kv_status. */

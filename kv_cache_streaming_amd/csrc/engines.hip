@@ -183,12 +183,11 @@ struct kv_swap {
     int64_t bank_bytes;
     hipStream_t copy;
     int32_t transport;
-    hipEvent_t ev[5];            // free0, free1, filled0, filled1, call
+    hipEvent_t ev[4];            // free0, free1, filled0, filled1
     bool free_valid[2];
     int next;
     hipEvent_t free_ev(int b) const { return ev[b]; }
     hipEvent_t filled_ev(int b) const { return ev[2 + b]; }
-    hipEvent_t call_ev() const { return ev[4]; }
 };
 
 struct kv_ring {
@@ -204,12 +203,11 @@ struct kv_ring {
     int64_t slot_bytes;
     int64_t steps, flushed;
     std::vector<int32_t> pos;    // steps * B positions, in step order
-    hipEvent_t ev[5];            // free0, free1, filled0, filled1, call
+    hipEvent_t ev[4];            // free0, free1, filled0, filled1
     bool wait_needed[2];         // a push must wait on free_ev before writing the bank
     bool free_valid[2];          // free_ev has been recorded at least once
     hipEvent_t free_ev(int b) const { return ev[b]; }
     hipEvent_t filled_ev(int b) const { return ev[2 + b]; }
-    hipEvent_t call_ev() const { return ev[4]; }
 };
 
 namespace {
@@ -298,7 +296,7 @@ int kv_swap_create(kv_swap **out, const kv_layout *lay, void *bank0, void *bank1
     e->transport = transport;
     e->free_valid[0] = e->free_valid[1] = false;
     e->next = 0;
-    if ((st = create_events(e->ev, 5))) {
+    if ((st = create_events(e->ev, 4))) {
         delete e;
         return st;
     }
@@ -383,11 +381,6 @@ int kv_swap_in(kv_swap *e, void *k, void *v, int32_t layer_begin, int32_t layer_
     std::vector<Chunk> chunks;
     if ((st = plan_chunks(lay, layer_begin, layer_count, rt, e->bank_bytes, &chunks)))
         return st;
-    if (!chunks.empty()) {
-        if ((st = record(e->call_ev(), compute, "swap-in call")) ||
-            (st = wait(e->copy, e->call_ev(), "swap-in call wait")))
-            return st;
-    }
     for (const Chunk &c : chunks) {
         const int bk = e->next;
         e->next ^= 1;
@@ -502,7 +495,7 @@ int kv_ring_create(kv_ring **out, const kv_layout *lay, int32_t R, void *bank0, 
     r->steps = r->flushed = 0;
     r->wait_needed[0] = r->wait_needed[1] = false;
     r->free_valid[0] = r->free_valid[1] = false;
-    if ((st = create_events(r->ev, 5))) {
+    if ((st = create_events(r->ev, 4))) {
         delete r;
         return st;
     }
@@ -614,11 +607,6 @@ int kv_ring_restore(kv_ring *r, void *k, void *v, hipStream_t compute, hipEvent_
         return st;
     if ((st = check_banks_apart(r->bank, r->bank_bytes, lay, k, v)))
         return st;
-    if (r->steps > 0) {
-        if ((st = record(r->call_ev(), compute, "ring restore call")) ||
-            (st = wait(r->copy, r->call_ev(), "ring restore call wait")))
-            return st;
-    }
     for (int64_t j0 = 0, g = 0; j0 < r->steps; j0 += r->R, ++g) {
         const int64_t n = std::min<int64_t>(r->R, r->steps - j0);
         const int bk = (int)(g & 1);
