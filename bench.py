@@ -211,6 +211,55 @@ def hbm_copy_ceiling(torch, nbytes=1 << 30, reps=4):
     return gbps
 
 
+def large_slices(step, kv, reps=3):
+    """Isolated rates on the workload's largest slices: one pack and one unpack
+    of every layer and position of cache B (2.5 GB of payload in one call), and
+    one whole-cache swap per link direction alone."""
+    torch, w = step.torch, step.w
+    L, B = w.L, w.B
+    full = [w.Smax] * B
+    payload = kv.kv_pack_bytes(step.lay, L, full)
+    st = torch.empty(payload // 2, dtype=torch.int16, device="cuda")
+    Bc, Cc = step.caches["B"], step.caches["C"]
+    s = step.s["t"]
+    out = {"payload_bytes": payload}
+    for name, fn in (("pack", lambda: kv.kv_pack_tokens(step.lay, Bc[0], Bc[1], 0, L, [0] * B, full,
+                                                       st, payload, s)),
+                     ("unpack", lambda: kv.kv_unpack_tokens(step.lay, Cc[0], Cc[1], 0, L, [0] * B,
+                                                           full, st, payload, s))):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1000 / reps
+        out[name + "_us"] = round(sec * 1e6, 1)
+        out[name + "_hbm_GBps"] = round(2 * payload / sec / 1e9, 1)
+        out[name + "_frac_of_peak"] = round(2 * payload / sec / 1e9 / HBM_PEAK_GBPS, 4)
+    del st
+    lf = step.layer_full
+    hs = step.host_s[0].data_ptr()
+    for name, fn in (("swap_out", lambda: [step.eng_o.swap_out(Bc[0], Bc[1], l, 1, step.rows_start,
+                                                              step.rows_full, hs + l * lf, lf, s)
+                                           for l in range(L)]),
+                     ("swap_in", lambda: [step.eng_i.swap_in(Cc[0], Cc[1], l, 1, step.rows_start,
+                                                            step.rows_full, hs + l * lf, lf, s)
+                                          for l in range(L)])):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / reps
+        out[name + "_link_GBps"] = round(L * lf / sec / 1e9, 2)
+        out[name + "_frac_of_pcie"] = round(L * lf / sec / 1e9 / PCIE_PEAK_GBPS, 4)
+    return out
+
+
 def decode_push_us(step, reps=3):
     torch = step.torch
     st = step.s["t"]
@@ -371,6 +420,7 @@ def main():
         detail["decode_push_us"] = round(decode_push_us(step), 2)
         detail["link_ceiling_GBps"] = {k: round(v, 2) for k, v in link_ceiling(torch).items()}
         detail["hbm_copy_ceiling_GBps"] = round(hbm_copy_ceiling(torch), 1)
+        detail["large_slices"] = large_slices(step, kv)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(step, args.cpu_baseline_seconds)
