@@ -287,11 +287,51 @@ int kv_ring_flush(kv_ring *r, hipStream_t compute, hipEvent_t done);
  * `compute` after the last unpack. */
 int kv_ring_restore(kv_ring *r, void *k, void *v, hipStream_t compute, hipEvent_t done);
 
+/* Restore only steps [0, n) (n <= steps flushed so far; else KV_ERANGE), as
+ * after a failure when only the replicated prefix survives.  The ring then
+ * continues from step n: later steps are dropped, and the next push is step
+ * n (its slot overwrites the host image from there on). */
+int kv_ring_restore_steps(kv_ring *r, void *k, void *v, int64_t n, hipStream_t compute,
+                          hipEvent_t done);
+
 /* Steps pushed so far, or a negative kv_status. */
 int64_t kv_ring_steps(const kv_ring *r);
 
+/* Steps whose flush copy to the host has completed, so that the host image
+ * (the replica) holds steps [0, n): a non-blocking query of the ring's flush
+ * events ([DV, Failure detection and recovery]: a worker acknowledges a
+ * step once its update has reached the replica).  Negative kv_status on
+ * error. */
+int64_t kv_ring_durable_steps(kv_ring *r);
+
 /* Forget all steps (the host image and banks are reused from step 0). */
 int kv_ring_reset(kv_ring *r);
+
+/* ---------------------------------------------------------------------------
+ * Acknowledgement log and restart point ([DV, Failure detection and
+ * recovery, Fig 10]).  Worker x acknowledges (x, j, t) once the replica holds
+ * microbatch j's KV up to and including step t.  After a failure the pipeline
+ * restarts at one (microbatch j, step t).  Reading taken here: a
+ * (microbatch, step) pair is replicated when every worker has acknowledged
+ * it; steps run in (step, microbatch) order -- every microbatch's step t
+ * before any microbatch's step t+1 -- and the restart point is the earliest
+ * pair in that order that is not replicated, i.e. the smallest
+ * (t_j + 1, j) with t_j = min over workers of the last step acknowledged for
+ * microbatch j (-1 when none).  Host-only.
+ */
+typedef struct kv_acklog kv_acklog;
+
+/* workers >= 1, microbatches >= 1 (else KV_EINVAL). */
+int kv_acklog_create(kv_acklog **out, int32_t workers, int32_t microbatches);
+int kv_acklog_destroy(kv_acklog *a);
+
+/* Record (x, j, t); x in [0, workers), j in [0, microbatches), t >= 0 (else
+ * KV_ERANGE).  Acks may arrive out of order: an ack for an earlier step than
+ * one already recorded for (x, j) changes nothing. */
+int kv_ack(kv_acklog *a, int32_t x, int32_t j, int64_t t);
+
+/* The restart point (j, t) under the rule above. */
+int kv_ack_restart_point(const kv_acklog *a, int32_t *j, int64_t *t);
 
 /* ---------------------------------------------------------------------------
  * Live kernel timing.  Between kv_profile_begin and kv_profile_end every pack

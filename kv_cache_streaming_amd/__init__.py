@@ -91,7 +91,13 @@ _SIGNATURES = {
     "kv_ring_push": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "kv_ring_flush": (ctypes.c_int, [_P, _P, _P]),
     "kv_ring_restore": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "kv_ring_restore_steps": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P]),
     "kv_ring_steps": (_I64, [_P]),
+    "kv_ring_durable_steps": (_I64, [_P]),
+    "kv_acklog_create": (ctypes.c_int, [ctypes.POINTER(_P), _I32, _I32]),
+    "kv_acklog_destroy": (ctypes.c_int, [_P]),
+    "kv_ack": (ctypes.c_int, [_P, _I32, _I32, _I64]),
+    "kv_ack_restart_point": (ctypes.c_int, [_P, ctypes.POINTER(_I32), ctypes.POINTER(_I64)]),
     "kv_ring_reset": (ctypes.c_int, [_P]),
     "kv_profile_begin": (ctypes.c_int, []),
     "kv_profile_end": (ctypes.c_int, [ctypes.POINTER(kv_kernel_stat), _I32]),
@@ -360,9 +366,17 @@ class KvRing:
         _check(_lib.kv_ring_restore(self._h, _addr(k), _addr(v), _stream(compute), _event(done)),
                "kv_ring_restore")
 
+    def restore_steps(self, k, v, n, compute=None, done=None):
+        _check(_lib.kv_ring_restore_steps(self._h, _addr(k), _addr(v), n, _stream(compute),
+                                          _event(done)), "kv_ring_restore_steps")
+
     @property
     def steps(self) -> int:
         return _check(_lib.kv_ring_steps(self._h), "kv_ring_steps")
+
+    @property
+    def durable_steps(self) -> int:
+        return _check(_lib.kv_ring_durable_steps(self._h), "kv_ring_durable_steps")
 
     def reset(self):
         _check(_lib.kv_ring_reset(self._h), "kv_ring_reset")
@@ -389,8 +403,60 @@ def kv_ring_restore(r: KvRing, *args, **kw) -> None:
     r.restore(*args, **kw)
 
 
+def kv_ring_restore_steps(r: KvRing, *args, **kw) -> None:
+    r.restore_steps(*args, **kw)
+
+
 def kv_ring_steps(r: KvRing) -> int:
     return r.steps
+
+
+def kv_ring_durable_steps(r: KvRing) -> int:
+    return r.durable_steps
+
+
+# ---------------------------------------------------------------- acknowledgement log
+
+class KvAckLog:
+    """Handle of an acknowledgement log (kv_acklog_create / kv_acklog_destroy)."""
+
+    def __init__(self, workers: int, microbatches: int):
+        self._destroy = _lib.kv_acklog_destroy
+        h = _P()
+        _check(_lib.kv_acklog_create(ctypes.byref(h), workers, microbatches), "kv_acklog_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._destroy(self._h)
+            self._h = None
+
+    __del__ = close
+
+    def ack(self, x: int, j: int, t: int) -> None:
+        _check(_lib.kv_ack(self._h, x, j, t), "kv_ack")
+
+    def restart_point(self):
+        j, t = _I32(), _I64()
+        _check(_lib.kv_ack_restart_point(self._h, ctypes.byref(j), ctypes.byref(t)),
+               "kv_ack_restart_point")
+        return j.value, t.value
+
+
+def kv_acklog_create(workers: int, microbatches: int) -> KvAckLog:
+    return KvAckLog(workers, microbatches)
+
+
+def kv_acklog_destroy(a: KvAckLog) -> None:
+    a.close()
+
+
+def kv_ack(a: KvAckLog, x: int, j: int, t: int) -> None:
+    a.ack(x, j, t)
+
+
+def kv_ack_restart_point(a: KvAckLog):
+    return a.restart_point()
 
 
 def kv_ring_reset(r: KvRing) -> None:

@@ -18,7 +18,9 @@
 
 #include <algorithm>
 #include <cstring>
+#include <deque>
 #include <new>
+#include <utility>
 #include <vector>
 
 using namespace kvs;
@@ -206,6 +208,10 @@ struct kv_ring {
     hipEvent_t ev[4];            // free0, free1, filled0, filled1
     bool wait_needed[2];         // a push must wait on free_ev before writing the bank
     bool free_valid[2];          // free_ev has been recorded at least once
+    // flush copies not yet known complete: (event after the copy, steps held once it lands)
+    std::deque<std::pair<hipEvent_t, int64_t>> landing;
+    std::vector<hipEvent_t> spare;   // recycled landing events
+    int64_t durable;             // steps known to be in the host image
     hipEvent_t free_ev(int b) const { return ev[b]; }
     hipEvent_t filled_ev(int b) const { return ev[2 + b]; }
 };
@@ -493,6 +499,7 @@ int kv_ring_create(kv_ring **out, const kv_layout *lay, int32_t R, void *bank0, 
     r->transport = transport;
     r->slot_bytes = slot;
     r->steps = r->flushed = 0;
+    r->durable = 0;
     r->wait_needed[0] = r->wait_needed[1] = false;
     r->free_valid[0] = r->free_valid[1] = false;
     if ((st = create_events(r->ev, 4))) {
@@ -508,6 +515,10 @@ int kv_ring_destroy(kv_ring *r)
     if (!r)
         return KV_OK;
     for (hipEvent_t ev : r->ev)
+        (void)hipEventDestroy(ev);
+    for (auto &p : r->landing)
+        (void)hipEventDestroy(p.first);
+    for (hipEvent_t ev : r->spare)
         (void)hipEventDestroy(ev);
     delete r;
     return KV_OK;
@@ -534,6 +545,18 @@ int ring_flush_range(kv_ring *r, int64_t first, int64_t n, hipStream_t compute)
     r->wait_needed[bk] = true;
     r->free_valid[bk] = true;
     r->flushed = first + n;
+    hipEvent_t landed = nullptr;
+    if (!r->spare.empty()) {
+        landed = r->spare.back();
+        r->spare.pop_back();
+    } else if ((st = create_events(&landed, 1))) {
+        return st;
+    }
+    if ((st = record(landed, r->copy, "ring landed"))) {
+        r->spare.push_back(landed);
+        return st;
+    }
+    r->landing.emplace_back(landed, r->flushed);
     return KV_OK;
 }
 
@@ -593,22 +616,21 @@ int kv_ring_flush(kv_ring *r, hipStream_t compute, hipEvent_t done)
     return KV_OK;
 }
 
-int kv_ring_restore(kv_ring *r, void *k, void *v, hipStream_t compute, hipEvent_t done)
+namespace {
+
+// Unpack steps [0, n) of the host image into (k, v) in ascending step order.
+int ring_restore_n(kv_ring *r, void *k, void *v, int64_t n_steps, hipStream_t compute,
+                   hipEvent_t done)
 {
-    if (!r)
-        return set_error(KV_EINVAL, "ring handle is NULL");
     const kv_layout &lay = r->lay;
-    if (r->flushed != r->steps)
-        return set_error(KV_EBUSY, "%lld of %lld steps are not flushed; call kv_ring_flush",
-                         (long long)(r->steps - r->flushed), (long long)r->steps);
     int st;
     if ((st = check_device_buffer(k, lay.k_bytes, "key cache")) ||
         (st = check_device_buffer(v, lay.v_bytes, "value cache")))
         return st;
     if ((st = check_banks_apart(r->bank, r->bank_bytes, lay, k, v)))
         return st;
-    for (int64_t j0 = 0, g = 0; j0 < r->steps; j0 += r->R, ++g) {
-        const int64_t n = std::min<int64_t>(r->R, r->steps - j0);
+    for (int64_t j0 = 0, g = 0; j0 < n_steps; j0 += r->R, ++g) {
+        const int64_t n = std::min<int64_t>(r->R, n_steps - j0);
         const int bk = (int)(g & 1);
         if (r->free_valid[bk] && (st = wait(r->copy, r->free_ev(bk), "ring restore bank wait")))
             return st;
@@ -638,6 +660,65 @@ int kv_ring_restore(kv_ring *r, void *k, void *v, hipStream_t compute, hipEvent_
     return KV_OK;
 }
 
+}  // namespace
+
+int kv_ring_restore(kv_ring *r, void *k, void *v, hipStream_t compute, hipEvent_t done)
+{
+    if (!r)
+        return set_error(KV_EINVAL, "ring handle is NULL");
+    if (r->flushed != r->steps)
+        return set_error(KV_EBUSY, "%lld of %lld steps are not flushed; call kv_ring_flush",
+                         (long long)(r->steps - r->flushed), (long long)r->steps);
+    return ring_restore_n(r, k, v, r->steps, compute, done);
+}
+
+int kv_ring_restore_steps(kv_ring *r, void *k, void *v, int64_t n, hipStream_t compute,
+                          hipEvent_t done)
+{
+    if (!r)
+        return set_error(KV_EINVAL, "ring handle is NULL");
+    if (n < 0 || n > r->flushed)
+        return set_error(KV_ERANGE, "restore of %lld steps; %lld are flushed", (long long)n,
+                         (long long)r->flushed);
+    const int st = ring_restore_n(r, k, v, n, compute, done);
+    if (st != KV_OK)
+        return st;
+    // the ring now continues from step n: later steps are gone
+    if (n < r->steps) {
+        r->steps = r->flushed = n;
+        r->pos.resize((size_t)n * r->lay.B);
+        r->durable = std::min(r->durable, n);
+        std::deque<std::pair<hipEvent_t, int64_t>> keep;
+        for (auto &p : r->landing) {
+            if (p.second <= n)
+                keep.push_back(p);
+            else
+                r->spare.push_back(p.first);
+        }
+        r->landing.swap(keep);
+    }
+    return KV_OK;
+}
+
+int64_t kv_ring_durable_steps(kv_ring *r)
+{
+    if (!r)
+        return set_error(KV_EINVAL, "ring handle is NULL");
+    while (!r->landing.empty()) {
+        const hipError_t q = hipEventQuery(r->landing.front().first);
+        if (q == hipErrorNotReady) {
+            (void)hipGetLastError();
+            break;
+        }
+        if (q != hipSuccess)
+            return hip_fail(q, "kv_ring_durable_steps");
+        r->durable = r->landing.front().second;
+        r->spare.push_back(r->landing.front().first);
+        r->landing.pop_front();
+    }
+    return r->durable;
+}
+
 int64_t kv_ring_steps(const kv_ring *r)
 {
     if (!r)
@@ -652,6 +733,10 @@ int kv_ring_reset(kv_ring *r)
     if (r->steps > r->flushed)
         return set_error(KV_EBUSY, "unflushed steps; flush before reset");
     r->steps = r->flushed = 0;
+    r->durable = 0;
+    for (auto &p : r->landing)
+        r->spare.push_back(p.first);
+    r->landing.clear();
     r->pos.clear();
     return KV_OK;
 }

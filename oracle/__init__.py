@@ -19,7 +19,9 @@ Sources (the pages this project follows):
 Function map: ``pack`` is gather, ``unpack`` is scatter, ``swap_out`` is a pack
 over a layer range into host memory, ``swap_in`` the matching unpack,
 ``ring_host`` / ``ring_restore`` the staging-ring image and its restore,
-``prompt_ranges`` the per-row ranges of a prompt-layer pack.
+``prompt_ranges`` the per-row ranges of a prompt-layer pack, ``restart_point``
+the (microbatch, step) a pipeline resumes from after a failure (Failure
+detection and recovery, Fig 10).
 """
 from __future__ import annotations
 
@@ -69,6 +71,8 @@ def load(path: str = _LIB):
     lib.oracle_unpack.argtypes = [_i64] * 5 + [_p, _p, _i64, _i64, _p, _p, _p]
     lib.oracle_prompt_ranges.restype = None
     lib.oracle_prompt_ranges.argtypes = [_i64, _i32, _i32, _p, _p, _p]
+    lib.oracle_restart_point.restype = None
+    lib.oracle_restart_point.argtypes = [_i64, _i64, _i64, _p, _p, _p, _i64, _p, _p]
     lib.oracle_ring_restore.restype = None
     lib.oracle_ring_restore.argtypes = [_i64] * 5 + [_p, _p, _i64, _p, _i64, _p]
     if path == _LIB:
@@ -175,3 +179,16 @@ def ring_restore(dims, key, value, positions, host, lib=None) -> None:
         raise ValueError("host image shorter than the ring's steps")
     lib.oracle_ring_restore(L, B, H, D, S, _ptr(key), _ptr(value), steps, _ptr(pos), slot,
                             _ptr(host))
+
+
+def restart_point(workers: int, microbatches: int, acks, lib=None):
+    """(j, t) to resume from, given acknowledgements [(x, j, t), ...]."""
+    lib = lib or load()
+    a = np.asarray(list(acks), dtype=np.int64).reshape(-1, 3)
+    xs, js, ts = (np.ascontiguousarray(a[:, i]) for i in range(3))
+    max_step = int(a[:, 2].max()) + 1 if len(a) else 0
+    j = np.zeros(1, np.int64)
+    t = np.zeros(1, np.int64)
+    lib.oracle_restart_point(workers, microbatches, len(a), _ptr(xs), _ptr(js), _ptr(ts),
+                             max_step, _ptr(j), _ptr(t))
+    return int(j[0]), int(t[0])

@@ -43,6 +43,10 @@
  *    clipped to [0, row_len_b).
  *  - Ring restore: slots are unpacked in ascending step order, so a later
  *    step wins when two steps name the same position.
+ *  - Restart point after a failure ("Failure detection and recovery",
+ *    Fig 10): a (microbatch, step) pair counts as replicated once every worker
+ *    has acknowledged it; steps run in (step, microbatch) order; the pipeline
+ *    restarts at the first pair in that order that is not replicated.
  *
  * Every function here is plain C99, single-threaded.
  */
@@ -156,4 +160,30 @@ void oracle_ring_restore(int64_t L, int64_t B, int64_t H, int64_t D, int64_t Sma
     for (int64_t j = 0; j < steps; ++j)
         oracle_unpack(L, B, H, D, Smax, key, value, 0, L, pos + j * B, one,
                       host + j * slot_elems);
+}
+
+/* Restart point after a failure, from acknowledgements (x, j, t): worker x's
+ * replica holds microbatch j up to and including step t.  Walk the pairs in
+ * processing order -- step 0 of microbatches 0..M-1, then step 1, ... -- and
+ * return the first pair some worker has not acknowledged (an ack for step t
+ * covers every earlier step of that microbatch).  `max_step` bounds the walk. */
+void oracle_restart_point(int64_t workers, int64_t microbatches, int64_t n_acks,
+                          const int64_t *ack_x, const int64_t *ack_j, const int64_t *ack_t,
+                          int64_t max_step, int64_t *j_out, int64_t *t_out)
+{
+    for (int64_t t = 0; t <= max_step; ++t)
+        for (int64_t j = 0; j < microbatches; ++j)
+            for (int64_t x = 0; x < workers; ++x) {
+                int covered = 0;
+                for (int64_t a = 0; a < n_acks; ++a)
+                    if (ack_x[a] == x && ack_j[a] == j && ack_t[a] >= t)
+                        covered = 1;
+                if (!covered) {
+                    *j_out = j;
+                    *t_out = t;
+                    return;
+                }
+            }
+    *j_out = 0;
+    *t_out = max_step + 1;
 }

@@ -226,6 +226,21 @@ def check_offsets(lib, dims=(2, 3, 2, 16, 5)):
         assert v == np.ravel_multi_index((l, b, h, s, d), (L, B, H, S, D))
 
 
+def check_restart_point(lib):
+    # hand-worked: 2 workers, 3 microbatches
+    acks = [(0, 0, 5), (1, 0, 4), (0, 1, 5), (1, 1, 5), (0, 2, 4), (1, 2, 4)]
+    # replicated: mb0 up to 4, mb1 up to 5, mb2 up to 4 -> first gap in (step, mb)
+    # order is step 5 of mb 0
+    assert oracle.restart_point(2, 3, acks, lib=lib) == (0, 5)
+    acks = [(0, 0, 7), (0, 1, 6), (0, 2, 6)]
+    assert oracle.restart_point(1, 3, acks, lib=lib) == (1, 7)
+    assert oracle.restart_point(1, 2, [], lib=lib) == (0, 0)
+    # a worker that acknowledged nothing for microbatch 1 pins it at step 0
+    assert oracle.restart_point(2, 2, [(0, 0, 3), (1, 0, 3), (0, 1, 3)], lib=lib) == (1, 0)
+    # out-of-order acks: the later step covers the earlier
+    assert oracle.restart_point(1, 1, [(0, 0, 9), (0, 0, 2)], lib=lib) == (0, 10)
+
+
 def run_all(lib):
     check_offsets(lib)
     check_brute_force(lib)
@@ -233,6 +248,7 @@ def run_all(lib):
     check_round_trip(lib)
     check_prompt_ranges(lib)
     check_ring(lib)
+    check_restart_point(lib)
 
 
 if __name__ == "__main__":          # used by the mutant test: exit 0 iff every pin holds

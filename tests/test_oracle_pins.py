@@ -49,6 +49,10 @@ def test_ring_restore_last_writer_wins(lib):
     oracle_pins.check_ring(lib)
 
 
+def test_restart_point_hand_worked(lib):
+    oracle_pins.check_restart_point(lib)
+
+
 def test_closed_form_on_the_pages_example(lib):
     """KV bytes of the lsln.cn 100K-context example equal 2 x B x S x H x D x P x N."""
     with open(os.path.join(HERE, "golden", "kv_capacity_100k.json")) as f:
@@ -92,6 +96,11 @@ MUTANTS = {
                             "return layer_count * H * D * tokens;"),
     "prompt_clip_missing": ("if (row_len != NULL && row_len[b] < end)",
                             "if (row_len != NULL && row_len[b] > end)"),
+    "restart_worker_any_not_all": ("                    if (ack_x[a] == x && ack_j[a] == j && ack_t[a] >= t)",
+                                   "                    if (ack_j[a] == j && ack_t[a] >= t)"),
+    "restart_order_mb_major": ("    for (int64_t t = 0; t <= max_step; ++t)\n        for (int64_t j = 0; j < microbatches; ++j)\n            for (int64_t x = 0; x < workers; ++x) {",
+                               "    for (int64_t j = 0; j < microbatches; ++j)\n        for (int64_t t = 0; t <= max_step; ++t)\n            for (int64_t x = 0; x < workers; ++x) {"),
+    "restart_ack_exclusive": ("ack_t[a] >= t)", "ack_t[a] > t)"),
     "ring_order_reversed": ("for (int64_t j = 0; j < steps; ++j)\n        oracle_unpack(L, B, H, D, Smax, key, value, 0, L, pos + j * B",
                             "for (int64_t j = steps - 1; j >= 0; --j)\n        oracle_unpack(L, B, H, D, Smax, key, value, 0, L, pos + j * B"),
 }
