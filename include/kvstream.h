@@ -308,6 +308,54 @@ int64_t kv_ring_durable_steps(kv_ring *r);
 int kv_ring_reset(kv_ring *r);
 
 /* ---------------------------------------------------------------------------
+ * Microbatch swapping on two device slots ([DV, Microbatch swapping workflow,
+ * Fig 9]): N microbatches share two device caches; while microbatch x is
+ * processed in one slot, x+1 is being swapped into the other.  Microbatch x's
+ * KV lives on the host as its prompt image (packed tokens [0, prompt_len) of
+ * every layer) plus the host image of rings[x], one slot per generated step:
+ * the incremental swap-out of a step is a ring push (flushed at once when the
+ * ring has R = 1), and a full swap-in is the prompt image followed by the
+ * ring's steps.  The library orders everything with events: no host waits.
+ */
+typedef struct kv_mbswap kv_mbswap;
+
+/* microbatches >= 2.  Slots: two full caches of `lay` (device, 16-byte
+ * aligned).  `in`: the swap engine used for prompt swap-ins.  rings[x]: one
+ * ring per microbatch.  prompt_host[x] / prompt_bytes[x]: pinned prompt
+ * images, complete before kv_mbswap_start; prompt_len: int32[microbatches*B].
+ * `swap_stream`: the stream that runs the swap-in unpacks, so that they
+ * overlap the compute stream's work.  The handle keeps the pointers; the
+ * caller keeps the memory and the other handles alive. */
+int kv_mbswap_create(kv_mbswap **out, const kv_layout *lay, int32_t microbatches,
+                     void *slot0_k, void *slot0_v, void *slot1_k, void *slot1_v,
+                     kv_swap *in, kv_ring *const *rings, void *const *prompt_host,
+                     const int64_t *prompt_bytes, const int32_t *prompt_len,
+                     hipStream_t swap_stream);
+int kv_mbswap_destroy(kv_mbswap *m);
+
+/* Swap microbatches 0 and 1 into slots 0 and 1; `compute` waits for slot 0. */
+int kv_mbswap_start(kv_mbswap *m, hipStream_t compute);
+
+/* The microbatch of the current round and the slot (k, v) that holds it. */
+int kv_mbswap_current(const kv_mbswap *m, int32_t *x, void **k, void **v);
+
+/* End the current round after the caller's step wrote one token per row at
+ * pos[b] (int32[B]) on `compute`: swap out that update (rings[x] push), swap
+ * microbatch (x+2) % N into the slot x leaves (after the push has read it),
+ * advance to x+1 and make `compute` wait until x+1's slot is loaded. */
+int kv_mbswap_round(kv_mbswap *m, const int32_t *pos, hipStream_t compute);
+
+/* Appendix E of [DV]: with swapping the batch doubles from B to 2B, and
+ * swapping pays iff 2 * N * t >= sum_{i=p}^{N+p} max(t, transf_i) with
+ * transf_i = i * B * C / bw, the time to bring back the cache of B requests
+ * holding i tokens.  N: tokens generated; t: seconds per decode step; p:
+ * prompt length; C: KV bytes per token per request (2 * L * H * D * P for
+ * the layers one GPU holds); bw: host-link bytes per second.  Writes both
+ * sides and returns 1 if swapping pays, 0 if not, or a negative kv_status. */
+int kv_swap_pays(int64_t N, double t, int64_t p, int64_t B, double C, double bw,
+                 double *lhs, double *rhs);
+
+/* ---------------------------------------------------------------------------
  * Acknowledgement log and restart point ([DV, Failure detection and
  * recovery, Fig 10]).  Worker x acknowledges (x, j, t) once the replica holds
  * microbatch j's KV up to and including step t.  After a failure the pipeline

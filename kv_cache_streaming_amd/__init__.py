@@ -94,6 +94,16 @@ _SIGNATURES = {
     "kv_ring_restore_steps": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P]),
     "kv_ring_steps": (_I64, [_P]),
     "kv_ring_durable_steps": (_I64, [_P]),
+    "kv_mbswap_create": (ctypes.c_int, [ctypes.POINTER(_P), _LAY, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, _P, _P]),
+    "kv_mbswap_destroy": (ctypes.c_int, [_P]),
+    "kv_mbswap_start": (ctypes.c_int, [_P, _P]),
+    "kv_mbswap_current": (ctypes.c_int, [_P, ctypes.POINTER(_I32), ctypes.POINTER(_P),
+                                         ctypes.POINTER(_P)]),
+    "kv_mbswap_round": (ctypes.c_int, [_P, _P, _P]),
+    "kv_swap_pays": (ctypes.c_int, [_I64, ctypes.c_double, _I64, _I64, ctypes.c_double,
+                                    ctypes.c_double, ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_double)]),
     "kv_acklog_create": (ctypes.c_int, [ctypes.POINTER(_P), _I32, _I32]),
     "kv_acklog_destroy": (ctypes.c_int, [_P]),
     "kv_ack": (ctypes.c_int, [_P, _I32, _I32, _I64]),
@@ -413,6 +423,81 @@ def kv_ring_steps(r: KvRing) -> int:
 
 def kv_ring_durable_steps(r: KvRing) -> int:
     return r.durable_steps
+
+
+# ---------------------------------------------------------------- microbatch swapping
+
+class KvMbSwap:
+    """Microbatch swapping on two device slots (kv_mbswap_create / _destroy)."""
+
+    def __init__(self, lay, slots, swap_in_engine: KvSwap, rings, prompt_host, prompt_bytes,
+                 prompt_len, swap_stream=None):
+        n = len(rings)
+        self.lay, self.n = lay, n
+        self._keep = (slots, swap_in_engine, rings, prompt_host)
+        self._destroy = _lib.kv_mbswap_destroy
+        ring_ptrs = (_P * n)(*[r._h.value for r in rings])
+        host_ptrs = (_P * n)(*[_addr(h) for h in prompt_host])
+        self._bytes = np.ascontiguousarray(np.asarray(prompt_bytes, dtype=np.int64))
+        self._len = np.ascontiguousarray(np.asarray(prompt_len, dtype=np.int32).reshape(-1))
+        if self._len.size != n * lay.B or self._bytes.size != n:
+            raise ValueError("prompt_len needs microbatches*B values, prompt_bytes one per microbatch")
+        (k0, v0), (k1, v1) = slots
+        h = _P()
+        _check(_lib.kv_mbswap_create(ctypes.byref(h), ctypes.byref(lay), n, _addr(k0), _addr(v0),
+                                     _addr(k1), _addr(v1), swap_in_engine._h, ring_ptrs, host_ptrs,
+                                     self._bytes.ctypes.data, self._len.ctypes.data,
+                                     _stream(swap_stream)), "kv_mbswap_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._destroy(self._h)
+            self._h = None
+
+    __del__ = close
+
+    def start(self, compute=None):
+        _check(_lib.kv_mbswap_start(self._h, _stream(compute)), "kv_mbswap_start")
+
+    def current(self):
+        """(microbatch, k address, v address) of the current round."""
+        x, k, v = _I32(), _P(), _P()
+        _check(_lib.kv_mbswap_current(self._h, ctypes.byref(x), ctypes.byref(k), ctypes.byref(v)),
+               "kv_mbswap_current")
+        return x.value, k.value, v.value
+
+    def round(self, pos, compute=None):
+        p = _Rows(pos, self.lay.B, "pos")
+        _check(_lib.kv_mbswap_round(self._h, p.ptr, _stream(compute)), "kv_mbswap_round")
+
+
+def kv_mbswap_create(*args, **kw) -> KvMbSwap:
+    return KvMbSwap(*args, **kw)
+
+
+def kv_mbswap_destroy(m: KvMbSwap) -> None:
+    m.close()
+
+
+def kv_mbswap_start(m: KvMbSwap, compute=None) -> None:
+    m.start(compute)
+
+
+def kv_mbswap_current(m: KvMbSwap):
+    return m.current()
+
+
+def kv_mbswap_round(m: KvMbSwap, pos, compute=None) -> None:
+    m.round(pos, compute)
+
+
+def kv_swap_pays(N: int, t: float, p: int, B: int, C: float, bw: float):
+    """(pays, lhs, rhs) of the Appendix E break-even test."""
+    lhs, rhs = ctypes.c_double(), ctypes.c_double()
+    r = _check(_lib.kv_swap_pays(N, t, p, B, C, bw, ctypes.byref(lhs), ctypes.byref(rhs)),
+               "kv_swap_pays")
+    return bool(r), lhs.value, rhs.value
 
 
 # ---------------------------------------------------------------- acknowledgement log

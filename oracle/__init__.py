@@ -73,6 +73,9 @@ def load(path: str = _LIB):
     lib.oracle_prompt_ranges.argtypes = [_i64, _i32, _i32, _p, _p, _p]
     lib.oracle_restart_point.restype = None
     lib.oracle_restart_point.argtypes = [_i64, _i64, _i64, _p, _p, _p, _i64, _p, _p]
+    lib.oracle_swap_pays.restype = ctypes.c_int
+    lib.oracle_swap_pays.argtypes = [_i64, ctypes.c_double, _i64, _i64, ctypes.c_double,
+                                     ctypes.c_double, _p, _p]
     lib.oracle_ring_restore.restype = None
     lib.oracle_ring_restore.argtypes = [_i64] * 5 + [_p, _p, _i64, _p, _i64, _p]
     if path == _LIB:
@@ -192,3 +195,12 @@ def restart_point(workers: int, microbatches: int, acks, lib=None):
     lib.oracle_restart_point(workers, microbatches, len(a), _ptr(xs), _ptr(js), _ptr(ts),
                              max_step, _ptr(j), _ptr(t))
     return int(j[0]), int(t[0])
+
+
+def swap_pays(N: int, t: float, p: int, B: int, C: float, bw: float, lib=None):
+    """(pays, lhs, rhs) of the Appendix E microbatch-swapping inequality."""
+    lib = lib or load()
+    lhs = np.zeros(1, np.float64)
+    rhs = np.zeros(1, np.float64)
+    r = lib.oracle_swap_pays(N, t, p, B, C, bw, _ptr(lhs), _ptr(rhs))
+    return bool(r), float(lhs[0]), float(rhs[0])

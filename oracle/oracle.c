@@ -43,6 +43,8 @@
  *    clipped to [0, row_len_b).
  *  - Ring restore: slots are unpacked in ascending step order, so a later
  *    step wins when two steps name the same position.
+ *  - Appendix E (microbatch swapping benefit): the inequality
+ *    2 N t >= sum_{i=p}^{N+p} max(t, i B C / bw), bounds inclusive as printed.
  *  - Restart point after a failure ("Failure detection and recovery",
  *    Fig 10): a (microbatch, step) pair counts as replicated once every worker
  *    has acknowledged it; steps run in (step, microbatch) order; the pipeline
@@ -186,4 +188,22 @@ void oracle_restart_point(int64_t workers, int64_t microbatches, int64_t n_acks,
             }
     *j_out = 0;
     *t_out = max_step + 1;
+}
+
+/* Appendix E of the DejaVu summary: doubling the batch from B to 2B by
+ * swapping pays when 2*N*t (two batches of B without swapping, N decode steps
+ * of t each) is at least the swapped run, in which the step that holds i
+ * tokens lasts max(t, i*B*C/bw) -- the compute time or the time to bring the
+ * other batch's cache back -- summed for i = p .. N+p.  Returns 1 if it pays. */
+int oracle_swap_pays(int64_t N, double t, int64_t p, int64_t B, double C, double bw,
+                     double *lhs, double *rhs)
+{
+    double sum = 0.0;
+    for (int64_t i = p; i <= N + p; ++i) {
+        double transfer = (double)i * (double)B * C / bw;
+        sum += transfer > t ? transfer : t;
+    }
+    *lhs = 2.0 * (double)N * t;
+    *rhs = sum;
+    return *lhs >= *rhs;
 }

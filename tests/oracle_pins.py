@@ -241,6 +241,22 @@ def check_restart_point(lib):
     assert oracle.restart_point(1, 1, [(0, 0, 9), (0, 0, 2)], lib=lib) == (0, 10)
 
 
+def check_swap_pays(lib):
+    # closed form 1: a link so fast that every transfer beats the step: N+1 steps of t
+    pays, lhs, rhs = oracle.swap_pays(100, 0.03, 500, 8, 1e6, 1e18, lib=lib)
+    assert lhs == 2 * 100 * 0.03 and abs(rhs - 101 * 0.03) < 1e-12 and pays
+    # closed form 2: t = 0, so every step lasts its transfer: (B C / bw) * sum_{i=p}^{N+p} i
+    N, p, B, C, bw = 50, 7, 3, 2.0, 5.0
+    pays, lhs, rhs = oracle.swap_pays(N, 0.0, p, B, C, bw, lib=lib)
+    assert lhs == 0.0 and abs(rhs - B * C / bw * (N + 1) * (2 * p + N) / 2) < 1e-9 and not pays
+    # hand-worked crossover: N=2, p=1, B=1, C=1, bw=1, t=2.5 -> steps hold 1,2,3 tokens:
+    # max(2.5,1)+max(2.5,2)+max(2.5,3) = 8.0 > 2*2*2.5 = 10? no: 8.0 <= 10 -> pays
+    pays, lhs, rhs = oracle.swap_pays(2, 2.5, 1, 1, 1.0, 1.0, lib=lib)
+    assert (pays, lhs, rhs) == (True, 10.0, 8.0)
+    pays, lhs, rhs = oracle.swap_pays(2, 1.0, 3, 1, 1.0, 1.0, lib=lib)   # 3+4+5 = 12 > 4
+    assert (pays, lhs, rhs) == (False, 4.0, 12.0)
+
+
 def run_all(lib):
     check_offsets(lib)
     check_brute_force(lib)
@@ -249,6 +265,7 @@ def run_all(lib):
     check_prompt_ranges(lib)
     check_ring(lib)
     check_restart_point(lib)
+    check_swap_pays(lib)
 
 
 if __name__ == "__main__":          # used by the mutant test: exit 0 iff every pin holds

@@ -53,6 +53,10 @@ def test_restart_point_hand_worked(lib):
     oracle_pins.check_restart_point(lib)
 
 
+def test_swap_pays_closed_forms(lib):
+    oracle_pins.check_swap_pays(lib)
+
+
 def test_closed_form_on_the_pages_example(lib):
     """KV bytes of the lsln.cn 100K-context example equal 2 x B x S x H x D x P x N."""
     with open(os.path.join(HERE, "golden", "kv_capacity_100k.json")) as f:
@@ -101,6 +105,11 @@ MUTANTS = {
     "restart_order_mb_major": ("    for (int64_t t = 0; t <= max_step; ++t)\n        for (int64_t j = 0; j < microbatches; ++j)\n            for (int64_t x = 0; x < workers; ++x) {",
                                "    for (int64_t j = 0; j < microbatches; ++j)\n        for (int64_t t = 0; t <= max_step; ++t)\n            for (int64_t x = 0; x < workers; ++x) {"),
     "restart_ack_exclusive": ("ack_t[a] >= t)", "ack_t[a] > t)"),
+    "swap_pays_upper_bound_exclusive": ("for (int64_t i = p; i <= N + p; ++i) {\n        double transfer",
+                                        "for (int64_t i = p; i < N + p; ++i) {\n        double transfer"),
+    "swap_pays_batch_dropped": ("double transfer = (double)i * (double)B * C / bw;",
+                                "double transfer = (double)i * C / bw;"),
+    "swap_pays_single_run": ("*lhs = 2.0 * (double)N * t;", "*lhs = (double)N * t;"),
     "ring_order_reversed": ("for (int64_t j = 0; j < steps; ++j)\n        oracle_unpack(L, B, H, D, Smax, key, value, 0, L, pos + j * B",
                             "for (int64_t j = steps - 1; j >= 0; --j)\n        oracle_unpack(L, B, H, D, Smax, key, value, 0, L, pos + j * B"),
 }
