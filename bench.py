@@ -1,6 +1,6 @@
 """Benchmark of the KV buffered-copy path on one MI355X.
 
-One step is one pass of the whole path over one batch of the
+By default one step is one pass of the whole path over one batch of the
 GPT-2-1.5B-shaped workload (L=48, B=8, H=25, D=64, Smax=1024, fp16; prompt
 length 1000; 24 decode steps; staging ring of 8 slots).  It follows the
 dataflow of the DejaVu workers, emulated on one GPU:
@@ -27,10 +27,18 @@ pack/unpack kernel with the most GPU time: algorithmic bytes (payload read +
 payload written) per launch over its average duration, both measured live
 with hipEvents bracketing every launch on its own stream.  `cpu_baseline`
 is the oracle on a bounded sample of the same step.
+
+`--workload` selects the other shapes, each with the step its class below
+describes: opt-66b-16l (RingStep: the decode ring of a 16-layer OPT-66B
+stage), bloom-176b-10l (SwapStep: duplex microbatch swapping on a 10-layer
+BLOOM-176B stage, plus the steady-state schedule against its Appendix E
+prediction), gqa-100k (LongStep: 100K-token contexts), gpt2-small-tiny (the
+default step at GPT-2-small size).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -40,18 +48,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-# The step drives four streams (two compute, one copy stream per link
-# direction) besides the default one.  HIP maps streams onto a fixed number of
-# hardware queues per process; with fewer queues than busy streams, streams
-# share a queue and their work serialises, so the two link directions never
-# overlap.  Ask for eight (must happen before the HIP runtime starts).
-if int(os.environ.get("GPU_MAX_HW_QUEUES", "0") or 0) < 8:
-    os.environ["GPU_MAX_HW_QUEUES"] = "8"
+# A step drives up to eight streams (compute streams, one copy stream per link
+# direction, the swap stream of the microbatch schedule) besides the default
+# one.  HIP maps streams onto a fixed number of hardware queues per process;
+# with fewer queues than streams, streams share a queue and their work
+# serialises: the two link directions stop overlapping, and a swap-in waits
+# behind the compute it should hide under.  Ask for sixteen (must happen before
+# the HIP runtime starts).
+if int(os.environ.get("GPU_MAX_HW_QUEUES", "0") or 0) < 16:
+    os.environ["GPU_MAX_HW_QUEUES"] = "16"
 
 METRIC = "KV pack/unpack GB/s (% HBM peak) + swap host-link GB/s, 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
 PCIE_PEAK_GBPS = 63.0          # PCIe 5.0 x16, per direction
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "traffic_gpt2-1.5b.txt")
+
+def counters_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
 
 
 def parse_args():
@@ -59,7 +71,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="gpt2-1.5b")
+    ap.add_argument("--workload", default="gpt2-1.5b", choices=sorted(STEPS),
+                    help="gpt2-1.5b is the headline; the others measure the remaining workloads")
     ap.add_argument("--swap-bank-mib", type=int, default=256)
     ap.add_argument("--transport", choices=("auto", "kernel", "runtime", "dma", "dma_out"), default="auto",
                     help="bank<->host transfers (see kv_transport in include/kvstream.h)")
@@ -72,8 +85,9 @@ def parse_args():
     return ap.parse_args()
 
 
-class Step:
-    """All buffers and handles of one workload, and the step itself."""
+class StreamStep:
+    """Prompt streaming, decode ring and microbatch swap of a uniform-prompt
+    workload (the GPT-2 shapes): the five phases listed at the top."""
 
     def __init__(self, w, swap_bank_bytes, transport=0):
         import torch
@@ -162,6 +176,352 @@ class Step:
                                hs_in + l * lf, lf, sp)
         torch.cuda.synchronize()
 
+
+def _pinned(torch, nbytes):
+    return torch.empty((nbytes + 1) // 2, dtype=torch.int16, pin_memory=True)
+
+
+class HostBuffer:
+    """Page-locked host memory of exactly `nbytes` (hipHostMalloc).  torch rounds
+    a pinned request up to a power of two, which for host images of tens of GB
+    nearly doubles the page-locked footprint."""
+
+    def __init__(self, kv, nbytes):
+        lib = kv._lib      # resolves to the HIP runtime the library and torch share
+        lib.hipHostMalloc.restype = ctypes.c_int
+        lib.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t,
+                                      ctypes.c_uint]
+        lib.hipHostFree.restype = ctypes.c_int
+        lib.hipHostFree.argtypes = [ctypes.c_void_p]
+        self._free = lib.hipHostFree
+        p = ctypes.c_void_p()
+        r = lib.hipHostMalloc(ctypes.byref(p), nbytes, 0)
+        if r != 0 or not p.value:
+            raise MemoryError(f"hipHostMalloc of {nbytes} bytes failed (hipError {r})")
+        self.ptr, self.nbytes = p.value, nbytes
+
+    def data_ptr(self):
+        return self.ptr
+
+    def close(self):
+        if getattr(self, "ptr", None):
+            self._free(self.ptr)
+            self.ptr = None
+
+    __del__ = close
+
+
+def _bank(torch, nbytes):
+    return torch.empty((nbytes + 1) // 2, dtype=torch.int16, device="cuda")
+
+
+def _filled_cache(torch, w, seed):
+    import synth
+    n = w.L * w.B * w.H * w.D * w.Smax
+    k = torch.empty(n, dtype=torch.int16, device="cuda")
+    v = torch.empty(n, dtype=torch.int16, device="cuda")
+    synth.fill_device_cache(k, seed, w.dtype)
+    synth.fill_device_cache(v, seed + 1, w.dtype)
+    return k, v
+
+
+def _duplex_layers(eng_o, eng_i, src, dst, L, start, count, img_out, img_in, per_layer, s_out,
+                   s_in, packed):
+    """Layer-pipelined swap-out of `src` || swap-in into `dst`, where `dst` may be
+    the region `src` is leaving: the unpack of layer l waits for the pack of
+    layer l (event `packed[l]`), nothing else couples the two directions."""
+    for l in range(L):
+        eng_o.swap_out(src[0], src[1], l, 1, start, count, img_out + l * per_layer, per_layer, s_out)
+        packed[l].record(s_out)
+        s_in.wait_event(packed[l])
+        eng_i.swap_in(dst[0], dst[1], l, 1, start, count, img_in + l * per_layer, per_layer, s_in)
+
+
+class RingStep:
+    """Decode leg of one token-generation stage of a pipeline: the 16-layer
+    OPT-66B slice, ragged current lengths U{256..1800}.  One step = 64 decode
+    steps of cache A (one token per row at len_b + j) packed into a 16-slot
+    staging ring, flushed to pinned host memory every 16 steps, then the ring's
+    host image restored into cache D (recovery on a fresh worker)."""
+
+    def __init__(self, w, swap_bank_bytes, transport=0):
+        import torch
+
+        import kv_cache_streaming_amd as kv
+        import synth
+        self.kv, self.w, self.torch = kv, w, torch
+        self.lay = kv.kv_layout_init(*w.dims, w.dtype)
+        self.A = _filled_cache(torch, w, w.value_seed)
+        self.D = _filled_cache(torch, w, w.value_seed + 300)
+        self.positions = [list(map(int, p)) for p in synth.decode_positions(w)]
+        self.slot = kv.kv_pack_bytes(self.lay, w.L, None, 1)
+        self.s = {name: torch.cuda.Stream() for name in ("t", "d2h")}
+        R = w.ring_slots
+        self.ring_host = _pinned(torch, w.decode_steps * self.slot)
+        self.ring = kv.KvRing(self.lay, R, _bank(torch, R * self.slot), _bank(torch, R * self.slot),
+                              self.ring_host, copy_stream=self.s["d2h"], transport=transport)
+
+    def link_bytes(self):
+        return 2 * self.w.decode_steps * self.slot
+
+    def run(self):
+        st = self.s["t"]
+        self.ring.reset()
+        for pos in self.positions:
+            self.ring.push(self.A[0], self.A[1], pos, st)
+        self.ring.flush(st)
+        self.ring.restore(self.D[0], self.D[1], st)
+        self.torch.cuda.synchronize()
+
+    def cpu_ops(self):
+        """(layer-0 source, per-op (name, start, count)) for the oracle sample."""
+        B = self.w.B
+        return self.A, [("decode pack", p, [1] * B) for p in self.positions]
+
+
+class SwapStep:
+    """Microbatch swapping on one stage: the 10-layer BLOOM-176B slice, 16 rows
+    of 1500 tokens per microbatch, four microbatches with a host image each
+    (13.76 GB) and two device slots.  One step = one round of the round-robin:
+    while microbatch x computes in one slot, microbatch x-1 is swapped out of
+    the other slot layer by layer and microbatch x+1 is swapped into it, each
+    layer's unpack waiting only for that layer's pack (both link directions at
+    once)."""
+
+    def __init__(self, w, swap_bank_bytes, transport=0):
+        import torch
+
+        import kv_cache_streaming_amd as kv
+        self.kv, self.w, self.torch = kv, w, torch
+        L, B = w.L, w.B
+        self.lay = kv.kv_layout_init(*w.dims, w.dtype)
+        self.rows_start = [0] * B
+        self.rows = [w.prompt_len] * B
+        self.per_layer = kv.kv_pack_bytes(self.lay, 1, self.rows)
+        self.image = L * self.per_layer
+        self.N = w.microbatches
+        n = L * B * w.H * w.D * w.Smax
+        self.slots = [(torch.empty(n, dtype=torch.int16, device="cuda"),
+                       torch.empty(n, dtype=torch.int16, device="cuda")) for _ in range(2)]
+        self.host = HostBuffer(kv, self.N * self.image)
+        self.img = [self.host.data_ptr() + x * self.image for x in range(self.N)]
+        self.s = {name: torch.cuda.Stream() for name in ("out", "in", "d2h", "h2d", "swap")}
+        sb = swap_bank_bytes
+        self.eng_o = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb, self.s["d2h"],
+                               transport)
+        self.eng_i = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb, self.s["h2d"],
+                               transport)
+        self.packed = [torch.cuda.Event() for _ in range(L)]
+        # every microbatch's host image, written through a swap-out of a slot
+        # filled with that microbatch's values
+        import synth
+        for x in range(self.N):
+            k, v = self.slots[x % 2]
+            synth.fill_device_cache(k, w.value_seed + 40 * x, w.dtype)
+            synth.fill_device_cache(v, w.value_seed + 40 * x + 1, w.dtype)
+            torch.cuda.synchronize()
+            self.eng_o.swap_out(k, v, 0, L, self.rows_start, self.rows, self.img[x], self.image,
+                                torch.cuda.current_stream())
+            torch.cuda.synchronize()
+        self.r = 0
+
+    def link_bytes(self):
+        return 2 * self.image
+
+    def run(self):
+        N, r = self.N, self.r
+        self.r += 1
+        x = r % N
+        other = self.slots[(r + 1) % 2]          # holds x-1, receives x+1
+        _duplex_layers(self.eng_o, self.eng_i, other, other, self.w.L, self.rows_start, self.rows,
+                       self.img[(x - 1) % N], self.img[(x + 1) % N], self.per_layer,
+                       self.s["out"], self.s["in"], self.packed)
+        self.torch.cuda.synchronize()
+
+    def cpu_ops(self):
+        return self.slots[0], [("swap pack", self.rows_start, self.rows)] * self.w.L
+
+    def schedule(self, kv, rounds_per_mb=2, steady_from=2):
+        """The steady-state schedule of the pages' microbatch swapping: after
+        each decode step of microbatch x, only that step's new tokens go out
+        (an incremental swap-out through a staging ring) while microbatch x+2
+        comes back into the slot x leaves, during the step of x+1.  A round
+        costs max(t, transfer) for a decode step of t seconds; the rows below
+        hold the measured round time against that figure for a few t, with t
+        played by a timed busy-wait on the compute stream."""
+        import numpy as np
+        torch, w, lay = self.torch, self.w, self.lay
+        L, B, N = w.L, w.B, self.N
+        slot = kv.kv_pack_bytes(lay, L, None, 1)
+        rounds = N * rounds_per_mb
+        rings = [kv.KvRing(lay, 1, _bank(torch, slot), _bank(torch, slot),
+                           _pinned(torch, rounds_per_mb * slot), copy_stream=self.s["d2h"])
+                 for _ in range(N)]
+        rng = np.random.default_rng(7)
+        new = torch.from_numpy(rng.integers(-32768, 32768, size=slot // 2, dtype=np.int16)).cuda()
+        by_addr = {t.data_ptr(): t for pair in self.slots for t in pair}
+        c = torch.cuda.Stream()
+        # busy-wait calibration: cycles per millisecond of the sleep kernel
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(c):
+            torch.cuda._sleep(1000)
+            e0.record(c)
+            torch.cuda._sleep(2_000_000)
+            e1.record(c)
+        torch.cuda.synchronize()
+        cycles_per_ms = 2_000_000 / e0.elapsed_time(e1)
+        # transfer time of one image alone (swap-in of a whole microbatch)
+        t0 = time.perf_counter()
+        self.eng_i.swap_in(self.slots[0][0], self.slots[0][1], 0, L, self.rows_start, self.rows,
+                           self.img[0], self.image, c)
+        torch.cuda.synchronize()
+        transf = time.perf_counter() - t0
+        bw = self.image / transf
+        C = 2 * L * w.H * w.D * 2
+        out = {"microbatches": N, "device_slots": 2, "rounds": rounds,
+               "image_bytes": self.image, "step_update_bytes": slot,
+               "swap_in_alone_ms": round(transf * 1000, 2), "swap_in_alone_GBps": round(bw / 1e9, 2),
+               "rows": []}
+        for t_ms in (0.0, 0.5 * transf * 1000, 2.0 * transf * 1000):
+            for rg in rings:
+                rg.reset()
+            m = kv.KvMbSwap(lay, self.slots, self.eng_i, rings, self.img, [self.image] * N,
+                            [w.prompt_len] * (N * B), self.s["swap"])
+            torch.cuda.synchronize()
+            m.start(c)
+            marks = []
+            gen = [0] * N
+            for r in range(rounds):
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record(c)
+                marks.append(ev)
+                x, ka, va = m.current()
+                if t_ms > 0:
+                    with torch.cuda.stream(c):
+                        torch.cuda._sleep(int(t_ms * cycles_per_ms))
+                pos = [w.prompt_len + gen[x]] * B
+                kv.kv_unpack_tokens(lay, by_addr[ka], by_addr[va], 0, L, pos, [1] * B, new, slot, c)
+                m.round(pos, c)
+                gen[x] += 1
+            end = torch.cuda.Event(enable_timing=True)
+            end.record(c)
+            marks.append(end)
+            torch.cuda.synchronize()
+            per = [marks[i].elapsed_time(marks[i + 1]) for i in range(steady_from, rounds)]
+            pays, lhs, rhs = kv.kv_swap_pays(64, t_ms / 1000, w.prompt_len, B, C, bw)
+            out["rows"].append({"t_ms": round(t_ms, 2),
+                                "round_ms_median": round(float(np.median(per)), 2),
+                                "predicted_round_ms": round(max(t_ms, transf * 1000), 2),
+                                "appendix_e_64_tokens": {"pays": pays, "lhs_s": round(lhs, 3),
+                                                         "rhs_s": round(rhs, 3)}})
+            m.close()
+        for rg in rings:
+            rg.close()
+        return out
+
+
+class LongStep:
+    """The 100K-context workload: 60 layers, 4 rows, 8 KV heads, D=128, bf16,
+    current lengths U{20000..99936}.  One step = the row of the longest context
+    swapped out to pinned host memory layer by layer while its previous image
+    is swapped back in (both directions at once), the whole prompt of every
+    row streamed out in 4096-token chunks per layer, and 64 decode steps
+    through a 16-slot staging ring restored into the cache."""
+
+    def __init__(self, w, swap_bank_bytes, transport=0):
+        import torch
+
+        import kv_cache_streaming_amd as kv
+        import synth
+        self.kv, self.w, self.torch = kv, w, torch
+        L, B = w.L, w.B
+        self.lay = kv.kv_layout_init(*w.dims, w.dtype)
+        self.lens = [int(x) for x in synth.row_lengths(w)]
+        self.positions = [list(map(int, p)) for p in synth.decode_positions(w)]
+        self.A = _filled_cache(torch, w, w.value_seed)
+        self.s = {name: torch.cuda.Stream()
+                  for name in ("p", "t", "out", "in", "d2h", "d2h_row", "h2d")}
+        # prompt chunks of one layer: (first token, bytes); every layer has the same
+        ch = w.chunk_tokens
+        self.chunks = []
+        for c0 in range(0, max(self.lens), ch):
+            cnt = [max(0, min(ch, n - c0)) for n in self.lens]
+            self.chunks.append((c0, kv.kv_pack_bytes(self.lay, 1, cnt)))
+        self.prompt_layer = sum(c[1] for c in self.chunks)
+        cb = max(c[1] for c in self.chunks)
+        self.eng_p = kv.KvSwap(self.lay, _bank(torch, cb), _bank(torch, cb), cb, self.s["d2h"],
+                               transport)
+        # layer l's chunks land in host region l % 2, one layer each: the host
+        # buffer a prompt worker forwards from (the whole prompt, 60 GB at these
+        # lengths, need not stay page-locked on this side)
+        self.prompt_host = [HostBuffer(kv, self.prompt_layer) for _ in range(2)]
+        # the swapped row
+        bstar = max(range(B), key=lambda b: self.lens[b])
+        self.row_start = [0] * B
+        self.row_count = [self.lens[b] if b == bstar else 0 for b in range(B)]
+        self.row_layer = kv.kv_pack_bytes(self.lay, 1, self.row_count)
+        self.row_image = L * self.row_layer
+        # a bank holds at least one row of one layer (the engine splits at rows)
+        sb = max(swap_bank_bytes, -(-self.row_layer // (1 << 20)) << 20)
+        self.eng_o = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb,
+                               self.s["d2h_row"], transport)
+        self.eng_i = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb, self.s["h2d"],
+                               transport)
+        self.row_host = [HostBuffer(kv, self.row_image) for _ in range(2)]
+        self.packed = [torch.cuda.Event() for _ in range(L)]
+        self.row_in = torch.cuda.Event()
+        torch.cuda.synchronize()
+        self.eng_o.swap_out(self.A[0], self.A[1], 0, L, self.row_start, self.row_count,
+                            self.row_host[1], self.row_image, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        self.slot = kv.kv_pack_bytes(self.lay, L, None, 1)
+        R = w.ring_slots
+        self.ring_host = _pinned(torch, w.decode_steps * self.slot)
+        self.ring = kv.KvRing(self.lay, R, _bank(torch, R * self.slot), _bank(torch, R * self.slot),
+                              self.ring_host, copy_stream=self.s["d2h"], transport=transport)
+        self.k = 0
+
+    def link_bytes(self):
+        return (self.w.L * self.prompt_layer + 2 * self.row_image
+                + 2 * self.w.decode_steps * self.slot)
+
+    def run(self):
+        torch, w = self.torch, self.w
+        out, inn = self.k % 2, (self.k + 1) % 2
+        self.k += 1
+        _duplex_layers(self.eng_o, self.eng_i, self.A, self.A, w.L, self.row_start,
+                       self.row_count, self.row_host[out].data_ptr(),
+                       self.row_host[inn].data_ptr(), self.row_layer, self.s["out"],
+                       self.s["in"], self.packed)
+        # the prompt chunks read the swapped row too: start them once it is back
+        self.row_in.record(self.s["in"])
+        self.s["p"].wait_event(self.row_in)
+        for l in range(w.L):
+            off = self.prompt_host[l % 2].data_ptr()
+            for c0, nb in self.chunks:
+                self.eng_p.stream_prompt_layer(self.A[0], self.A[1], l, c0, w.chunk_tokens,
+                                               self.lens, off, nb, self.s["p"])
+                off += nb
+        st = self.s["t"]
+        self.ring.reset()
+        for pos in self.positions:
+            self.ring.push(self.A[0], self.A[1], pos, st)
+        self.ring.flush(st)
+        self.ring.restore(self.A[0], self.A[1], st)
+        torch.cuda.synchronize()
+
+    def cpu_ops(self):
+        B, ch = self.w.B, self.w.chunk_tokens
+        ops = []
+        for c0, nb in self.chunks:
+            cnt = [max(0, min(ch, n - c0)) for n in self.lens]
+            ops.append(("prompt chunk pack", [c0 if c else 0 for c in cnt], cnt))
+        ops.append(("row swap pack", self.row_start, self.row_count))
+        return self.A, ops
+
+
+STEPS = {"gpt2-small-tiny": StreamStep, "gpt2-1.5b": StreamStep, "opt-66b-16l": RingStep,
+         "bloom-176b-10l": SwapStep, "gqa-100k": LongStep}
 
 def link_ceiling(torch, nbytes=1 << 30, reps=3):
     """GB/s of one large contiguous pinned copy each way, and both at once."""
@@ -279,14 +639,15 @@ def decode_push_us(step, reps=3):
     return min(times)
 
 
-def read_counters(kernel_name):
-    """Per-launch HBM traffic of `kernel_name` from the committed counter summary,
-    or None when absent or taken on a different kernel source."""
-    if not os.path.exists(COUNTERS_FILE):
+def read_counters(workload, kernel_name):
+    """Per-launch HBM traffic of `kernel_name` from the committed counter summary
+    of the workload, or None when absent or taken on a different kernel source."""
+    path = counters_file(workload)
+    if not os.path.exists(path):
         return None
     import hashlib
     fields = {}
-    for line in open(COUNTERS_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
@@ -344,6 +705,37 @@ def cpu_baseline(step, budget_s):
                       f"(single-threaded C oracle)"}
 
 
+
+def cpu_baseline_layer(step, budget_s):
+    """The oracle, as it stands, on the workload's per-layer calls, run on a
+    host copy of layer 0 (the caches of these workloads are tens of GB)."""
+    import numpy as np
+
+    import oracle
+    w = step.w
+    L, B, H, D, S = w.dims
+    dims1 = (1, B, H, D, S)
+    n1 = B * H * D * S
+    src, ops = step.cpu_ops()
+    K = src[0][:n1].cpu().numpy().view(np.uint16)
+    V = src[1][:n1].cpu().numpy().view(np.uint16)
+    K2, V2 = np.zeros_like(K), np.zeros_like(V)
+    done_bytes, ran = 0, {}
+    t0 = time.perf_counter()
+    for name, start, count in ops:
+        if time.perf_counter() - t0 > budget_s:
+            break
+        packed = oracle.pack(dims1, K, V, 0, 1, start, count)
+        oracle.unpack(dims1, K2, V2, 0, 1, start, count, packed)
+        done_bytes += 2 * packed.nbytes
+        ran[name] = ran.get(name, 0) + 1
+    elapsed = time.perf_counter() - t0
+    sample = ", ".join(f"{v} x {k} + unpack" for k, v in ran.items())
+    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"layer 0 only: {sample}: {done_bytes / 1e9:.3f} GB of KV payload packed "
+                      f"and unpacked in {elapsed:.1f} s (single-threaded C oracle)"}
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -357,7 +749,7 @@ def main():
     import synth
     w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
-    step = Step(w, args.swap_bank_mib << 20,
+    step = STEPS[w.name](w, args.swap_bank_mib << 20,
                 {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3, "dma_out": 4}[args.transport])
     torch.cuda.synchronize()
 
@@ -407,7 +799,7 @@ def main():
         hbm = [k for k in kernels if not k.startswith("link_copy")]
         dom = max(hbm, key=lambda k: kernels[k]["gpu_ms_per_step"])
         d = kernels[dom]
-        traffic = read_counters(dom)
+        traffic = read_counters(w.name, dom)
         roofline = {"bound": "hbm", "kernel": dom, "achieved": d["GBps"], "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(d["GBps"] / HBM_PEAK_GBPS, 4),
                     "traffic": traffic,
@@ -417,13 +809,17 @@ def main():
     detail = {"kernels": kernels, "link_bytes_per_step": link,
               "link_peak_per_direction_GBps": PCIE_PEAK_GBPS}
     if not args.no_profile:
-        detail["decode_push_us"] = round(decode_push_us(step), 2)
         detail["link_ceiling_GBps"] = {k: round(v, 2) for k, v in link_ceiling(torch).items()}
-        detail["hbm_copy_ceiling_GBps"] = round(hbm_copy_ceiling(torch), 1)
-        detail["large_slices"] = large_slices(step, kv)
+        if isinstance(step, StreamStep):
+            detail["decode_push_us"] = round(decode_push_us(step), 2)
+            detail["hbm_copy_ceiling_GBps"] = round(hbm_copy_ceiling(torch), 1)
+            detail["large_slices"] = large_slices(step, kv)
+        if isinstance(step, SwapStep):
+            detail["microbatch_schedule"] = step.schedule(kv)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(step, args.cpu_baseline_seconds)
+        cpu = (cpu_baseline(step, args.cpu_baseline_seconds) if isinstance(step, StreamStep)
+               else cpu_baseline_layer(step, args.cpu_baseline_seconds))
 
     line = {"metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
@@ -431,8 +827,10 @@ def main():
             "data": "synthetic",
             "config": {"workload": w.name, "L": w.L, "B": w.B, "H": w.H, "D": w.D,
                        "Smax": w.Smax, "kv_dtype": "fp16" if w.dtype == 0 else "bf16",
-                       "prompt_len": w.prompt_len, "decode_steps": w.decode_steps,
-                       "ring_slots": w.ring_slots, "swap_bank_mib": args.swap_bank_mib,
+                       "prompt_len": w.prompt_len or f"U{{{w.len_lo}..{w.len_hi}}}",
+                       "decode_steps": w.decode_steps, "ring_slots": w.ring_slots,
+                       "chunk_tokens": w.chunk_tokens, "microbatches": w.microbatches,
+                       "swap_bank_mib": args.swap_bank_mib,
                        "transport": args.transport,
                        "hw_queues": int(os.environ["GPU_MAX_HW_QUEUES"])},
             "roofline": roofline, "cpu_baseline": cpu, "detail": detail}

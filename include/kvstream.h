@@ -324,8 +324,12 @@ typedef struct kv_mbswap kv_mbswap;
  * ring per microbatch.  prompt_host[x] / prompt_bytes[x]: pinned prompt
  * images, complete before kv_mbswap_start; prompt_len: int32[microbatches*B].
  * `swap_stream`: the stream that runs the swap-in unpacks, so that they
- * overlap the compute stream's work.  The handle keeps the pointers; the
- * caller keeps the memory and the other handles alive. */
+ * overlap the compute stream's work.  The overlap needs the compute stream,
+ * `swap_stream` and the engine's and rings' copy streams on distinct hardware
+ * queues: HIP maps streams onto GPU_MAX_HW_QUEUES queues per process, and
+ * streams that share a queue run one after the other (a round then costs
+ * compute plus transfer instead of the larger of the two).  The handle keeps
+ * the pointers; the caller keeps the memory and the other handles alive. */
 int kv_mbswap_create(kv_mbswap **out, const kv_layout *lay, int32_t microbatches,
                      void *slot0_k, void *slot0_v, void *slot1_k, void *slot1_v,
                      kv_swap *in, kv_ring *const *rings, void *const *prompt_host,
