@@ -19,7 +19,9 @@ Sources (the pages this project follows):
 Function map: ``pack`` is gather, ``unpack`` is scatter, ``swap_out`` is a pack
 over a layer range into host memory, ``swap_in`` the matching unpack,
 ``ring_host`` / ``ring_restore`` the staging-ring image and its restore,
-``prompt_ranges`` the per-row ranges of a prompt-layer pack, ``restart_point``
+``prompt_ranges`` the per-row ranges of a prompt-layer pack, ``stream_out`` /
+``stream_in`` the piece of one worker's partition that another holds and its
+merge (Table 1, Fast prompt KV transfer), ``restart_point``
 the (microbatch, step) a pipeline resumes from after a failure (Failure
 detection and recovery, Fig 10).
 """
@@ -76,6 +78,12 @@ def load(path: str = _LIB):
     lib.oracle_swap_pays.restype = ctypes.c_int
     lib.oracle_swap_pays.argtypes = [_i64, ctypes.c_double, _i64, _i64, ctypes.c_double,
                                      ctypes.c_double, _p, _p]
+    lib.oracle_stream_elems.restype = _i64
+    lib.oracle_stream_elems.argtypes = [_p, _p, _i64, _p]
+    lib.oracle_stream_out.restype = None
+    lib.oracle_stream_out.argtypes = [_i64, _i64, _p, _p, _p, _p, _p, _p, _p]
+    lib.oracle_stream_in.restype = None
+    lib.oracle_stream_in.argtypes = [_i64, _i64, _p, _p, _p, _p, _p, _p, _p]
     lib.oracle_ring_restore.restype = None
     lib.oracle_ring_restore.argtypes = [_i64] * 5 + [_p, _p, _i64, _p, _i64, _p]
     if path == _LIB:
@@ -204,3 +212,50 @@ def swap_pays(N: int, t: float, p: int, B: int, C: float, bw: float, lib=None):
     rhs = np.zeros(1, np.float64)
     r = lib.oracle_swap_pays(N, t, p, B, C, bw, _ptr(lhs), _ptr(rhs))
     return bool(r), float(lhs[0]), float(rhs[0])
+
+
+def _part(p) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(p, dtype=np.int64).reshape(-1))
+    if a.size != 6:
+        raise ValueError("a partition is (layer0, layers, head0, heads, row0, rows)")
+    return a
+
+
+def part_dims(part, D: int, Smax: int):
+    """(L, B, H, D, Smax) of the cache that holds `part`."""
+    p = _part(part)
+    return (int(p[1]), int(p[5]), int(p[3]), D, Smax)
+
+
+def stream_elems(src, dst, D: int, count, lib=None) -> int:
+    """16-bit elements of the piece `src` sends `dst` (count: per source row)."""
+    lib = lib or load()
+    s, d = _part(src), _part(dst)
+    c = _rows(count, int(s[5]))
+    return lib.oracle_stream_elems(_ptr(s), _ptr(d), D, _ptr(c))
+
+
+def stream_out(src, dst, D: int, Smax: int, key, value, start, count, lib=None) -> np.ndarray:
+    """The piece of the source partition's caches that `dst` holds."""
+    lib = lib or load()
+    s, d = _part(src), _part(dst)
+    key, value = _u16(key, "key"), _u16(value, "value")
+    st, ct = _rows(start, int(s[5])), _rows(count, int(s[5]))
+    out = np.empty(stream_elems(s, d, D, ct, lib), dtype=np.uint16)
+    lib.oracle_stream_out(D, Smax, _ptr(s), _ptr(d), _ptr(key), _ptr(value), _ptr(st), _ptr(ct),
+                          _ptr(out))
+    return out
+
+
+def stream_in(dst, src, D: int, Smax: int, key, value, start, count, piece, lib=None) -> None:
+    """Merge the piece `src` sent into the destination caches (in place)."""
+    lib = lib or load()
+    s, d = _part(src), _part(dst)
+    key, value = _u16(key, "key"), _u16(value, "value")
+    st, ct = _rows(start, int(d[5])), _rows(count, int(d[5]))
+    piece = _u16(np.ascontiguousarray(piece), "piece")
+    need = lib.oracle_stream_elems(_ptr(d), _ptr(s), D, _ptr(ct))   # the meet is symmetric
+    if piece.size < need:
+        raise ValueError(f"piece holds {piece.size} elements, {need} needed")
+    lib.oracle_stream_in(D, Smax, _ptr(d), _ptr(s), _ptr(key), _ptr(value), _ptr(st), _ptr(ct),
+                         _ptr(piece))

@@ -49,6 +49,13 @@
  *    Fig 10): a (microbatch, step) pair counts as replicated once every worker
  *    has acknowledged it; steps run in (step, microbatch) order; the pipeline
  *    restarts at the first pair in that order that is not replicated.
+ *  - stream_out / stream_in (Table 1, Fast prompt KV transfer): a worker's
+ *    cache holds one partition of the model's KV -- a global layer range, a
+ *    global head range and a global request (row) range, stored at local
+ *    indices from 0.  The piece a source sends a destination is the
+ *    intersection of the two partitions, in the packed order above taken over
+ *    global (layer, K/V, row, head, token, dim); the destination merges each
+ *    piece it receives at its own local indices.
  *
  * Every function here is plain C99, single-threaded.
  */
@@ -206,4 +213,91 @@ int oracle_swap_pays(int64_t N, double t, int64_t p, int64_t B, double C, double
     *lhs = 2.0 * (double)N * t;
     *rhs = sum;
     return *lhs >= *rhs;
+}
+
+/* ---- stream_out / stream_in between partitions ---------------------------
+ * A partition is six integers: {layer0, layers, head0, heads, row0, rows}.
+ * The worker's cache has L = layers, H = heads, B = rows, and its local
+ * (l, b, h) is the global (layer0 + l, row0 + b, head0 + h). */
+
+/* Intersection [*lo, *hi) of [a0, a0 + an) and [b0, b0 + bn). */
+static void oracle_meet(int64_t a0, int64_t an, int64_t b0, int64_t bn, int64_t *lo, int64_t *hi)
+{
+    *lo = a0 > b0 ? a0 : b0;
+    *hi = (a0 + an) < (b0 + bn) ? (a0 + an) : (b0 + bn);
+    if (*hi < *lo)
+        *hi = *lo;
+}
+
+/* 16-bit elements of the piece `src` sends `dst`: 2 * layers * heads * D *
+ * (sum of the source's counts over the shared rows).  `count` is per source row. */
+int64_t oracle_stream_elems(const int64_t *src, const int64_t *dst, int64_t D,
+                            const int32_t *count)
+{
+    int64_t l_lo, l_hi, h_lo, h_hi, r_lo, r_hi;
+    oracle_meet(src[0], src[1], dst[0], dst[1], &l_lo, &l_hi);
+    oracle_meet(src[2], src[3], dst[2], dst[3], &h_lo, &h_hi);
+    oracle_meet(src[4], src[5], dst[4], dst[5], &r_lo, &r_hi);
+    int64_t tokens = 0;
+    for (int64_t r = r_lo; r < r_hi; ++r)
+        tokens += count[r - src[4]];
+    return 2 * (l_hi - l_lo) * (h_hi - h_lo) * D * tokens;
+}
+
+/* stream_out: the piece of the source cache that the destination holds, in
+ * the packed order over global indices.  start/count: per source row. */
+void oracle_stream_out(int64_t D, int64_t Smax, const int64_t *src, const int64_t *dst,
+                       const uint16_t *key, const uint16_t *value,
+                       const int32_t *start, const int32_t *count, uint16_t *out)
+{
+    const int64_t L = src[1], H = src[3], B = src[5];
+    int64_t l_lo, l_hi, h_lo, h_hi, r_lo, r_hi;
+    oracle_meet(src[0], src[1], dst[0], dst[1], &l_lo, &l_hi);
+    oracle_meet(src[2], src[3], dst[2], dst[3], &h_lo, &h_hi);
+    oracle_meet(src[4], src[5], dst[4], dst[5], &r_lo, &r_hi);
+    int64_t o = 0;
+    for (int64_t gl = l_lo; gl < l_hi; ++gl)
+        for (int kv = 0; kv < 2; ++kv)
+            for (int64_t gr = r_lo; gr < r_hi; ++gr)
+                for (int64_t gh = h_lo; gh < h_hi; ++gh) {
+                    const int64_t l = gl - src[0], b = gr - src[4], h = gh - src[2];
+                    for (int64_t t = 0; t < count[b]; ++t)
+                        for (int64_t d = 0; d < D; ++d) {
+                            const int64_t s = start[b] + t;
+                            if (kv == 0)
+                                out[o] = key[oracle_key_offset(L, B, H, D, Smax, l, b, h, s, d)];
+                            else
+                                out[o] = value[oracle_value_offset(L, B, H, D, Smax, l, b, h, s, d)];
+                            ++o;
+                        }
+                }
+}
+
+/* stream_in: merge the piece `src` sent into the destination cache at the
+ * destination's local indices.  start/count: per destination row. */
+void oracle_stream_in(int64_t D, int64_t Smax, const int64_t *dst, const int64_t *src,
+                      uint16_t *key, uint16_t *value,
+                      const int32_t *start, const int32_t *count, const uint16_t *in)
+{
+    const int64_t L = dst[1], H = dst[3], B = dst[5];
+    int64_t l_lo, l_hi, h_lo, h_hi, r_lo, r_hi;
+    oracle_meet(src[0], src[1], dst[0], dst[1], &l_lo, &l_hi);
+    oracle_meet(src[2], src[3], dst[2], dst[3], &h_lo, &h_hi);
+    oracle_meet(src[4], src[5], dst[4], dst[5], &r_lo, &r_hi);
+    int64_t o = 0;
+    for (int64_t gl = l_lo; gl < l_hi; ++gl)
+        for (int kv = 0; kv < 2; ++kv)
+            for (int64_t gr = r_lo; gr < r_hi; ++gr)
+                for (int64_t gh = h_lo; gh < h_hi; ++gh) {
+                    const int64_t l = gl - dst[0], b = gr - dst[4], h = gh - dst[2];
+                    for (int64_t t = 0; t < count[b]; ++t)
+                        for (int64_t d = 0; d < D; ++d) {
+                            const int64_t s = start[b] + t;
+                            if (kv == 0)
+                                key[oracle_key_offset(L, B, H, D, Smax, l, b, h, s, d)] = in[o];
+                            else
+                                value[oracle_value_offset(L, B, H, D, Smax, l, b, h, s, d)] = in[o];
+                            ++o;
+                        }
+                }
 }

@@ -24,7 +24,13 @@ The pins:
 * pack leaves the source caches untouched;
 * prompt ranges: hand-worked clip cases;
 * ring restore: the final cache holds, at every position, the value of the
-  latest step that named it (last writer wins), written out per element.
+  latest step that named it (last writer wins), written out per element;
+* stream_out / stream_in between partitions: coordinate-decoded pieces list
+  exactly the shared (global layer, K/V, row, head, token, dim) elements in
+  order; a partition sent to itself, or split by layers or rows only, equals
+  the already-pinned pack; a split into a grid of destinations followed by
+  the merge back reproduces the source (numpy slices of the logical
+  [l, b, h, s, d] views), and the pieces' sizes add up to the whole.
 """
 from __future__ import annotations
 
@@ -257,6 +263,100 @@ def check_swap_pays(lib):
     assert (pays, lhs, rhs) == (False, 4.0, 12.0)
 
 
+def _logical_k(K6):
+    """[L,B,H,D/8,S,8] -> [L,B,H,S,D] view order (a copy)."""
+    L, B, H, C, S, _ = K6.shape
+    return K6.transpose(0, 1, 2, 4, 3, 5).reshape(L, B, H, S, C * 8)
+
+
+def _meet(a0, an, b0, bn):
+    lo, hi = max(a0, b0), min(a0 + an, b0 + bn)
+    return range(lo, max(lo, hi))
+
+
+def check_stream(lib):
+    D, S = 16, 6
+    src = (2, 3, 1, 3, 10, 3)                 # layers 2..4, heads 1..3, requests 10..12
+    dims = oracle.part_dims(src, D, S)
+    K, V, n = coord_caches(dims)
+    Kf, Vf = K.ravel().copy(), V.ravel().copy()
+    start, count = [1, 0, 3], [4, 6, 2]
+    dsts = [src, (0, 10, 0, 10, 0, 20), (3, 1, 0, 2, 11, 5), (0, 3, 2, 5, 0, 11),
+            (4, 4, 3, 1, 12, 1), (5, 2, 0, 8, 0, 20), (2, 3, 0, 8, 13, 4), (2, 2, 2, 1, 9, 3)]
+    for dst in dsts:
+        out = oracle.stream_out(src, dst, D, S, Kf, Vf, start, count, lib=lib)
+        got = decode(out, dims, n)
+        got[:, 0] += src[0]                  # local -> global
+        got[:, 2] += src[4]
+        got[:, 3] += src[2]
+        want = [(gl, kv, gr, gh, s, d)
+                for gl in _meet(src[0], src[1], dst[0], dst[1]) for kv in (0, 1)
+                for gr in _meet(src[4], src[5], dst[4], dst[5])
+                for gh in _meet(src[2], src[3], dst[2], dst[3])
+                for s in range(start[gr - src[4]], start[gr - src[4]] + count[gr - src[4]])
+                for d in range(D)]
+        want = np.array(want, dtype=np.int64).reshape(-1, 6)
+        assert got.shape == want.shape and np.array_equal(got, want), f"stream_out piece for {dst}"
+    assert np.array_equal(Kf, K.ravel()) and np.array_equal(Vf, V.ravel()), "stream_out wrote its input"
+    # special cases that reduce to the pinned pack
+    whole = oracle.stream_out(src, src, D, S, Kf, Vf, start, count, lib=lib)
+    assert np.array_equal(whole, oracle.pack(dims, Kf, Vf, 0, 3, start, count, lib=lib))
+    lay1 = oracle.stream_out(src, (3, 1, 0, 9, 0, 99), D, S, Kf, Vf, start, count, lib=lib)
+    assert np.array_equal(lay1, oracle.pack(dims, Kf, Vf, 1, 1, start, count, lib=lib))
+    rows = oracle.stream_out(src, (0, 9, 0, 9, 11, 1), D, S, Kf, Vf, start, count, lib=lib)
+    assert np.array_equal(rows, oracle.pack(dims, Kf, Vf, 0, 3, start, [0, 6, 0], lib=lib))
+
+    # split into a 2 x 2 x 2 grid of destinations, then merge back
+    D, S = 16, 7
+    src = (4, 4, 8, 4, 20, 4)
+    dims = oracle.part_dims(src, D, S)
+    rng = np.random.default_rng(21)
+    K6 = rng.integers(0, 1 << 16, size=(4, 4, 4, D // 8, S, 8), dtype=np.uint32).astype(np.uint16)
+    V5 = rng.integers(0, 1 << 16, size=(4, 4, 4, S, D), dtype=np.uint32).astype(np.uint16)
+    start = np.array([0, 2, 5, 1], np.int32)
+    count = np.array([7, 3, 0, 6], np.int32)
+    Kl, Vl = _logical_k(K6), V5
+    total = 0
+    back_k = np.zeros_like(K6)
+    back_v = np.zeros_like(V5)
+    for dl, dh, dr in itertools.product((0, 2), (0, 2), (0, 2)):
+        dst = (4 + dl, 2, 8 + dh, 2, 20 + dr, 2)
+        shift = 1 if dr else 0               # the destination keeps its tokens one slot later
+        dst_start = [int(start[dr + b]) + (shift if start[dr + b] + count[dr + b] + shift <= S else 0)
+                     for b in range(2)]
+        dst_count = [int(count[dr + b]) for b in range(2)]
+        piece = oracle.stream_out(src, dst, D, S, K6.ravel(), V5.ravel(), start, count, lib=lib)
+        total += piece.size
+        dK = np.full((2, 2, 2, D // 8, S, 8), 0xABCD, np.uint16)
+        dV = np.full((2, 2, 2, S, D), 0xABCD, np.uint16)
+        dk, dv = dK.reshape(-1), dV.reshape(-1)
+        oracle.stream_in(dst, src, D, S, dk, dv, dst_start, dst_count, piece, lib=lib)
+        dKl = _logical_k(dK)
+        for b in range(2):
+            a, c, e = int(start[dr + b]), dst_count[b], dst_start[b]
+            assert np.array_equal(dKl[:, b, :, e:e + c], Kl[dl:dl + 2, dr + b, dh:dh + 2, a:a + c]), \
+                f"merged K of {dst}"
+            assert np.array_equal(dV[:, b, :, e:e + c], Vl[dl:dl + 2, dr + b, dh:dh + 2, a:a + c]), \
+                f"merged V of {dst}"
+            mk = np.ones(dKl.shape, bool)
+            mk[:, b, :, e:e + c] = False
+            mk[:, 1 - b] = False
+            assert np.all(dKl[mk] == 0xABCD) and np.all(dV[mk] == 0xABCD), "stream_in wrote outside"
+        # and back to a source-shaped cache
+        back = oracle.stream_out(dst, src, D, S, dk, dv, dst_start, dst_count, lib=lib)
+        assert np.array_equal(back, piece), "piece changed on the way back"
+        oracle.stream_in(src, dst, D, S, back_k.reshape(-1), back_v.reshape(-1), start, count,
+                         back, lib=lib)
+    assert total == oracle.pack_elems(dims, 4, count, lib=lib), "pieces do not add up to the whole"
+    mk = np.zeros(K6.shape, bool)
+    mv = np.zeros(V5.shape, bool)
+    for b in range(4):
+        mk[:, b, :, :, start[b]:start[b] + count[b], :] = True
+        mv[:, b, :, start[b]:start[b] + count[b], :] = True
+    assert np.array_equal(back_k[mk], K6[mk]) and not back_k[~mk].any(), "split + merge lost K"
+    assert np.array_equal(back_v[mv], V5[mv]) and not back_v[~mv].any(), "split + merge lost V"
+
+
 def run_all(lib):
     check_offsets(lib)
     check_brute_force(lib)
@@ -266,6 +366,7 @@ def run_all(lib):
     check_ring(lib)
     check_restart_point(lib)
     check_swap_pays(lib)
+    check_stream(lib)
 
 
 if __name__ == "__main__":          # used by the mutant test: exit 0 iff every pin holds

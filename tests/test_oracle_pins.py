@@ -53,6 +53,10 @@ def test_restart_point_hand_worked(lib):
     oracle_pins.check_restart_point(lib)
 
 
+def test_stream_split_and_merge(lib):
+    oracle_pins.check_stream(lib)
+
+
 def test_swap_pays_closed_forms(lib):
     oracle_pins.check_swap_pays(lib)
 
@@ -87,15 +91,16 @@ MUTANTS = {
                                 "return (((l * B + b) * H + h) * D + d) * Smax + s;"),
     "value_head_term_dropped": ("return (((l * B + b) * H + h) * Smax + s) * D + d;",
                                 "return (((l * B + b) * H + 0) * Smax + s) * D + d;"),
-    "pack_start_dropped": ("int64_t s = start[b] + t;\n                            if (kv == 0)\n                                out",
-                           "int64_t s = t;\n                            if (kv == 0)\n                                out"),
-    "pack_kv_swapped": ("out[o] = key[", "out[o] = value["),
+    "pack_start_dropped": ("  int64_t s = start[b] + t;\n                            if (kv == 0)\n                                out",
+                           "  int64_t s = t;\n                            if (kv == 0)\n                                out"),
+    "pack_kv_swapped": ("  int64_t s = start[b] + t;\n                            if (kv == 0)\n                                out[o] = key[",
+                        "  int64_t s = start[b] + t;\n                            if (kv == 0)\n                                out[o] = value["),
     "pack_last_token_dropped": ("for (int64_t t = 0; t < count[b]; ++t)\n                        for (int64_t d = 0; d < D; ++d) {\n                            int64_t s = start[b] + t;\n                            if (kv == 0)\n                                out",
                                 "for (int64_t t = 0; t + 1 < count[b]; ++t)\n                        for (int64_t d = 0; d < D; ++d) {\n                            int64_t s = start[b] + t;\n                            if (kv == 0)\n                                out"),
-    "unpack_kv_swapped": ("key[oracle_key_offset(L, B, H, D, Smax, l, b, h, s, d)] = in[o];",
-                          "value[oracle_key_offset(L, B, H, D, Smax, l, b, h, s, d)] = in[o];"),
-    "unpack_start_dropped": ("int64_t s = start[b] + t;\n                            if (kv == 0)\n                                key",
-                             "int64_t s = t;\n                            if (kv == 0)\n                                key"),
+    "unpack_kv_swapped": ("  int64_t s = start[b] + t;\n                            if (kv == 0)\n                                key[oracle_key_offset(L, B, H, D, Smax, l, b, h, s, d)] = in[o];",
+                          "  int64_t s = start[b] + t;\n                            if (kv == 0)\n                                value[oracle_key_offset(L, B, H, D, Smax, l, b, h, s, d)] = in[o];"),
+    "unpack_start_dropped": ("  int64_t s = start[b] + t;\n                            if (kv == 0)\n                                key",
+                             "  int64_t s = t;\n                            if (kv == 0)\n                                key"),
     "size_factor_dropped": ("return 2 * layer_count * H * D * tokens;",
                             "return layer_count * H * D * tokens;"),
     "prompt_clip_missing": ("if (row_len != NULL && row_len[b] < end)",
@@ -110,6 +115,14 @@ MUTANTS = {
     "swap_pays_batch_dropped": ("double transfer = (double)i * (double)B * C / bw;",
                                 "double transfer = (double)i * C / bw;"),
     "swap_pays_single_run": ("*lhs = 2.0 * (double)N * t;", "*lhs = (double)N * t;"),
+    "stream_out_head_from_meet": ("b = gr - src[4], h = gh - src[2];", "b = gr - src[4], h = gh - h_lo;"),
+    "stream_in_row_from_source": ("const int64_t l = gl - dst[0], b = gr - dst[4]",
+                                  "const int64_t l = gl - dst[0], b = gr - src[4]"),
+    "stream_meet_upper_from_first": ("*hi = (a0 + an) < (b0 + bn) ? (a0 + an) : (b0 + bn);",
+                                     "*hi = a0 + an;"),
+    "stream_out_heads_before_rows": ("            for (int64_t gr = r_lo; gr < r_hi; ++gr)\n                for (int64_t gh = h_lo; gh < h_hi; ++gh) {\n                    const int64_t l = gl - src[0]",
+                                     "            for (int64_t gh = h_lo; gh < h_hi; ++gh)\n                for (int64_t gr = r_lo; gr < r_hi; ++gr) {\n                    const int64_t l = gl - src[0]"),
+    "stream_size_counts_destination_rows": ("tokens += count[r - src[4]];", "tokens += count[r - dst[4]];"),
     "ring_order_reversed": ("for (int64_t j = 0; j < steps; ++j)\n        oracle_unpack(L, B, H, D, Smax, key, value, 0, L, pos + j * B",
                             "for (int64_t j = steps - 1; j >= 0; --j)\n        oracle_unpack(L, B, H, D, Smax, key, value, 0, L, pos + j * B"),
 }
