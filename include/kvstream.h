@@ -155,6 +155,49 @@ int kv_unpack_prompt_layer(const kv_layout *lay, void *k, void *v,
                            hipStream_t s);
 
 /* ---------------------------------------------------------------------------
+ * stream_out / stream_in between partitions ([DV, DejaVuLib primitives,
+ * Table 1]; Fast prompt KV transfer): the source and destination workers may
+ * split the model differently (pipeline depth: layer ranges; tensor
+ * parallelism: head ranges; batch size: request ranges).  A worker's cache
+ * holds one partition, stored at local indices from 0.  The piece a source
+ * sends a destination is the intersection of the two partitions, packed in
+ * the order of kv_pack_tokens over the shared layers, rows and heads (global
+ * order); the source splits its cache into one piece per destination, the
+ * destination merges the pieces of all its sources.
+ */
+typedef struct kv_part {
+    int32_t layer0, layers;  /* global layers [layer0, layer0 + layers) = local layers [0, layers) */
+    int32_t head0, heads;    /* global heads [head0, head0 + heads) = local heads [0, heads) */
+    int32_t row0, rows;      /* global requests [row0, row0 + rows) = local rows [0, rows) */
+} kv_part;
+
+/* Bytes of the piece `self` and `peer` share: 2 * (shared layers) *
+ * (shared heads) * D * P * (sum of count_b over the shared rows), count
+ * being int32[self->rows] (NULL: one token per row).  0 when they do not
+ * meet.  `lay` must describe self's cache (L = layers, B = rows, H = heads),
+ * else KV_EINVAL.  Pure host call; negative kv_status on error. */
+int64_t kv_stream_bytes(const kv_layout *lay, const kv_part *self, const kv_part *peer,
+                        const int32_t *count);
+
+/* stream_out: pack the piece of src's cache (k, v; layout `lay`) that `dst`
+ * holds into `staging` (device memory).  start/count: int32[src->rows], the
+ * token range [start_b, start_b + count_b) of each local row (count NULL:
+ * one token per row); rows outside dst are not read.  Errors as
+ * kv_pack_tokens; an empty intersection enqueues nothing. */
+int kv_stream_out(const kv_layout *lay, const kv_part *src, const void *k, const void *v,
+                  const kv_part *dst, const int32_t *start, const int32_t *count,
+                  void *staging, int64_t staging_bytes, hipStream_t s);
+
+/* stream_in: merge the piece `src` sent (staging, as kv_stream_out wrote
+ * it) into dst's cache (k, v; layout `lay`).  start/count: int32[dst->rows]
+ * in dst's local rows; the shared rows' counts must equal the source's
+ * (staging_bytes must cover the piece as these counts size it, else
+ * KV_ESIZE).  Writes exactly the piece's elements. */
+int kv_stream_in(const kv_layout *lay, const kv_part *dst, void *k, void *v,
+                 const kv_part *src, const int32_t *start, const int32_t *count,
+                 const void *staging, int64_t staging_bytes, hipStream_t s);
+
+/* ---------------------------------------------------------------------------
  * Swap engine: staged, layer-pipelined transfers between a cache and pinned
  * host memory ([DV, Microbatch swapping workflow, Fig 9]; flush/fetch in
  * Table 1, local leg).  Two caller-owned device banks alternate: the pack of

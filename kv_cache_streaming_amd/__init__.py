@@ -59,6 +59,13 @@ class kv_chunk(ctypes.Structure):
                 ("bank_off", ctypes.c_int64 * 2), ("bytes", ctypes.c_int64 * 2)]
 
 
+class kv_part(ctypes.Structure):
+    """A worker's partition: global layer, head and request (row) ranges."""
+    _fields_ = [("layer0", ctypes.c_int32), ("layers", ctypes.c_int32),
+                ("head0", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("row0", ctypes.c_int32), ("rows", ctypes.c_int32)]
+
+
 class kv_kernel_stat(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 40), ("launches", ctypes.c_int64),
                 ("ms", ctypes.c_double), ("bytes", ctypes.c_int64)]
@@ -68,6 +75,7 @@ _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _LAY = ctypes.POINTER(kv_layout)
+_PART = ctypes.POINTER(kv_part)
 
 # name -> (restype, argtypes), mirroring include/kvstream.h
 _SIGNATURES = {
@@ -79,6 +87,9 @@ _SIGNATURES = {
     "kv_unpack_tokens": (ctypes.c_int, [_LAY, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P]),
     "kv_pack_prompt_layer": (ctypes.c_int, [_LAY, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P]),
     "kv_unpack_prompt_layer": (ctypes.c_int, [_LAY, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P]),
+    "kv_stream_bytes": (_I64, [_LAY, _PART, _PART, _P]),
+    "kv_stream_out": (ctypes.c_int, [_LAY, _PART, _P, _P, _PART, _P, _P, _P, _I64, _P]),
+    "kv_stream_in": (ctypes.c_int, [_LAY, _PART, _P, _P, _PART, _P, _P, _P, _I64, _P]),
     "kv_swap_create": (ctypes.c_int, [ctypes.POINTER(_P), _LAY, _P, _P, _I64, _P, _I32]),
     "kv_swap_destroy": (ctypes.c_int, [_P]),
     "kv_swap_out": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
@@ -267,6 +278,44 @@ def kv_swap_plan(lay, layer_begin, layer_count, start, count, bank_bytes):
                         row_begin=c.row_begin, row_end=c.row_end, staged_bytes=c.staged_bytes,
                         pieces=[(c.host_off[p], c.bank_off[p], c.bytes[p]) for p in range(c.pieces)]))
     return out
+
+
+# ---------------------------------------------------------------- partitions
+
+def _part(p) -> kv_part:
+    if isinstance(p, kv_part):
+        return p
+    vals = [int(x) for x in p]
+    if len(vals) != 6:
+        raise ValueError("a partition is (layer0, layers, head0, heads, row0, rows)")
+    return kv_part(*vals)
+
+
+def kv_stream_bytes(lay, self_part, peer_part, count=None) -> int:
+    me = _part(self_part)
+    ct = _Rows(count, me.rows, "count")
+    return _check(_lib.kv_stream_bytes(ctypes.byref(lay), ctypes.byref(me),
+                                       ctypes.byref(_part(peer_part)), ct.ptr), "kv_stream_bytes")
+
+
+def kv_stream_out(lay, src_part, k, v, dst_part, start, count, staging, staging_bytes=None,
+                  stream=None) -> None:
+    src = _part(src_part)
+    st, ct = _Rows(start, src.rows, "start"), _Rows(count, src.rows, "count")
+    nb = _nbytes(staging) if staging_bytes is None else staging_bytes
+    _check(_lib.kv_stream_out(ctypes.byref(lay), ctypes.byref(src), _addr(k), _addr(v),
+                              ctypes.byref(_part(dst_part)), st.ptr, ct.ptr, _addr(staging), nb,
+                              _stream(stream)), "kv_stream_out")
+
+
+def kv_stream_in(lay, dst_part, k, v, src_part, start, count, staging, staging_bytes=None,
+                 stream=None) -> None:
+    dst = _part(dst_part)
+    st, ct = _Rows(start, dst.rows, "start"), _Rows(count, dst.rows, "count")
+    nb = _nbytes(staging) if staging_bytes is None else staging_bytes
+    _check(_lib.kv_stream_in(ctypes.byref(lay), ctypes.byref(dst), _addr(k), _addr(v),
+                             ctypes.byref(_part(src_part)), st.ptr, ct.ptr, _addr(staging), nb,
+                             _stream(stream)), "kv_stream_in")
 
 
 # ---------------------------------------------------------------- swap engine

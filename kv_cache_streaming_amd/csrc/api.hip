@@ -160,7 +160,8 @@ int build_rows(const kv_layout &lay, const int32_t *start, const int32_t *count,
 }
 
 int enqueue_copy(bool pack, const kv_layout &lay, const void *k, const void *v, int32_t l0,
-                 int32_t nl, const RowTable &rt, int32_t max_count, void *stage, hipStream_t s)
+                 int32_t nl, const RowTable &rt, int32_t max_count, void *stage, hipStream_t s,
+                 int32_t h0, int32_t nh)
 {
     Geometry g;
     g.k = (uint4 *)k;
@@ -172,6 +173,8 @@ int enqueue_copy(bool pack, const kv_layout &lay, const void *k, const void *v, 
     g.Smax = lay.Smax;
     g.l0 = l0;
     g.nl = nl;
+    g.h0 = nh < 0 ? 0 : h0;
+    g.nh = nh < 0 ? lay.H : nh;
     g.tiles_per_row = 0;
     g.tile_tokens = 0;
     g.T = rt.off[lay.B];

@@ -41,8 +41,8 @@ __global__ __launch_bounds__(kThreads) void copy_rows_small(Geometry g, RowTable
     const uint32_t C = (uint32_t)g.C;
     uint32_t r = gid / C;
     const uint32_t c = gid - r * C;
-    const uint32_t h = r % (uint32_t)g.H;
-    r /= (uint32_t)g.H;
+    const uint32_t h = r % (uint32_t)g.nh;     // head within the moved range
+    r /= (uint32_t)g.nh;
     const uint32_t b = r % (uint32_t)g.B;
     r /= (uint32_t)g.B;
     if (r >= (uint32_t)g.nl)
@@ -53,11 +53,11 @@ __global__ __launch_bounds__(kThreads) void copy_rows_small(Geometry g, RowTable
     if (cnt <= 0)
         return;
     const int32_t s0 = rt.start[b];
-    const int64_t unit = ((int64_t)(g.l0 + li) * g.B + b) * g.H + h;
+    const int64_t unit = ((int64_t)(g.l0 + li) * g.B + b) * g.H + g.h0 + h;
     uint4 *kc = g.k + (unit * C + c) * g.Smax + s0;       // token t: kc[t]
     uint4 *vc = g.v + (unit * g.Smax + s0) * C + c;       // token t: vc[t*C]
-    const int64_t blk = (int64_t)g.H * g.T * C;           // one (layer, K|V) block
-    uint4 *ks = g.stage + 2 * (int64_t)li * blk + ((int64_t)g.H * off + (int64_t)h * cnt) * C + c;
+    const int64_t blk = (int64_t)g.nh * g.T * C;          // one (layer, K|V) block
+    uint4 *ks = g.stage + 2 * (int64_t)li * blk + ((int64_t)g.nh * off + (int64_t)h * cnt) * C + c;
     uint4 *vs = ks + blk;                                 // token t: ks[t*C], vs[t*C]
 
     int32_t t = 0;
@@ -130,8 +130,8 @@ __global__ __launch_bounds__(kThreads) void copy_tiles(Geometry g, RowTable rt)
     int32_t bid = blockIdx.x;
     const int32_t tile = bid % g.tiles_per_row;
     bid /= g.tiles_per_row;
-    const int32_t h = bid % g.H;
-    bid /= g.H;
+    const int32_t h = bid % g.nh;     // head within the moved range
+    bid /= g.nh;
     const int32_t b = bid % g.B;
     const int32_t li = bid / g.B;
 
@@ -144,12 +144,12 @@ __global__ __launch_bounds__(kThreads) void copy_tiles(Geometry g, RowTable rt)
     const int32_t nvec = nt * C;
     const int32_t s0 = rt.start[b] + t0;
 
-    const int64_t unit = ((int64_t)(g.l0 + li) * g.B + b) * g.H + h;
+    const int64_t unit = ((int64_t)(g.l0 + li) * g.B + b) * g.H + g.h0 + h;
     u32x4 *kc = (u32x4 *)(g.k + unit * C * g.Smax + s0);     // chunk c, token i: kc[c*Smax + i]
     u32x4 *vc = (u32x4 *)(g.v + (unit * g.Smax + s0) * C);   // nvec contiguous vectors
-    const int64_t blk = (int64_t)g.H * g.T * C;
+    const int64_t blk = (int64_t)g.nh * g.T * C;
     u32x4 *ks = (u32x4 *)(g.stage + 2 * (int64_t)li * blk +
-                          ((int64_t)g.H * off + (int64_t)h * cnt + t0) * C);
+                          ((int64_t)g.nh * off + (int64_t)h * cnt + t0) * C);
     u32x4 *vs = ks + blk;                                    // both nvec contiguous vectors
     const int tid = threadIdx.x;
     u32x4 kr[PER], vr[PER];
@@ -314,11 +314,11 @@ int launch_copy(bool pack, const Geometry &g0, const RowTable &rt, int32_t max_c
     Geometry g = g0;
     int64_t per_layer;
     if (small) {
-        per_layer = ((int64_t)g.B * g.H * g.C + kThreads - 1) / kThreads;
+        per_layer = ((int64_t)g.B * g.nh * g.C + kThreads - 1) / kThreads;
     } else {
         g.tile_tokens = tile_tokens_for(g.C);
         g.tiles_per_row = (max_count + g.tile_tokens - 1) / g.tile_tokens;
-        per_layer = (int64_t)g.B * g.H * g.tiles_per_row;
+        per_layer = (int64_t)g.B * g.nh * g.tiles_per_row;
     }
     // A launch covers whole layers.  Keep every grid within 2^31-1 blocks and,
     // for the small kernel, its flat thread id within 2^31.
@@ -327,7 +327,7 @@ int launch_copy(bool pack, const Geometry &g0, const RowTable &rt, int32_t max_c
         (int32_t)std::max<int64_t>(1, std::min<int64_t>(g.nl, max_blocks / per_layer));
     const char *name = small ? (pack ? "pack_rows_small" : "unpack_rows_small")
                              : (pack ? "pack_tiles" : "unpack_tiles");
-    const int64_t blk = (int64_t)g.H * g.T * g.C;  // vectors per (layer, K|V) block
+    const int64_t blk = (int64_t)g.nh * g.T * g.C;  // vectors per (layer, K|V) block
 
     for (int32_t done = 0; done < g0.nl; done += layers_per_launch) {
         Geometry gl = g;
@@ -338,7 +338,7 @@ int launch_copy(bool pack, const Geometry &g0, const RowTable &rt, int32_t max_c
         void *tok = profiling_enabled() ? profile_start(s) : nullptr;
         hipError_t e;
         if (small) {
-            const int64_t threads = (int64_t)gl.nl * gl.B * gl.H * gl.C;
+            const int64_t threads = (int64_t)gl.nl * gl.B * gl.nh * gl.C;
             const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads)), block(kThreads);
             if (pack)
                 copy_rows_small<true><<<grid, block, 0, s>>>(gl, rt);

@@ -24,8 +24,9 @@ struct Geometry {
     uint4 *k;        // key cache base
     uint4 *v;        // value cache base
     uint4 *stage;    // packed buffer base
-    int32_t B, H, C, Smax;  // C = D/8 vectors per head row
+    int32_t B, H, C, Smax;  // C = D/8 vectors per head row; H = heads of the cache
     int32_t l0, nl;         // layer range
+    int32_t h0, nh;         // head range [h0, h0 + nh) moved; the packed format has nh heads
     int32_t tiles_per_row;  // tile kernel: tiles per row (ceil(max count / tile tokens))
     int32_t tile_tokens;    // tile kernel: tokens per tile
     int64_t T;              // sum of counts
@@ -53,8 +54,10 @@ int prompt_rows(const kv_layout &lay, int32_t tok_begin, int32_t tok_count,
 
 // Validated pack/unpack of a whole call (used by the public entry points and
 // the engines).  Buffers are assumed checked by the caller.
+// Heads [h0, h0 + nh) only when nh >= 0 (default: all heads).
 int enqueue_copy(bool pack, const kv_layout &lay, const void *k, const void *v, int32_t l0,
-                 int32_t nl, const RowTable &rt, int32_t max_count, void *stage, hipStream_t s);
+                 int32_t nl, const RowTable &rt, int32_t max_count, void *stage, hipStream_t s,
+                 int32_t h0 = 0, int32_t nh = -1);
 
 // ---- kernels (kernels.hip) ----
 // Launches the pack (or unpack) kernels for one call; returns KV_OK or KV_EHIP.
