@@ -278,6 +278,50 @@ class RingStep:
         B = self.w.B
         return self.A, [("decode pack", p, [1] * B) for p in self.positions]
 
+    def repartition(self, kv, reps=3):
+        """stream_out / stream_in of the slice's prompt region (every row's
+        current length) into 2 pipeline stages x 2 tensor-parallel ranks:
+        each piece is 8 layers x 36 heads; rates in HBM bytes (read + write of
+        the piece) per second, pieces timed one after another with events."""
+        import synth
+        torch, w, lay = self.torch, self.w, self.lay
+        L, B, H = w.L, w.B, w.H
+        src = (0, L, 0, H, 0, B)
+        lens = [int(x) for x in synth.row_lengths(w)]
+        start = [0] * B
+        dsts = [(l0, L // 2, h0, H // 2, 0, B) for l0 in (0, L // 2) for h0 in (0, H // 2)]
+        nbytes = kv.kv_stream_bytes(lay, src, dsts[0], lens)
+        dlay = kv.kv_layout_init(L // 2, B, H // 2, w.D, w.Smax, w.dtype)
+        dn = (L // 2) * B * (H // 2) * w.D * w.Smax
+        caches = [(torch.empty(dn, dtype=torch.int16, device="cuda"),
+                   torch.empty(dn, dtype=torch.int16, device="cuda")) for _ in dsts]
+        st = [torch.empty(nbytes // 2, dtype=torch.int16, device="cuda") for _ in dsts]
+        s = self.s["t"]
+        out = {"pieces": len(dsts), "piece_bytes": nbytes}
+        for name in ("stream_out", "stream_in"):
+            def run():
+                for i, d in enumerate(dsts):
+                    if name == "stream_out":
+                        kv.kv_stream_out(lay, src, self.A[0], self.A[1], d, start, lens, st[i],
+                                         nbytes, s)
+                    else:
+                        kv.kv_stream_in(dlay, d, caches[i][0], caches[i][1], src, start, lens,
+                                        st[i], nbytes, s)
+            run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(reps):
+                run()
+            e1.record(s)
+            torch.cuda.synchronize()
+            sec = e0.elapsed_time(e1) / 1000 / reps / len(dsts)
+            out[name + "_us_per_piece"] = round(sec * 1e6, 1)
+            out[name + "_hbm_GBps"] = round(2 * nbytes / sec / 1e9, 1)
+            out[name + "_frac_of_peak"] = round(2 * nbytes / sec / 1e9 / HBM_PEAK_GBPS, 4)
+        del caches, st
+        return out
+
 
 class SwapStep:
     """Microbatch swapping on one stage: the 10-layer BLOOM-176B slice, 16 rows
@@ -816,6 +860,8 @@ def main():
             detail["large_slices"] = large_slices(step, kv)
         if isinstance(step, SwapStep):
             detail["microbatch_schedule"] = step.schedule(kv)
+        if isinstance(step, RingStep):
+            detail["repartition_2x2"] = step.repartition(kv)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = (cpu_baseline(step, args.cpu_baseline_seconds) if isinstance(step, StreamStep)

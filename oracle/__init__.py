@@ -21,7 +21,8 @@ over a layer range into host memory, ``swap_in`` the matching unpack,
 ``ring_host`` / ``ring_restore`` the staging-ring image and its restore,
 ``prompt_ranges`` the per-row ranges of a prompt-layer pack, ``stream_out`` /
 ``stream_in`` the piece of one worker's partition that another holds and its
-merge (Table 1, Fast prompt KV transfer), ``restart_point``
+merge (Table 1, Fast prompt KV transfer), ``pack_paged`` / ``unpack_paged`` the
+same packed format gathered from a block-table pool, ``restart_point``
 the (microbatch, step) a pipeline resumes from after a failure (Failure
 detection and recovery, Fig 10).
 """
@@ -78,6 +79,14 @@ def load(path: str = _LIB):
     lib.oracle_swap_pays.restype = ctypes.c_int
     lib.oracle_swap_pays.argtypes = [_i64, ctypes.c_double, _i64, _i64, ctypes.c_double,
                                      ctypes.c_double, _p, _p]
+    lib.oracle_paged_key_offset.restype = _i64
+    lib.oracle_paged_key_offset.argtypes = [_i64] * 9
+    lib.oracle_paged_value_offset.restype = _i64
+    lib.oracle_paged_value_offset.argtypes = [_i64] * 9
+    lib.oracle_pack_paged.restype = None
+    lib.oracle_pack_paged.argtypes = [_i64] * 4 + [_p, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _p]
+    lib.oracle_unpack_paged.restype = None
+    lib.oracle_unpack_paged.argtypes = [_i64] * 4 + [_p, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _p]
     lib.oracle_stream_elems.restype = _i64
     lib.oracle_stream_elems.argtypes = [_p, _p, _i64, _p]
     lib.oracle_stream_out.restype = None
@@ -259,3 +268,56 @@ def stream_in(dst, src, D: int, Smax: int, key, value, start, count, piece, lib=
         raise ValueError(f"piece holds {piece.size} elements, {need} needed")
     lib.oracle_stream_in(D, Smax, _ptr(d), _ptr(s), _ptr(key), _ptr(value), _ptr(st), _ptr(ct),
                          _ptr(piece))
+
+
+# ---- paged pool: dims are (L, NB, H, D, P) = layers, physical blocks, heads,
+# head dim, tokens per block
+
+def paged_key_offset(pdims, l, blk, h, o, d, lib=None) -> int:
+    L, NB, H, D, P = pdims
+    return (lib or load()).oracle_paged_key_offset(NB, H, D, P, l, blk, h, o, d)
+
+
+def paged_value_offset(pdims, l, blk, h, o, d, lib=None) -> int:
+    L, NB, H, D, P = pdims
+    return (lib or load()).oracle_paged_value_offset(NB, H, D, P, l, blk, h, o, d)
+
+
+def _table(table, B):
+    t = np.ascontiguousarray(np.asarray(table, dtype=np.int32))
+    if t.ndim != 2 or t.shape[0] != B:
+        raise ValueError(f"block table must be [B={B}, stride]")
+    return t
+
+
+def pack_paged(pdims, key, value, layer_begin, layer_count, table, start, count, lib=None):
+    """Gather rows' token ranges from a paged pool into the packed format."""
+    lib = lib or load()
+    L, NB, H, D, P = pdims
+    key, value = _u16(key, "key"), _u16(value, "value")
+    st = np.ascontiguousarray(np.asarray(start, dtype=np.int32).reshape(-1))
+    B = st.size
+    ct = _rows(count, B)
+    tb = _table(table, B)
+    out = np.empty(2 * layer_count * H * D * int(ct.sum()), dtype=np.uint16)
+    lib.oracle_pack_paged(NB, H, D, P, _ptr(key), _ptr(value), layer_begin, layer_count, B,
+                          _ptr(tb), tb.shape[1], _ptr(st), _ptr(ct), _ptr(out))
+    return out
+
+
+def unpack_paged(pdims, key, value, layer_begin, layer_count, table, start, count, packed,
+                 lib=None) -> None:
+    """Scatter ``packed`` into the pool in place (inverse of :func:`pack_paged`)."""
+    lib = lib or load()
+    L, NB, H, D, P = pdims
+    key, value = _u16(key, "key"), _u16(value, "value")
+    st = np.ascontiguousarray(np.asarray(start, dtype=np.int32).reshape(-1))
+    B = st.size
+    ct = _rows(count, B)
+    tb = _table(table, B)
+    packed = _u16(np.ascontiguousarray(packed), "packed")
+    need = 2 * layer_count * H * D * int(ct.sum())
+    if packed.size < need:
+        raise ValueError(f"packed holds {packed.size} elements, {need} needed")
+    lib.oracle_unpack_paged(NB, H, D, P, _ptr(key), _ptr(value), layer_begin, layer_count, B,
+                            _ptr(tb), tb.shape[1], _ptr(st), _ptr(ct), _ptr(packed))

@@ -49,6 +49,12 @@
  *    Fig 10): a (microbatch, step) pair counts as replicated once every worker
  *    has acknowledged it; steps run in (step, microbatch) order; the pipeline
  *    restarts at the first pair in that order that is not replicated.
+ *  - Paged pool (vLLM's paging and Mooncake's chunks are named in the pages;
+ *    neither layout is given): the contiguous layouts with (row, Smax)
+ *    replaced by (physical block, block_tokens P) -- key
+ *    [L, NB, H, D/8, P, 8], value [L, NB, H, P, D] -- and a block table per
+ *    row: row b's token s lives in block table[b*stride + s/P] at slot s%P.
+ *    A paged pack writes the same packed format as a contiguous pack.
  *  - stream_out / stream_in (Table 1, Fast prompt KV transfer): a worker's
  *    cache holds one partition of the model's KV -- a global layer range, a
  *    global head range and a global request (row) range, stored at local
@@ -300,4 +306,73 @@ void oracle_stream_in(int64_t D, int64_t Smax, const int64_t *dst, const int64_t
                             ++o;
                         }
                 }
+}
+
+/* ---- paged pool ----------------------------------------------------------- */
+
+/* Element offset of K(l, block, h, slot o, d) in the pool [L, NB, H, D/8, P, 8]. */
+int64_t oracle_paged_key_offset(int64_t NB, int64_t H, int64_t D, int64_t P,
+                                int64_t l, int64_t blk, int64_t h, int64_t o, int64_t d)
+{
+    return ((((l * NB + blk) * H + h) * (D / 8) + d / 8) * P + o) * 8 + d % 8;
+}
+
+/* Element offset of V(l, block, h, slot o, d) in the pool [L, NB, H, P, D]. */
+int64_t oracle_paged_value_offset(int64_t NB, int64_t H, int64_t D, int64_t P,
+                                  int64_t l, int64_t blk, int64_t h, int64_t o, int64_t d)
+{
+    return (((l * NB + blk) * H + h) * P + o) * D + d;
+}
+
+/* Gather from the pool: the packed format of oracle_pack, for rows whose
+ * tokens are found through their block tables. */
+void oracle_pack_paged(int64_t NB, int64_t H, int64_t D, int64_t P,
+                       const uint16_t *key, const uint16_t *value,
+                       int64_t layer_begin, int64_t layer_count, int64_t B,
+                       const int32_t *table, int64_t stride,
+                       const int32_t *start, const int32_t *count, uint16_t *out)
+{
+    int64_t o = 0;
+    for (int64_t l = layer_begin; l < layer_begin + layer_count; ++l)
+        for (int kv = 0; kv < 2; ++kv)
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t h = 0; h < H; ++h)
+                    for (int64_t t = 0; t < count[b]; ++t) {
+                        const int64_t s = start[b] + t;
+                        const int64_t blk = table[b * stride + s / P];
+                        const int64_t slot = s % P;
+                        for (int64_t d = 0; d < D; ++d) {
+                            if (kv == 0)
+                                out[o] = key[oracle_paged_key_offset(NB, H, D, P, l, blk, h, slot, d)];
+                            else
+                                out[o] = value[oracle_paged_value_offset(NB, H, D, P, l, blk, h, slot, d)];
+                            ++o;
+                        }
+                    }
+}
+
+/* Scatter into the pool: the inverse of oracle_pack_paged. */
+void oracle_unpack_paged(int64_t NB, int64_t H, int64_t D, int64_t P,
+                         uint16_t *key, uint16_t *value,
+                         int64_t layer_begin, int64_t layer_count, int64_t B,
+                         const int32_t *table, int64_t stride,
+                         const int32_t *start, const int32_t *count, const uint16_t *in)
+{
+    int64_t o = 0;
+    for (int64_t l = layer_begin; l < layer_begin + layer_count; ++l)
+        for (int kv = 0; kv < 2; ++kv)
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t h = 0; h < H; ++h)
+                    for (int64_t t = 0; t < count[b]; ++t) {
+                        const int64_t s = start[b] + t;
+                        const int64_t blk = table[b * stride + s / P];
+                        const int64_t slot = s % P;
+                        for (int64_t d = 0; d < D; ++d) {
+                            if (kv == 0)
+                                key[oracle_paged_key_offset(NB, H, D, P, l, blk, h, slot, d)] = in[o];
+                            else
+                                value[oracle_paged_value_offset(NB, H, D, P, l, blk, h, slot, d)] = in[o];
+                            ++o;
+                        }
+                    }
 }

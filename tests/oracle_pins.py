@@ -30,7 +30,12 @@ The pins:
   order; a partition sent to itself, or split by layers or rows only, equals
   the already-pinned pack; a split into a grid of destinations followed by
   the merge back reproduces the source (numpy slices of the logical
-  [l, b, h, s, d] views), and the pieces' sizes add up to the whole.
+  [l, b, h, s, d] views), and the pieces' sizes add up to the whole;
+* paged pool: the offsets equal numpy's index of arrays shaped like the pool
+  layouts; a pool with one block of Smax tokens per row and the identity
+  table is the contiguous cache (pack/unpack equal the pinned ones); a random
+  pool and block tables assembled into contiguous caches with numpy fancy
+  indexing pack to the same words; unpack restores exactly the selected slots.
 """
 from __future__ import annotations
 
@@ -357,6 +362,73 @@ def check_stream(lib):
     assert np.array_equal(back_v[mv], V5[mv]) and not back_v[~mv].any(), "split + merge lost V"
 
 
+def check_paged(lib):
+    # offsets: numpy's C-order index of the pool layouts
+    pd = (2, 3, 2, 16, 4)
+    L, NB, H, D, P = pd
+    for l, blk, h, o, d in itertools.product(range(L), range(NB), range(H), range(P), range(D)):
+        assert oracle.paged_key_offset(pd, l, blk, h, o, d, lib=lib) == \
+            np.ravel_multi_index((l, blk, h, d // 8, o, d % 8), (L, NB, H, D // 8, P, 8))
+        assert oracle.paged_value_offset(pd, l, blk, h, o, d, lib=lib) == \
+            np.ravel_multi_index((l, blk, h, o, d), (L, NB, H, P, D))
+    rng = np.random.default_rng(17)
+    # identity: one block of Smax tokens per row is the contiguous cache
+    dims = (3, 4, 2, 24, 9)
+    L, B, H, D, S = dims
+    K = rng.integers(0, 1 << 16, size=L * B * H * D * S, dtype=np.uint32).astype(np.uint16)
+    V = rng.integers(0, 1 << 16, size=K.size, dtype=np.uint32).astype(np.uint16)
+    ident = np.arange(B, dtype=np.int32).reshape(B, 1)
+    for seed in range(8):
+        r = np.random.default_rng(seed)
+        st = r.integers(0, S, size=B).astype(np.int32)
+        ct = np.array([int(r.integers(0, S - x + 1)) for x in st], np.int32)
+        l0 = int(r.integers(0, L))
+        nl = int(r.integers(0, L - l0 + 1))
+        got = oracle.pack_paged((L, B, H, D, S), K, V, l0, nl, ident, st, ct, lib=lib)
+        assert np.array_equal(got, oracle.pack(dims, K, V, l0, nl, st, ct, lib=lib)), "identity pool"
+        k2, v2 = np.zeros_like(K), np.zeros_like(V)
+        oracle.unpack_paged((L, B, H, D, S), k2, v2, l0, nl, ident, st, ct, got, lib=lib)
+        k3, v3 = np.zeros_like(K), np.zeros_like(V)
+        oracle.unpack(dims, k3, v3, l0, nl, st, ct, got, lib=lib)
+        assert np.array_equal(k2, k3) and np.array_equal(v2, v3), "identity pool unpack"
+    # random pool and tables, assembled into contiguous caches by numpy
+    L, NB, H, D, P, B, stride = 2, 17, 3, 16, 4, 3, 5
+    Kp = rng.integers(0, 1 << 16, size=(L, NB, H, D // 8, P, 8), dtype=np.uint32).astype(np.uint16)
+    Vp = rng.integers(0, 1 << 16, size=(L, NB, H, P, D), dtype=np.uint32).astype(np.uint16)
+    S = stride * P
+    for seed in range(6):
+        r = np.random.default_rng(50 + seed)
+        table = r.integers(0, NB, size=(B, stride)).astype(np.int32)   # blocks may be shared
+        sidx = np.arange(S)
+        blk = table[:, sidx // P]                                       # [B, S]
+        Kc = Kp[:, blk, :, :, sidx % P, :]        # [B, S, L, H, C, 8] after advanced indexing
+        Kc = np.ascontiguousarray(Kc.transpose(2, 0, 3, 4, 1, 5))       # [L, B, H, C, S, 8]
+        Vc = Vp[:, blk, :, sidx % P, :]           # [B, S, L, H, D]
+        Vc = np.ascontiguousarray(Vc.transpose(2, 0, 3, 1, 4))          # [L, B, H, S, D]
+        st = r.integers(0, S, size=B).astype(np.int32)
+        ct = np.array([int(r.integers(0, S - x + 1)) for x in st], np.int32)
+        got = oracle.pack_paged((L, NB, H, D, P), Kp.ravel(), Vp.ravel(), 0, L, table, st, ct, lib=lib)
+        want = oracle.pack((L, B, H, D, S), Kc.ravel(), Vc.ravel(), 0, L, st, ct, lib=lib)
+        assert np.array_equal(got, want), "paged pack != contiguous pack of the assembled cache"
+    # round trip with distinct blocks: exactly the selected slots come back
+    table = rng.permutation(NB)[:B * stride].reshape(B, stride).astype(np.int32)
+    st = np.array([1, 0, 7], np.int32)
+    ct = np.array([17, 0, 9], np.int32)
+    packed = oracle.pack_paged((L, NB, H, D, P), Kp.ravel(), Vp.ravel(), 0, L, table, st, ct, lib=lib)
+    k2 = np.full(Kp.shape, 0xD00D, np.uint16)
+    v2 = np.full(Vp.shape, 0xD00D, np.uint16)
+    oracle.unpack_paged((L, NB, H, D, P), k2.reshape(-1), v2.reshape(-1), 0, L, table, st, ct,
+                        packed, lib=lib)
+    mk = np.zeros(Kp.shape, bool)
+    mv = np.zeros(Vp.shape, bool)
+    for b in range(B):
+        for s_ in range(st[b], st[b] + ct[b]):
+            mk[:, table[b, s_ // P], :, :, s_ % P, :] = True
+            mv[:, table[b, s_ // P], :, s_ % P, :] = True
+    assert np.array_equal(k2[mk], Kp[mk]) and np.all(k2[~mk] == 0xD00D), "paged round trip K"
+    assert np.array_equal(v2[mv], Vp[mv]) and np.all(v2[~mv] == 0xD00D), "paged round trip V"
+
+
 def run_all(lib):
     check_offsets(lib)
     check_brute_force(lib)
@@ -367,6 +439,7 @@ def run_all(lib):
     check_restart_point(lib)
     check_swap_pays(lib)
     check_stream(lib)
+    check_paged(lib)
 
 
 if __name__ == "__main__":          # used by the mutant test: exit 0 iff every pin holds

@@ -57,6 +57,10 @@ def test_stream_split_and_merge(lib):
     oracle_pins.check_stream(lib)
 
 
+def test_paged_pool(lib):
+    oracle_pins.check_paged(lib)
+
+
 def test_swap_pays_closed_forms(lib):
     oracle_pins.check_swap_pays(lib)
 
@@ -123,6 +127,16 @@ MUTANTS = {
     "stream_out_heads_before_rows": ("            for (int64_t gr = r_lo; gr < r_hi; ++gr)\n                for (int64_t gh = h_lo; gh < h_hi; ++gh) {\n                    const int64_t l = gl - src[0]",
                                      "            for (int64_t gh = h_lo; gh < h_hi; ++gh)\n                for (int64_t gr = r_lo; gr < r_hi; ++gr) {\n                    const int64_t l = gl - src[0]"),
     "stream_size_counts_destination_rows": ("tokens += count[r - src[4]];", "tokens += count[r - dst[4]];"),
+    "paged_block_and_slot_swapped": ("const int64_t blk = table[b * stride + s / P];\n                        const int64_t slot = s % P;\n                        for (int64_t d = 0; d < D; ++d) {\n                            if (kv == 0)\n                                out",
+                                     "const int64_t blk = table[b * stride + s % P];\n                        const int64_t slot = s / P;\n                        for (int64_t d = 0; d < D; ++d) {\n                            if (kv == 0)\n                                out"),
+    "paged_table_stride_ignored": ("const int64_t blk = table[b * stride + s / P];\n                        const int64_t slot = s % P;\n                        for (int64_t d = 0; d < D; ++d) {\n                            if (kv == 0)\n                                out",
+                                   "const int64_t blk = table[b + s / P];\n                        const int64_t slot = s % P;\n                        for (int64_t d = 0; d < D; ++d) {\n                            if (kv == 0)\n                                out"),
+    "paged_key_layout_transposed": ("* (D / 8) + d / 8) * P + o) * 8 + d % 8;",
+                                    "* P + o) * (D / 8) + d / 8) * 8 + d % 8;"),
+    "paged_value_block_term_dropped": ("return (((l * NB + blk) * H + h) * P + o) * D + d;",
+                                       "return (((l * NB + 0) * H + h) * P + o) * D + d;"),
+    "unpack_paged_slot_from_t": ("const int64_t slot = s % P;\n                        for (int64_t d = 0; d < D; ++d) {\n                            if (kv == 0)\n                                key",
+                                 "const int64_t slot = t % P;\n                        for (int64_t d = 0; d < D; ++d) {\n                            if (kv == 0)\n                                key"),
     "ring_order_reversed": ("for (int64_t j = 0; j < steps; ++j)\n        oracle_unpack(L, B, H, D, Smax, key, value, 0, L, pos + j * B",
                             "for (int64_t j = steps - 1; j >= 0; --j)\n        oracle_unpack(L, B, H, D, Smax, key, value, 0, L, pos + j * B"),
 }
