@@ -155,6 +155,65 @@ int kv_unpack_prompt_layer(const kv_layout *lay, void *k, void *v,
                            hipStream_t s);
 
 /* ---------------------------------------------------------------------------
+ * Paged pools.  The pages name vLLM's paged KV memory and Mooncake's
+ * chunk-organised KV ([DV, Related work]; [PD], KV Cache Pool) without giving
+ * a layout; the one taken here is the contiguous layout with (row, Smax)
+ * replaced by (physical block, block_tokens P): key
+ * [L, blocks, H, D/8, P, 8], value [L, blocks, H, P, D].  A row's tokens
+ * live in the blocks its table names: token s of row b is slot s % P of
+ * block table[b * table_stride + s / P].  Packing from a pool writes the same
+ * packed format as kv_pack_tokens, so everything downstream (rings, swap,
+ * streaming) is shared.
+ */
+typedef struct kv_paged {
+    int32_t L, blocks, H, D, block_tokens, dtype;
+    int32_t elem_bytes;        /* P = 2 */
+    int32_t vec_elems;         /* 8 elements per 16-byte key vector */
+    int64_t k_strides[6];      /* element strides of K [L,blocks,H,D/8,block_tokens,8] */
+    int64_t v_strides[5];      /* element strides of V [L,blocks,H,block_tokens,D] */
+    int64_t k_bytes, v_bytes;
+    uint32_t magic;
+    uint32_t reserved;
+} kv_paged;
+
+/* Pool descriptor.  Requires all dims > 0, D % 8 == 0, D <= KV_MAX_HEAD_DIM,
+ * dtype a kv_dtype, byte sizes that fit int64 and block_tokens * D/8 below
+ * 2^31 (else KV_EINVAL).  Pure host call. */
+int kv_paged_init(kv_paged *out, int32_t L, int32_t blocks, int32_t H, int32_t D,
+                  int32_t block_tokens, int32_t dtype);
+
+/* Bytes a pack of B rows over `layer_count` layers moves:
+ * 2 * layer_count * H * D * P * sum_b count_b (count NULL: one per row). */
+int64_t kv_paged_pack_bytes(const kv_paged *pg, int32_t layer_count, int32_t B,
+                            const int32_t *count);
+
+/* Gather from a pool: rows b < B (B <= KV_MAX_ROWS), tokens
+ * [start_b, start_b + count_b) (count NULL: one per row), layers
+ * [layer_begin, layer_begin + layer_count), into `staging` in the packed
+ * format of kv_pack_tokens.  `table`: device memory, int32[B * table_stride],
+ * caller-owned.  Requires start_b + count_b <= table_stride * block_tokens
+ * (else KV_ERANGE) and the usual buffer checks.  Block ids are read on the
+ * GPU: a token whose id lies outside [0, blocks) is skipped (its packed
+ * words are not written); kv_paged_check_table validates a host copy. */
+int kv_pack_paged(const kv_paged *pg, const void *k, const void *v, int32_t layer_begin,
+                  int32_t layer_count, int32_t B, const int32_t *table, int32_t table_stride,
+                  const int32_t *start, const int32_t *count, void *staging,
+                  int64_t staging_bytes, hipStream_t s);
+
+/* Scatter into a pool: the inverse of kv_pack_paged; writes exactly the
+ * selected slots (tokens of skipped blocks are not written).  The selected
+ * tokens must map to distinct slots. */
+int kv_unpack_paged(const kv_paged *pg, void *k, void *v, int32_t layer_begin,
+                    int32_t layer_count, int32_t B, const int32_t *table, int32_t table_stride,
+                    const int32_t *start, const int32_t *count, const void *staging,
+                    int64_t staging_bytes, hipStream_t s);
+
+/* Host check of a block table (host memory, same shape): KV_ERANGE if a
+ * selected token's block id lies outside [0, blocks), else KV_OK. */
+int kv_paged_check_table(const kv_paged *pg, int32_t B, const int32_t *table,
+                         int32_t table_stride, const int32_t *start, const int32_t *count);
+
+/* ---------------------------------------------------------------------------
  * stream_out / stream_in between partitions ([DV, DejaVuLib primitives,
  * Table 1]; Fast prompt KV transfer): the source and destination workers may
  * split the model differently (pipeline depth: layer ranges; tensor

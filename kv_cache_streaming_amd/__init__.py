@@ -59,6 +59,15 @@ class kv_chunk(ctypes.Structure):
                 ("bank_off", ctypes.c_int64 * 2), ("bytes", ctypes.c_int64 * 2)]
 
 
+class kv_paged(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int32), ("blocks", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("block_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("elem_bytes", ctypes.c_int32), ("vec_elems", ctypes.c_int32),
+                ("k_strides", ctypes.c_int64 * 6), ("v_strides", ctypes.c_int64 * 5),
+                ("k_bytes", ctypes.c_int64), ("v_bytes", ctypes.c_int64),
+                ("magic", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
 class kv_part(ctypes.Structure):
     """A worker's partition: global layer, head and request (row) ranges."""
     _fields_ = [("layer0", ctypes.c_int32), ("layers", ctypes.c_int32),
@@ -76,6 +85,7 @@ _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _LAY = ctypes.POINTER(kv_layout)
 _PART = ctypes.POINTER(kv_part)
+_PG = ctypes.POINTER(kv_paged)
 
 # name -> (restype, argtypes), mirroring include/kvstream.h
 _SIGNATURES = {
@@ -87,6 +97,13 @@ _SIGNATURES = {
     "kv_unpack_tokens": (ctypes.c_int, [_LAY, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P]),
     "kv_pack_prompt_layer": (ctypes.c_int, [_LAY, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P]),
     "kv_unpack_prompt_layer": (ctypes.c_int, [_LAY, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P]),
+    "kv_paged_init": (ctypes.c_int, [_PG, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "kv_paged_pack_bytes": (_I64, [_PG, _I32, _I32, _P]),
+    "kv_pack_paged": (ctypes.c_int, [_PG, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _I64,
+                                     _P]),
+    "kv_unpack_paged": (ctypes.c_int, [_PG, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _I64,
+                                       _P]),
+    "kv_paged_check_table": (ctypes.c_int, [_PG, _I32, _P, _I32, _P, _P]),
     "kv_stream_bytes": (_I64, [_LAY, _PART, _PART, _P]),
     "kv_stream_out": (ctypes.c_int, [_LAY, _PART, _P, _P, _PART, _P, _P, _P, _I64, _P]),
     "kv_stream_in": (ctypes.c_int, [_LAY, _PART, _P, _P, _PART, _P, _P, _P, _I64, _P]),
@@ -278,6 +295,65 @@ def kv_swap_plan(lay, layer_begin, layer_count, start, count, bank_bytes):
                         row_begin=c.row_begin, row_end=c.row_end, staged_bytes=c.staged_bytes,
                         pieces=[(c.host_off[p], c.bank_off[p], c.bytes[p]) for p in range(c.pieces)]))
     return out
+
+
+# ---------------------------------------------------------------- paged pools
+
+def kv_paged_init(L: int, blocks: int, H: int, D: int, block_tokens: int,
+                  dtype: int = KV_F16) -> kv_paged:
+    pg = kv_paged()
+    _check(_lib.kv_paged_init(ctypes.byref(pg), L, blocks, H, D, block_tokens, dtype),
+           "kv_paged_init")
+    return pg
+
+
+def _b_rows(start):
+    a = np.ascontiguousarray(np.asarray(start, dtype=np.int32).reshape(-1))
+    return a, a.size
+
+
+def kv_paged_pack_bytes(pg, layer_count: int, B: int, count=None) -> int:
+    ct = _Rows(count, B, "count")
+    return _check(_lib.kv_paged_pack_bytes(ctypes.byref(pg), layer_count, B, ct.ptr),
+                  "kv_paged_pack_bytes")
+
+
+def _table_stride(table, table_stride):
+    if table_stride is not None:
+        return table_stride
+    if hasattr(table, "shape") and len(table.shape) == 2:
+        return int(table.shape[1])
+    raise ValueError("pass table_stride for a flat block table")
+
+
+def kv_pack_paged(pg, k, v, layer_begin, layer_count, table, start, count, staging,
+                  staging_bytes=None, stream=None, table_stride=None) -> None:
+    st, B = _b_rows(start)
+    ct = _Rows(count, B, "count")
+    nb = _nbytes(staging) if staging_bytes is None else staging_bytes
+    _check(_lib.kv_pack_paged(ctypes.byref(pg), _addr(k), _addr(v), layer_begin, layer_count, B,
+                              _addr(table), _table_stride(table, table_stride), st.ctypes.data,
+                              ct.ptr, _addr(staging), nb, _stream(stream)), "kv_pack_paged")
+
+
+def kv_unpack_paged(pg, k, v, layer_begin, layer_count, table, start, count, staging,
+                    staging_bytes=None, stream=None, table_stride=None) -> None:
+    st, B = _b_rows(start)
+    ct = _Rows(count, B, "count")
+    nb = _nbytes(staging) if staging_bytes is None else staging_bytes
+    _check(_lib.kv_unpack_paged(ctypes.byref(pg), _addr(k), _addr(v), layer_begin, layer_count,
+                                B, _addr(table), _table_stride(table, table_stride),
+                                st.ctypes.data, ct.ptr, _addr(staging), nb, _stream(stream)),
+           "kv_unpack_paged")
+
+
+def kv_paged_check_table(pg, table, start, count=None) -> None:
+    """Host validation of a block table (numpy int32 [B, stride])."""
+    t = np.ascontiguousarray(np.asarray(table, dtype=np.int32))
+    st, B = _b_rows(start)
+    ct = _Rows(count, B, "count")
+    _check(_lib.kv_paged_check_table(ctypes.byref(pg), B, t.ctypes.data, t.shape[1],
+                                     st.ctypes.data, ct.ptr), "kv_paged_check_table")
 
 
 # ---------------------------------------------------------------- partitions

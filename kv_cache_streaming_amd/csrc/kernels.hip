@@ -205,6 +205,221 @@ __global__ __launch_bounds__(kThreads) void copy_tiles(Geometry g, RowTable rt)
     }
 }
 
+// ---- paged pool --------------------------------------------------------------
+// Token s of a row -> (index of its block in the row's table, slot in the block).
+__device__ __forceinline__ void paged_split(const PagedGeometry &g, uint32_t s, uint32_t &q,
+                                            uint32_t &slot)
+{
+    if (g.p_shift >= 0) {
+        q = s >> g.p_shift;
+        slot = s & (uint32_t)(g.P - 1);
+    } else {
+        q = s / (uint32_t)g.P;
+        slot = s - q * (uint32_t)g.P;
+    }
+}
+
+// Decode-sized ranges on a pool: one thread per (layer, row, head, vector c),
+// as copy_rows_small, with each token's block looked up in the row's table.
+template <bool kPack>
+__global__ __launch_bounds__(kThreads) void copy_paged_small(PagedGeometry g, RowTable rt)
+{
+    const uint32_t gid = blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t C = (uint32_t)g.C;
+    uint32_t r = gid / C;
+    const uint32_t c = gid - r * C;
+    const uint32_t h = r % (uint32_t)g.H;
+    r /= (uint32_t)g.H;
+    const uint32_t b = r % (uint32_t)g.B;
+    r /= (uint32_t)g.B;
+    if (r >= (uint32_t)g.nl)
+        return;
+    const int32_t li = (int32_t)r;
+    const int32_t off = rt.off[b];
+    const int32_t cnt = rt.off[b + 1] - off;
+    const int32_t s0 = rt.start[b];
+    const int64_t layer = g.l0 + li;
+    const int32_t *trow = g.table + (int64_t)b * g.table_stride;
+    const int64_t blk = (int64_t)g.H * g.T * C;
+    uint4 *ks = g.stage + 2 * (int64_t)li * blk + ((int64_t)g.H * off + (int64_t)h * cnt) * C + c;
+    uint4 *vs = ks + blk;
+    for (int32_t t = 0; t < cnt; ++t) {
+        uint32_t q, slot;
+        paged_split(g, (uint32_t)(s0 + t), q, slot);
+        const int32_t id = trow[q];
+        if (id < 0 || id >= g.NB)
+            continue;
+        const int64_t unit = (layer * g.NB + id) * g.H + h;
+        uint4 *kc = g.k + (unit * C + c) * g.P + slot;
+        uint4 *vc = g.v + (unit * g.P + slot) * C + c;
+        if (kPack) {
+            const uint4 a = *kc, d = *vc;
+            ks[t * C] = a;
+            vs[t * C] = d;
+        } else {
+            const uint4 a = ks[t * C], d = vs[t * C];
+            *kc = a;
+            *vc = d;
+        }
+    }
+}
+
+// Many tokens per row on a pool: the tile scheme of copy_tiles (K loaded
+// chunk-major, transposed through LDS, stored token-major), with the tile's
+// block ids staged in LDS first.  Within a block a key chunk row is P*16
+// contiguous bytes, so chunk-major loads stay contiguous per block.
+template <int CT, int PER, bool kPack>
+__global__ __launch_bounds__(kThreads) void copy_paged_tiles(PagedGeometry g, RowTable rt)
+{
+    constexpr int TV = kThreads * PER;
+    __shared__ u32x4 lds[TV];
+    __shared__ int32_t ids[TV + 1];       // blocks touched by the tile (at most its tokens + 1)
+    const int32_t C = CT ? CT : g.C;
+    const int32_t TT = CT ? TV / CT : g.tile_tokens;
+
+    int32_t bid = blockIdx.x;
+    const int32_t tile = bid % g.tiles_per_row;
+    bid /= g.tiles_per_row;
+    const int32_t h = bid % g.H;
+    bid /= g.H;
+    const int32_t b = bid % g.B;
+    const int32_t li = bid / g.B;
+
+    const int32_t off = rt.off[b];
+    const int32_t cnt = rt.off[b + 1] - off;
+    const int32_t t0 = tile * TT;
+    if (t0 >= cnt)
+        return;
+    const int32_t nt = min(TT, cnt - t0);
+    const int32_t nvec = nt * C;
+    const uint32_t s0 = (uint32_t)(rt.start[b] + t0);
+    uint32_t q0, o0, q1, o1;
+    paged_split(g, s0, q0, o0);
+    paged_split(g, s0 + (uint32_t)nt - 1u, q1, o1);
+    const int32_t nblk = (int32_t)(q1 - q0) + 1;
+    const int32_t *trow = g.table + (int64_t)b * g.table_stride + q0;
+    const int tid = threadIdx.x;
+    for (int j = tid; j < nblk; j += kThreads) {
+        const int32_t id = trow[j];
+        ids[j] = (id >= 0 && id < g.NB) ? id : -1;
+    }
+    __syncthreads();
+
+    const int64_t layer = g.l0 + li;
+    const int64_t CP = (int64_t)C * g.P;          // vectors of one (block, head) unit
+    const int64_t blk = (int64_t)g.H * g.T * C;
+    u32x4 *ks = (u32x4 *)(g.stage + 2 * (int64_t)li * blk +
+                          ((int64_t)g.H * off + (int64_t)h * cnt + t0) * C);
+    u32x4 *vs = ks + blk;
+    const u32x4 *kpool = (const u32x4 *)g.k;
+    const u32x4 *vpool = (const u32x4 *)g.v;
+    // unit base (in vectors) of tile token i, or -1 for a skipped block
+    auto unit_of = [&](int32_t i, uint32_t &slot) -> int64_t {
+        uint32_t q;
+        paged_split(g, o0 + (uint32_t)i, q, slot);
+        const int32_t id = ids[q];
+        return id < 0 ? -1 : ((layer * g.NB + id) * g.H + h) * CP;
+    };
+    u32x4 kr[PER], vr[PER];
+
+    if (kPack) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + p * kThreads, c = e / TT, i = e % TT;
+            if (c < C && i < nt) {
+                uint32_t slot;
+                const int64_t u = unit_of(i, slot);
+                if (u >= 0)
+                    kr[p] = kpool[u + (int64_t)c * g.P + slot];
+            }
+            if (e < nvec) {
+                uint32_t slot;
+                const int64_t u = unit_of(e / C, slot);
+                if (u >= 0)
+                    vr[p] = vpool[u + (int64_t)slot * C + e % C];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + p * kThreads, c = e / TT, i = e % TT;
+            if (c < C && i < nt)
+                lds[lds_slot<CT>(i, c, C)] = kr[p];
+            if (e < nvec) {
+                uint32_t slot;
+                if (unit_of(e / C, slot) >= 0)
+                    vs[e] = vr[p];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + p * kThreads;
+            if (e < nvec) {
+                uint32_t slot;
+                if (unit_of(e / C, slot) >= 0)
+                    ks[e] = lds[lds_slot<CT>(e / C, e % C, C)];
+            }
+        }
+    } else {
+        u32x4 *kw = (u32x4 *)g.k;
+        u32x4 *vw = (u32x4 *)g.v;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + p * kThreads;
+            if (e < nvec) {
+                kr[p] = ks[e];
+                vr[p] = vs[e];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + p * kThreads;
+            if (e < nvec) {
+                lds[lds_slot<CT>(e / C, e % C, C)] = kr[p];
+                uint32_t slot;
+                const int64_t u = unit_of(e / C, slot);
+                if (u >= 0)
+                    vw[u + (int64_t)slot * C + e % C] = vr[p];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + p * kThreads, c = e / TT, i = e % TT;
+            if (c < C && i < nt) {
+                uint32_t slot;
+                const int64_t u = unit_of(i, slot);
+                if (u >= 0)
+                    kw[u + (int64_t)c * g.P + slot] = lds[lds_slot<CT>(i, c, C)];
+            }
+        }
+    }
+}
+
+template <bool kPack>
+hipError_t launch_paged_tiles(const PagedGeometry &g, const RowTable &rt, int64_t blocks,
+                              hipStream_t s)
+{
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    switch (g.C) {
+    case 1: copy_paged_tiles<1, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 2: copy_paged_tiles<2, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 4: copy_paged_tiles<4, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 8: copy_paged_tiles<8, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 16: copy_paged_tiles<16, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 32: copy_paged_tiles<32, 4, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 64: copy_paged_tiles<64, 4, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 128: copy_paged_tiles<128, 4, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    default:
+        if (g.C <= 16)
+            copy_paged_tiles<0, 2, kPack><<<grid, block, 0, s>>>(g, rt);
+        else
+            copy_paged_tiles<0, 4, kPack><<<grid, block, 0, s>>>(g, rt);
+        break;
+    }
+    return hipGetLastError();
+}
+
 // Vectors per thread of the tile kernel: 512-vector tiles (two per thread)
 // for heads of up to 16 vectors -- more workgroups per launch, which fills
 // the 256 CUs better on the 50-70 MB slices of one layer -- and 1024-vector
@@ -348,6 +563,56 @@ int launch_copy(bool pack, const Geometry &g0, const RowTable &rt, int32_t max_c
         } else {
             const int64_t blocks = (int64_t)gl.nl * per_layer;
             e = pack ? launch_tiles_rt<true>(gl, rt, blocks, s) : launch_tiles_rt<false>(gl, rt, blocks, s);
+        }
+        if (tok)
+            profile_stop(tok, s, name, 2 * payload);
+        if (e != hipSuccess)
+            return hip_fail(e, name);
+    }
+    return KV_OK;
+}
+
+int launch_paged_copy(bool pack, const PagedGeometry &g0, const RowTable &rt, int32_t max_count,
+                      hipStream_t s)
+{
+    if (max_count <= 0 || g0.nl <= 0 || g0.T <= 0)
+        return KV_OK;
+    const bool small = max_count <= kSmallMaxTokens;
+    PagedGeometry g = g0;
+    int64_t per_layer;
+    if (small) {
+        per_layer = ((int64_t)g.B * g.H * g.C + kThreads - 1) / kThreads;
+    } else {
+        g.tile_tokens = tile_tokens_for(g.C);
+        g.tiles_per_row = (max_count + g.tile_tokens - 1) / g.tile_tokens;
+        per_layer = (int64_t)g.B * g.H * g.tiles_per_row;
+    }
+    const int64_t max_blocks = small ? 0x7fffffffLL / kThreads : 0x7fffffffLL;
+    const int32_t layers_per_launch =
+        (int32_t)std::max<int64_t>(1, std::min<int64_t>(g.nl, max_blocks / per_layer));
+    const char *name = small ? (pack ? "pack_paged_small" : "unpack_paged_small")
+                             : (pack ? "pack_paged_tiles" : "unpack_paged_tiles");
+    const int64_t blk = (int64_t)g.H * g.T * g.C;
+    for (int32_t done = 0; done < g0.nl; done += layers_per_launch) {
+        PagedGeometry gl = g;
+        gl.l0 = g0.l0 + done;
+        gl.nl = std::min<int32_t>(layers_per_launch, g0.nl - done);
+        gl.stage = g0.stage + 2 * (int64_t)done * blk;
+        const int64_t payload = 2 * (int64_t)gl.nl * blk * 16;
+        void *tok = profiling_enabled() ? profile_start(s) : nullptr;
+        hipError_t e;
+        if (small) {
+            const int64_t threads = (int64_t)gl.nl * gl.B * gl.H * gl.C;
+            const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads)), block(kThreads);
+            if (pack)
+                copy_paged_small<true><<<grid, block, 0, s>>>(gl, rt);
+            else
+                copy_paged_small<false><<<grid, block, 0, s>>>(gl, rt);
+            e = hipGetLastError();
+        } else {
+            const int64_t blocks = (int64_t)gl.nl * per_layer;
+            e = pack ? launch_paged_tiles<true>(gl, rt, blocks, s)
+                     : launch_paged_tiles<false>(gl, rt, blocks, s);
         }
         if (tok)
             profile_stop(tok, s, name, 2 * payload);

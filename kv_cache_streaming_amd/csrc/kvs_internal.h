@@ -32,6 +32,22 @@ struct Geometry {
     int64_t T;              // sum of counts
 };
 
+// Geometry of one launch on a paged pool: key [L, NB, H, D/8, P, 8], value
+// [L, NB, H, P, D]; row b's token s is in block table[b*table_stride + s/P]
+// at slot s%P.  Block ids outside [0, NB) are skipped by the kernels.
+struct PagedGeometry {
+    uint4 *k;
+    uint4 *v;
+    uint4 *stage;
+    const int32_t *table;   // device memory, int32[B * table_stride]
+    int32_t table_stride;
+    int32_t NB, H, C, P;    // physical blocks, heads, D/8, tokens per block
+    int32_t p_shift;        // log2(P) when P is a power of two, else -1
+    int32_t B, l0, nl;
+    int32_t tiles_per_row, tile_tokens;
+    int64_t T;              // sum of counts
+};
+
 // ---- errors (api.hip) ----
 int set_error(int status, const char *fmt, ...);
 int hip_fail(hipError_t e, const char *what);
@@ -63,6 +79,10 @@ int enqueue_copy(bool pack, const kv_layout &lay, const void *k, const void *v, 
 // Launches the pack (or unpack) kernels for one call; returns KV_OK or KV_EHIP.
 int launch_copy(bool pack, const Geometry &g, const RowTable &rt, int32_t max_count,
                 hipStream_t s);
+
+// Paged counterpart of launch_copy.
+int launch_paged_copy(bool pack, const PagedGeometry &g, const RowTable &rt, int32_t max_count,
+                      hipStream_t s);
 
 // Copies `bytes` (a multiple of 16) between a device buffer and pinned host
 // memory with the link-copy kernel.  `dst`/`src` are device-visible
