@@ -664,6 +664,49 @@ def large_slices(step, kv, reps=3):
     return out
 
 
+def paged_slices(step, kv, reps=3):
+    """Isolated rates of the paged pool kernels on the workload's prompt: every
+    layer's 1000 prompt tokens of 8 rows packed from (and unpacked into) a pool
+    of 16-token pages and one of 256-token chunks, the rows' blocks scattered
+    at random over the pool; HBM bytes = read + write of the payload."""
+    import numpy as np
+    torch, w = step.torch, step.w
+    L, B, H, D = w.L, w.B, w.H, w.D
+    count = [w.prompt_len] * B
+    start = [0] * B
+    s = step.s["t"]
+    out = {}
+    for P in (16, 256):
+        stride = -(-w.Smax // P)
+        NB = B * stride
+        pg = kv.kv_paged_init(L, NB, H, D, P, w.dtype)
+        n = L * NB * H * D * P
+        k = torch.empty(n, dtype=torch.int16, device="cuda").fill_(1)
+        v = torch.empty(n, dtype=torch.int16, device="cuda").fill_(2)
+        rng = np.random.default_rng(P)
+        table = torch.from_numpy(rng.permutation(NB).reshape(B, stride).astype(np.int32)).cuda()
+        payload = kv.kv_paged_pack_bytes(pg, L, B, count)
+        st = torch.empty(payload // 2, dtype=torch.int16, device="cuda")
+        row = {"block_tokens": P, "payload_bytes": payload}
+        for name, fn in (("pack", kv.kv_pack_paged), ("unpack", kv.kv_unpack_paged)):
+            fn(pg, k, v, 0, L, table, start, count, st, payload, s)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(reps):
+                fn(pg, k, v, 0, L, table, start, count, st, payload, s)
+            e1.record(s)
+            torch.cuda.synchronize()
+            sec = e0.elapsed_time(e1) / 1000 / reps
+            row[name + "_us"] = round(sec * 1e6, 1)
+            row[name + "_hbm_GBps"] = round(2 * payload / sec / 1e9, 1)
+            row[name + "_frac_of_peak"] = round(2 * payload / sec / 1e9 / HBM_PEAK_GBPS, 4)
+        out[f"pages_{P}"] = row
+        del k, v, st, table
+        torch.cuda.empty_cache()
+    return out
+
+
 def decode_push_us(step, reps=3):
     torch = step.torch
     st = step.s["t"]
@@ -858,6 +901,8 @@ def main():
             detail["decode_push_us"] = round(decode_push_us(step), 2)
             detail["hbm_copy_ceiling_GBps"] = round(hbm_copy_ceiling(torch), 1)
             detail["large_slices"] = large_slices(step, kv)
+            if step.w.B * step.w.Smax >= 4096:
+                detail["paged_slices"] = paged_slices(step, kv)
         if isinstance(step, SwapStep):
             detail["microbatch_schedule"] = step.schedule(kv)
         if isinstance(step, RingStep):
