@@ -372,9 +372,27 @@ int kv_ring_create(kv_ring **out, const kv_layout *lay, int32_t R,
                    void *host, int64_t host_bytes, hipStream_t copy, int32_t transport);
 int kv_ring_destroy(kv_ring *r);
 
-/* One decode step: pos is int32[B], every pos_b in [0, Smax). */
+/* One decode step: pos is int32[B], every pos_b in [0, Smax).  The step is
+ * packed from (k, v) on `compute` at this call, or, in gather-at-flush mode,
+ * when its bank fills or kv_ring_flush runs (see kv_ring_set_gather). */
 int kv_ring_push(kv_ring *r, const void *k, const void *v, const int32_t *pos,
                  hipStream_t compute);
+
+/* When a ring reads the cache.  KV_RING_GATHER_EACH_STEP (the default): every
+ * push packs its step at once.  KV_RING_GATHER_AT_FLUSH: a push only records
+ * the step; the steps of a bank are packed together just before the bank is
+ * copied out (on the compute stream of the push or flush that triggers it),
+ * so the pushed positions must keep their contents until then -- true of a
+ * decode loop, where each step writes a new position.  Steps whose positions
+ * advance by one on every row (and share the caches) are packed in one pass
+ * that reads whole cache lines; a single-step pack reads one 16-byte key
+ * vector per line.  The bytes produced are identical.  Changing the mode
+ * requires every pushed step flushed (else KV_EBUSY). */
+enum kv_ring_gather {
+    KV_RING_GATHER_EACH_STEP = 0,
+    KV_RING_GATHER_AT_FLUSH = 1
+};
+int kv_ring_set_gather(kv_ring *r, int32_t mode);
 
 /* Copy the filled but unflushed slots (a final partial bank) to the host.
  * `done` (nullable) is recorded on the copy stream after every copy so far:
@@ -383,7 +401,8 @@ int kv_ring_flush(kv_ring *r, hipStream_t compute, hipEvent_t done);
 
 /* Restore ([DV, Failure detection and recovery, Fig 10], data leg): copy the
  * host image back through the banks and unpack every step into (k, v) in
- * ascending step order (a later step wins where two name the same position).
+ * ascending step order (a later step wins where two name the same position;
+ * runs of steps whose positions advance by one are unpacked in one pass).
  * Requires every pushed step flushed (else KV_EBUSY).  The copies follow the
  * ring's own flushes on the copy stream.  `done` (nullable) is recorded on
  * `compute` after the last unpack. */

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libkvstream.so")
 KV_OK, KV_EINVAL, KV_ERANGE, KV_ESIZE, KV_EHIP, KV_EBUSY = 0, -1, -2, -3, -4, -5
 KV_F16, KV_BF16 = 0, 1
 KV_XFER_AUTO, KV_XFER_KERNEL, KV_XFER_RUNTIME, KV_XFER_DMA, KV_XFER_DMA_OUT = 0, 1, 2, 3, 4
+KV_RING_GATHER_EACH_STEP, KV_RING_GATHER_AT_FLUSH = 0, 1
 KV_MAX_ROWS = 256
 STATUS_NAMES = {0: "KV_OK", -1: "KV_EINVAL", -2: "KV_ERANGE", -3: "KV_ESIZE",
                 -4: "KV_EHIP", -5: "KV_EBUSY"}
@@ -120,6 +121,7 @@ _SIGNATURES = {
     "kv_ring_flush": (ctypes.c_int, [_P, _P, _P]),
     "kv_ring_restore": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "kv_ring_restore_steps": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P]),
+    "kv_ring_set_gather": (ctypes.c_int, [_P, _I32]),
     "kv_ring_steps": (_I64, [_P]),
     "kv_ring_durable_steps": (_I64, [_P]),
     "kv_mbswap_create": (ctypes.c_int, [ctypes.POINTER(_P), _LAY, _I32, _P, _P, _P, _P, _P, _P, _P,
@@ -505,6 +507,9 @@ class KvRing:
         _check(_lib.kv_ring_restore_steps(self._h, _addr(k), _addr(v), n, _stream(compute),
                                           _event(done)), "kv_ring_restore_steps")
 
+    def set_gather(self, mode: int) -> None:
+        _check(_lib.kv_ring_set_gather(self._h, mode), "kv_ring_set_gather")
+
     @property
     def steps(self) -> int:
         return _check(_lib.kv_ring_steps(self._h), "kv_ring_steps")
@@ -540,6 +545,10 @@ def kv_ring_restore(r: KvRing, *args, **kw) -> None:
 
 def kv_ring_restore_steps(r: KvRing, *args, **kw) -> None:
     r.restore_steps(*args, **kw)
+
+
+def kv_ring_set_gather(r: KvRing, mode: int) -> None:
+    r.set_gather(mode)
 
 
 def kv_ring_steps(r: KvRing) -> int:

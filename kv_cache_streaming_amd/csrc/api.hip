@@ -181,6 +181,37 @@ int enqueue_copy(bool pack, const kv_layout &lay, const void *k, const void *v, 
     return launch_copy(pack, g, rt, max_count, s);
 }
 
+int enqueue_steps(bool pack, const kv_layout &lay, const void *k, const void *v,
+                  const int32_t *pos0, int32_t n, void *stage, int64_t slot_bytes,
+                  hipStream_t s)
+{
+    RowTable rt;
+    for (int32_t b = 0; b < lay.B; ++b) {
+        if (pos0[b] < 0 || (int64_t)pos0[b] + n > lay.Smax)
+            return set_error(KV_ERANGE, "row %d: steps at [%d, +%d) outside [0, %d)", b, pos0[b],
+                             n, lay.Smax);
+        rt.start[b] = pos0[b];
+        rt.off[b] = b;
+    }
+    rt.off[lay.B] = lay.B;
+    Geometry g;
+    g.k = (uint4 *)k;
+    g.v = (uint4 *)v;
+    g.stage = (uint4 *)stage;
+    g.B = lay.B;
+    g.H = lay.H;
+    g.C = lay.D / 8;
+    g.Smax = lay.Smax;
+    g.l0 = 0;
+    g.nl = lay.L;
+    g.h0 = 0;
+    g.nh = lay.H;
+    g.tiles_per_row = 0;
+    g.tile_tokens = 0;
+    g.T = lay.B;
+    return launch_steps(pack, g, rt, n, slot_bytes / 16, s);
+}
+
 int prompt_rows(const kv_layout &lay, int32_t tok_begin, int32_t tok_count,
                 const int32_t *row_len, int32_t *start, int32_t *count)
 {

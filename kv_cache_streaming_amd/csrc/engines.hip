@@ -212,6 +212,9 @@ struct kv_ring {
     std::deque<std::pair<hipEvent_t, int64_t>> landing;
     std::vector<hipEvent_t> spare;   // recycled landing events
     int64_t durable;             // steps known to be in the host image
+    int32_t gather;              // KV_RING_GATHER_EACH_STEP or KV_RING_GATHER_AT_FLUSH
+    // caches of the steps [flushed, steps) not yet gathered (gather at flush)
+    std::vector<std::pair<const void *, const void *>> pend;
     hipEvent_t free_ev(int b) const { return ev[b]; }
     hipEvent_t filled_ev(int b) const { return ev[2 + b]; }
 };
@@ -500,6 +503,7 @@ int kv_ring_create(kv_ring **out, const kv_layout *lay, int32_t R, void *bank0, 
     r->slot_bytes = slot;
     r->steps = r->flushed = 0;
     r->durable = 0;
+    r->gather = KV_RING_GATHER_EACH_STEP;
     r->wait_needed[0] = r->wait_needed[1] = false;
     r->free_valid[0] = r->free_valid[1] = false;
     if ((st = create_events(r->ev, 4))) {
@@ -525,6 +529,72 @@ int kv_ring_destroy(kv_ring *r)
 }
 
 namespace {
+
+// Step j's positions are step j-1's plus one on every row.
+bool follows(const kv_ring *r, int64_t j)
+{
+    const int32_t B = r->lay.B;
+    const int32_t *p = &r->pos[(size_t)j * B];
+    for (int32_t b = 0; b < B; ++b)
+        if (p[b] != p[b - B] + 1)
+            return false;
+    return true;
+}
+
+// Pack (or unpack) steps [j0, j0+n) between caches and their slots at
+// `slots` (step j0's slot first), one pass per run of steps whose positions
+// advance by one per row, else one pack per step.  The caches are (k, v) for
+// every step, or caches[i] for step j0+i when `caches` is given (a run then
+// also needs the same caches).
+int ring_copy_steps(kv_ring *r, bool pack, const void *k, const void *v, int64_t j0, int64_t n,
+                    void *slots, hipStream_t compute,
+                    const std::pair<const void *, const void *> *caches)
+{
+    const kv_layout &lay = r->lay;
+    int st;
+    for (int64_t a = 0; a < n;) {
+        int64_t e = a + 1;
+        while (e < n && (!caches || caches[e] == caches[a]) && follows(r, j0 + e))
+            ++e;
+        const void *ka = caches ? caches[a].first : k;
+        const void *va = caches ? caches[a].second : v;
+        void *slot = (char *)slots + a * r->slot_bytes;
+        const int32_t *p = &r->pos[(size_t)(j0 + a) * lay.B];
+        if (e - a >= 2) {
+            if ((st = enqueue_steps(pack, lay, ka, va, p, (int32_t)(e - a), slot, r->slot_bytes,
+                                    compute)))
+                return st;
+        } else {
+            RowTable rt;
+            int32_t mx;
+            if ((st = build_rows(lay, p, nullptr, &rt, &mx)) ||
+                (st = enqueue_copy(pack, lay, ka, va, 0, lay.L, rt, mx, slot, compute)))
+                return st;
+        }
+        a = e;
+    }
+    return KV_OK;
+}
+
+// Gather the steps pushed since the last flush (gather-at-flush mode).
+int ring_gather(kv_ring *r, hipStream_t compute)
+{
+    if (r->pend.empty())
+        return KV_OK;
+    const int64_t j0 = r->flushed;
+    const int bk = (int)((j0 / r->R) & 1);
+    int st;
+    if (r->wait_needed[bk]) {
+        if ((st = wait(compute, r->free_ev(bk), "ring bank wait")))
+            return st;
+        r->wait_needed[bk] = false;
+    }
+    st = ring_copy_steps(r, true, nullptr, nullptr, j0, (int64_t)r->pend.size(),
+                         (char *)r->bank[bk] + (j0 % r->R) * r->slot_bytes, compute,
+                         r->pend.data());
+    r->pend.clear();
+    return st;
+}
 
 // Copy steps [first, first+n) -- all in one bank -- to the host image.
 int ring_flush_range(kv_ring *r, int64_t first, int64_t n, hipStream_t compute)
@@ -587,19 +657,38 @@ int kv_ring_push(kv_ring *r, const void *k, const void *v, const int32_t *pos,
     if ((st = build_rows(lay, pos, nullptr, &rt, &mx)))
         return st;
     const int64_t j = r->steps;
-    const int bk = (int)((j / r->R) & 1);
-    if (r->wait_needed[bk]) {
-        if ((st = wait(compute, r->free_ev(bk), "ring bank wait")))
+    if (r->gather == KV_RING_GATHER_AT_FLUSH) {
+        r->pend.emplace_back(k, v);
+    } else {
+        const int bk = (int)((j / r->R) & 1);
+        if (r->wait_needed[bk]) {
+            if ((st = wait(compute, r->free_ev(bk), "ring bank wait")))
+                return st;
+            r->wait_needed[bk] = false;
+        }
+        void *slot = (char *)r->bank[bk] + (j % r->R) * r->slot_bytes;
+        if ((st = enqueue_copy(true, lay, k, v, 0, lay.L, rt, mx, slot, compute)))
             return st;
-        r->wait_needed[bk] = false;
     }
-    void *slot = (char *)r->bank[bk] + (j % r->R) * r->slot_bytes;
-    if ((st = enqueue_copy(true, lay, k, v, 0, lay.L, rt, mx, slot, compute)))
-        return st;
     r->pos.insert(r->pos.end(), pos, pos + lay.B);
     r->steps = j + 1;
-    if (r->steps % r->R == 0)
+    if (r->steps % r->R == 0) {
+        if ((st = ring_gather(r, compute)))
+            return st;
         return ring_flush_range(r, r->flushed, r->steps - r->flushed, compute);
+    }
+    return KV_OK;
+}
+
+int kv_ring_set_gather(kv_ring *r, int32_t mode)
+{
+    if (!r)
+        return set_error(KV_EINVAL, "ring handle is NULL");
+    if (mode != KV_RING_GATHER_EACH_STEP && mode != KV_RING_GATHER_AT_FLUSH)
+        return set_error(KV_EINVAL, "gather mode %d is not a kv_ring_gather", mode);
+    if (r->steps != r->flushed)
+        return set_error(KV_EBUSY, "unflushed steps; flush before changing the gather mode");
+    r->gather = mode;
     return KV_OK;
 }
 
@@ -608,6 +697,8 @@ int kv_ring_flush(kv_ring *r, hipStream_t compute, hipEvent_t done)
     if (!r)
         return set_error(KV_EINVAL, "ring handle is NULL");
     int st;
+    if ((st = ring_gather(r, compute)))
+        return st;
     if (r->steps > r->flushed &&
         (st = ring_flush_range(r, r->flushed, r->steps - r->flushed, compute)))
         return st;
@@ -641,15 +732,10 @@ int ring_restore_n(kv_ring *r, void *k, void *v, int64_t n_steps, hipStream_t co
         if ((st = record(r->filled_ev(bk), r->copy, "ring restore loaded")) ||
             (st = wait(compute, r->filled_ev(bk), "ring restore unpack wait")))
             return st;
-        for (int64_t j = j0; j < j0 + n; ++j) {
-            RowTable rt;
-            int32_t mx;
-            if ((st = build_rows(lay, &r->pos[j * lay.B], nullptr, &rt, &mx)))
-                return st;
-            void *slot = (char *)r->bank[bk] + (j - j0) * r->slot_bytes;
-            if ((st = enqueue_copy(false, lay, k, v, 0, lay.L, rt, mx, slot, compute)))
-                return st;
-        }
+        // ascending steps; a run of positions advancing by one holds no
+        // position twice, so one pass per run keeps the later-step-wins order
+        if ((st = ring_copy_steps(r, false, k, v, j0, n, r->bank[bk], compute, nullptr)))
+            return st;
         if ((st = record(r->free_ev(bk), compute, "ring restore unpacked")))
             return st;
         r->wait_needed[bk] = true;
@@ -686,6 +772,7 @@ int kv_ring_restore_steps(kv_ring *r, void *k, void *v, int64_t n, hipStream_t c
     // the ring now continues from step n: later steps are gone
     if (n < r->steps) {
         r->steps = r->flushed = n;
+        r->pend.clear();
         r->pos.resize((size_t)n * r->lay.B);
         r->durable = std::min(r->durable, n);
         std::deque<std::pair<hipEvent_t, int64_t>> keep;
@@ -738,6 +825,7 @@ int kv_ring_reset(kv_ring *r)
         r->spare.push_back(p.first);
     r->landing.clear();
     r->pos.clear();
+    r->pend.clear();
     return KV_OK;
 }
 

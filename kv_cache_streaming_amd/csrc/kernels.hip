@@ -93,6 +93,76 @@ __global__ __launch_bounds__(kThreads) void copy_rows_small(Geometry g, RowTable
     }
 }
 
+// Several decode steps in one pass (a ring bank): step t of every row sits at
+// position start_b + t, and its one-token-per-row packed block is at
+// stage + t * slot_vecs.  One thread per (layer, row, head, key vector c)
+// walks the n positions: its n key vectors are contiguous in the cache, so
+// whole cache lines are read or written, where a single-step pack touches one
+// 16-byte vector per line.
+template <bool kPack>
+__global__ __launch_bounds__(kThreads) void copy_steps(Geometry g, RowTable rt, int32_t n,
+                                                       int64_t slot_vecs)
+{
+    const uint32_t gid = blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t C = (uint32_t)g.C;
+    uint32_t r = gid / C;
+    const uint32_t c = gid - r * C;
+    const uint32_t h = r % (uint32_t)g.H;
+    r /= (uint32_t)g.H;
+    const uint32_t b = r % (uint32_t)g.B;
+    r /= (uint32_t)g.B;
+    if (r >= (uint32_t)g.nl)
+        return;
+    const int32_t li = (int32_t)r;
+    const int32_t s0 = rt.start[b];
+    const int64_t unit = ((int64_t)(g.l0 + li) * g.B + b) * g.H + h;
+    uint4 *kc = g.k + (unit * C + c) * g.Smax + s0;        // step t: kc[t]
+    uint4 *vc = g.v + (unit * g.Smax + s0) * C + c;        // step t: vc[t*C]
+    const int64_t blk = (int64_t)g.H * g.B * C;            // one (layer, K|V) block of a slot
+    uint4 *ks = g.stage + 2 * (int64_t)li * blk + ((int64_t)g.H * b + h) * C + c;
+    uint4 *vs = ks + blk;                                  // step t: ks[t*slot_vecs], vs[...]
+    int32_t t = 0;
+    for (; t + 4 <= n; t += 4) {
+        if (kPack) {
+            const uint4 a0 = kc[t], a1 = kc[t + 1], a2 = kc[t + 2], a3 = kc[t + 3];
+            const uint4 d0 = vc[t * C], d1 = vc[(t + 1) * C], d2 = vc[(t + 2) * C],
+                        d3 = vc[(t + 3) * C];
+            ks[t * slot_vecs] = a0;
+            ks[(t + 1) * slot_vecs] = a1;
+            ks[(t + 2) * slot_vecs] = a2;
+            ks[(t + 3) * slot_vecs] = a3;
+            vs[t * slot_vecs] = d0;
+            vs[(t + 1) * slot_vecs] = d1;
+            vs[(t + 2) * slot_vecs] = d2;
+            vs[(t + 3) * slot_vecs] = d3;
+        } else {
+            const uint4 a0 = ks[t * slot_vecs], a1 = ks[(t + 1) * slot_vecs],
+                        a2 = ks[(t + 2) * slot_vecs], a3 = ks[(t + 3) * slot_vecs];
+            const uint4 d0 = vs[t * slot_vecs], d1 = vs[(t + 1) * slot_vecs],
+                        d2 = vs[(t + 2) * slot_vecs], d3 = vs[(t + 3) * slot_vecs];
+            kc[t] = a0;
+            kc[t + 1] = a1;
+            kc[t + 2] = a2;
+            kc[t + 3] = a3;
+            vc[t * C] = d0;
+            vc[(t + 1) * C] = d1;
+            vc[(t + 2) * C] = d2;
+            vc[(t + 3) * C] = d3;
+        }
+    }
+    for (; t < n; ++t) {
+        if (kPack) {
+            const uint4 a = kc[t], d = vc[t * C];
+            ks[t * slot_vecs] = a;
+            vs[t * slot_vecs] = d;
+        } else {
+            const uint4 a = ks[t * slot_vecs], d = vs[t * slot_vecs];
+            kc[t] = a;
+            vc[t * C] = d;
+        }
+    }
+}
+
 // LDS slot of (token i, chunk c) in a tile stored token-major.  For a
 // power-of-two CT the chunk index is XOR-ed with a function of the row so
 // that 16 consecutive tokens of one chunk (chunk-major access) land in 16
@@ -564,6 +634,38 @@ int launch_copy(bool pack, const Geometry &g0, const RowTable &rt, int32_t max_c
             const int64_t blocks = (int64_t)gl.nl * per_layer;
             e = pack ? launch_tiles_rt<true>(gl, rt, blocks, s) : launch_tiles_rt<false>(gl, rt, blocks, s);
         }
+        if (tok)
+            profile_stop(tok, s, name, 2 * payload);
+        if (e != hipSuccess)
+            return hip_fail(e, name);
+    }
+    return KV_OK;
+}
+
+int launch_steps(bool pack, const Geometry &g0, const RowTable &rt, int32_t n,
+                 int64_t slot_vecs, hipStream_t s)
+{
+    if (n <= 0 || g0.nl <= 0)
+        return KV_OK;
+    const int64_t per_layer = (int64_t)g0.B * g0.H * g0.C;       // threads
+    const int32_t layers_per_launch = (int32_t)std::max<int64_t>(
+        1, std::min<int64_t>(g0.nl, (0x7fffffffLL / kThreads) * kThreads / per_layer));
+    const int64_t blk = (int64_t)g0.H * g0.B * g0.C;
+    const char *name = pack ? "pack_steps" : "unpack_steps";
+    for (int32_t done = 0; done < g0.nl; done += layers_per_launch) {
+        Geometry gl = g0;
+        gl.l0 = g0.l0 + done;
+        gl.nl = std::min<int32_t>(layers_per_launch, g0.nl - done);
+        gl.stage = g0.stage + 2 * (int64_t)done * blk;
+        const int64_t payload = 2 * (int64_t)gl.nl * blk * 16 * n;
+        const int64_t threads = (int64_t)gl.nl * per_layer;
+        void *tok = profiling_enabled() ? profile_start(s) : nullptr;
+        const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads)), block(kThreads);
+        if (pack)
+            copy_steps<true><<<grid, block, 0, s>>>(gl, rt, n, slot_vecs);
+        else
+            copy_steps<false><<<grid, block, 0, s>>>(gl, rt, n, slot_vecs);
+        const hipError_t e = hipGetLastError();
         if (tok)
             profile_stop(tok, s, name, 2 * payload);
         if (e != hipSuccess)

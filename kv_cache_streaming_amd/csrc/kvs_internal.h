@@ -75,10 +75,22 @@ int enqueue_copy(bool pack, const kv_layout &lay, const void *k, const void *v, 
                  int32_t nl, const RowTable &rt, int32_t max_count, void *stage, hipStream_t s,
                  int32_t h0 = 0, int32_t nh = -1);
 
+// n consecutive decode steps of a ring: step t of row b at pos0[b] + t, its
+// slot at stage + t * slot_bytes.  All L layers and H heads.
+int enqueue_steps(bool pack, const kv_layout &lay, const void *k, const void *v,
+                  const int32_t *pos0, int32_t n, void *stage, int64_t slot_bytes,
+                  hipStream_t s);
+
 // ---- kernels (kernels.hip) ----
 // Launches the pack (or unpack) kernels for one call; returns KV_OK or KV_EHIP.
 int launch_copy(bool pack, const Geometry &g, const RowTable &rt, int32_t max_count,
                 hipStream_t s);
+
+// n decode steps at once: step t of row b at position rt.start[b] + t, its
+// one-token-per-row packed block at g.stage + t * slot_vecs (16-byte vectors).
+// Uses g.k, g.v, g.stage, B, H, C, Smax, l0, nl.
+int launch_steps(bool pack, const Geometry &g, const RowTable &rt, int32_t n,
+                 int64_t slot_vecs, hipStream_t s);
 
 // Paged counterpart of launch_copy.
 int launch_paged_copy(bool pack, const PagedGeometry &g, const RowTable &rt, int32_t max_count,

@@ -25,11 +25,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.fixture(scope="module")
 def kv():
-    from kv_cache_streaming_amd import _build
-    if not os.path.exists(_build.LIB):
-        _build.build()
-    import kv_cache_streaming_amd as kv
-    return kv
+    from libload import kv_module
+    return kv_module()
 
 
 def header_functions():

@@ -216,15 +216,20 @@ def test_error_paths(kv):
 TRANSPORTS = [0, 1, 2, 3]   # KV_XFER_AUTO, KV_XFER_KERNEL, KV_XFER_RUNTIME, KV_XFER_DMA
 
 
-def run_ring(kv, dims, R, positions, seed, bits=True, mutate=False, delay_cycles=0, transport=0):
-    """Push every step, flush, restore into a zero cache; compare with the oracle."""
+def run_ring(kv, dims, R, positions, seed, bits=True, mutate=False, delay_cycles=0, transport=0,
+             gather=0, caches=1):
+    """Push every step, flush, restore into a zero cache; compare with the oracle.
+    `caches` > 1: step j reads cache pair (j // 3) % caches (runs of three steps
+    per cache)."""
     import torch
     L, B, H, D, S = dims
     note(f"ring dims={dims} R={R} steps={len(positions)} mutate={mutate} delay={delay_cycles} "
-         f"transport={transport}")
-    K, V = synth.cache_pair(dims, seed, bits=bits)
+         f"transport={transport} gather={gather} caches={caches}")
+    pairs = [synth.cache_pair(dims, seed + 1000 * i, bits=bits) for i in range(caches)]
+    K, V = pairs[0]
     lay = kv.kv_layout_init(L, B, H, D, S, 0)
-    dk, dv = dev(K), dev(V)
+    devs = [(dev(a), dev(b)) for a, b in pairs]
+    dk, dv = devs[0]
     slot = kv.kv_pack_bytes(lay, L, None, 1)
     banks = [empty(R * slot // 2), empty(R * slot // 2)]
     steps = len(positions)
@@ -233,15 +238,19 @@ def run_ring(kv, dims, R, positions, seed, bits=True, mutate=False, delay_cycles
     compute = torch.cuda.current_stream()
     ring = kv.KvRing(lay, R, banks[0], banks[1], hostbuf, host_bytes=steps * slot,
                      copy_stream=copy, transport=transport)
+    if gather:
+        ring.set_gather(kv.KV_RING_GATHER_AT_FLUSH)
     slots = []
     rng = np.random.default_rng(seed)
     if delay_cycles:
         with torch.cuda.stream(copy):
             torch.cuda._sleep(delay_cycles)   # a bounded spin: makes every flush copy late
     for j, pos in enumerate(positions):
-        slots.append(oracle.pack(dims, K, V, 0, L, pos, [1] * B))
-        ring.push(dk, dv, pos, compute)
+        ci = (j // 3) % caches
+        slots.append(oracle.pack(dims, pairs[ci][0], pairs[ci][1], 0, L, pos, [1] * B))
+        ring.push(devs[ci][0], devs[ci][1], pos, compute)
         if mutate:
+            assert caches == 1 and not gather
             # the cache changes between steps (new values at random places)
             idx = rng.integers(0, K.size, size=64)
             K[idx] = rng.integers(0, 1 << 16, size=64).astype(np.uint16)
@@ -264,11 +273,60 @@ def run_ring(kv, dims, R, positions, seed, bits=True, mutate=False, delay_cycles
     ring.close()
 
 
+@pytest.mark.parametrize("gather", [0, 1])
 @pytest.mark.parametrize("transport", TRANSPORTS)
-def test_ring_decode_flow(kv, transport):
+def test_ring_decode_flow(kv, transport, gather):
     dims = (3, 4, 2, 64, 50)
     pos = [[10 + j, 20 + j, 3 + j, 40 + (j % 9)] for j in range(19)]   # 2 full banks + a partial
-    run_ring(kv, dims, 8, pos, seed=21, transport=transport)
+    run_ring(kv, dims, 8, pos, seed=21, transport=transport, gather=gather)
+
+
+@pytest.mark.parametrize("D,R,steps", [(128, 16, 37), (8, 5, 12), (24, 7, 15), (1024, 4, 9)])
+def test_ring_gather_at_flush_runs(kv, D, R, steps):
+    """Gather at flush: runs of consecutive positions packed in one pass, broken
+    by a position jump (row 1 at step 6) and by the cache changing every three
+    steps; the host image and the restore equal the per-step oracle."""
+    dims = (2, 3, 2, D, 60)
+    pos = [[j, 10 + j + (5 if j >= 6 else 0), 17 if j % 4 == 3 else 2 + j]
+           for j in range(steps)]
+    run_ring(kv, dims, R, pos, seed=24, gather=1, caches=2)
+
+
+def test_ring_gather_at_flush_partial_flushes(kv):
+    """Explicit flushes in the middle of a bank: the pending steps are gathered
+    then, and later steps continue in the same bank."""
+    import torch
+    dims = (2, 2, 2, 64, 40)
+    L, B, H, D, S = dims
+    note(f"ring gather-at-flush with partial flushes dims={dims}")
+    K, V = synth.cache_pair(dims, 25, bits=True)
+    lay = kv.kv_layout_init(L, B, H, D, S, 0)
+    dk, dv = dev(K), dev(V)
+    slot = kv.kv_pack_bytes(lay, L, None, 1)
+    R, steps = 6, 14
+    hostbuf = pinned(steps * slot // 2 + CANARY)
+    ring = kv.KvRing(lay, R, empty(R * slot // 2), empty(R * slot // 2), hostbuf,
+                     host_bytes=steps * slot, copy_stream=torch.cuda.Stream())
+    ring.set_gather(kv.KV_RING_GATHER_AT_FLUSH)
+    pos = [[3 + j, 20 + j] for j in range(steps)]
+    for j in range(steps):
+        ring.push(dk, dv, pos[j])
+        if j == 2:
+            with pytest.raises(kv.KvError) as e:      # a pending step: the mode is fixed until a flush
+                ring.set_gather(kv.KV_RING_GATHER_EACH_STEP)
+            assert e.value.status == kv.KV_EBUSY
+        if j in (1, 4, 9):
+            ring.flush()
+    done = torch.cuda.Event()
+    ring.flush(None, done)
+    done.synchronize()
+    assert ring.steps == steps
+    want = oracle.ring_host([oracle.pack(dims, K, V, 0, L, p, [1] * B) for p in pos])
+    got = pinned_host_view(hostbuf)
+    assert np.array_equal(got[:want.size], want)
+    assert np.all(got[want.size:] == 0x5C5C)
+    ring.set_gather(kv.KV_RING_GATHER_EACH_STEP)      # everything flushed: allowed
+    ring.close()
 
 
 @pytest.mark.parametrize("transport", TRANSPORTS)
@@ -276,6 +334,14 @@ def test_ring_duplicate_positions_last_writer_wins(kv, transport):
     dims = (2, 3, 3, 16, 6)
     pos = [[j % 6, (2 * j) % 6, 5] for j in range(11)]
     run_ring(kv, dims, 4, pos, seed=22, mutate=True, transport=transport)
+
+
+def test_ring_restore_runs_keep_the_last_writer(kv):
+    """Runs of consecutive positions that revisit earlier positions (each row
+    cycles through 0..5): the restore applies runs in step order."""
+    dims = (2, 2, 2, 64, 6)
+    pos = [[j % 6, (j + 3) % 6] for j in range(17)]
+    run_ring(kv, dims, 8, pos, seed=26, gather=1)
 
 
 @pytest.mark.parametrize("transport", TRANSPORTS)
@@ -286,6 +352,12 @@ def test_ring_bank_reuse_waits_for_a_late_flush(kv, transport):
     pos = [[j, 63 - j] for j in range(13)]
     run_ring(kv, dims, 2, pos, seed=23, mutate=True, delay_cycles=200_000_000,
              transport=transport)
+
+
+def test_ring_gather_at_flush_waits_for_a_late_flush(kv):
+    dims = (2, 2, 2, 32, 64)
+    pos = [[j, 40 + j] for j in range(13)]
+    run_ring(kv, dims, 2, pos, seed=27, delay_cycles=200_000_000, gather=1)
 
 
 def run_swap(kv, dims, l0, nl, start, count, bank_bytes, seed, delay_cycles=0, transport=0):

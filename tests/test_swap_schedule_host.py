@@ -7,12 +7,8 @@ import oracle
 
 @pytest.fixture(scope="module")
 def kv():
-    import os
-    from kv_cache_streaming_amd import _build
-    if not os.path.exists(_build.LIB):
-        _build.build()
-    import kv_cache_streaming_amd as kv
-    return kv
+    from libload import kv_module
+    return kv_module()
 
 
 def test_matches_the_oracle(kv):
