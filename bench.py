@@ -62,6 +62,9 @@ METRIC = "KV pack/unpack GB/s (% HBM peak) + swap host-link GB/s, 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
 PCIE_PEAK_GBPS = 63.0          # PCIe 5.0 x16, per direction
 
+RING_GATHER = 1   # kv_ring_gather of the rings the steps use (set from --ring-gather)
+
+
 def counters_file(workload):
     return os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
 
@@ -76,8 +79,14 @@ def parse_args():
     ap.add_argument("--swap-bank-mib", type=int, default=256)
     ap.add_argument("--transport", choices=("auto", "kernel", "runtime", "dma", "dma_out"), default="auto",
                     help="bank<->host transfers (see kv_transport in include/kvstream.h)")
+    ap.add_argument("--ring-gather", choices=("flush", "each"), default="flush",
+                    help="rings pack a bank's decode steps at flush time in one pass (flush) or "
+                         "each step as it is pushed (each); see kv_ring_set_gather")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-detail", action="store_true",
+                    help="skip the isolated measurements after the timed steps (ceilings, large "
+                         "slices, schedule): a kernel trace then holds the steps' launches only")
     ap.add_argument("--no-profile", action="store_true",
                     help="do not bracket launches with events (for external profilers)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -134,6 +143,7 @@ class StreamStep:
         self.ring_host = pinned(w.decode_steps * self.slot)
         self.ring = kv.KvRing(self.lay, R, bank(R * self.slot), bank(R * self.slot),
                               self.ring_host, copy_stream=self.s["d2h"], transport=x)
+        self.ring.set_gather(RING_GATHER)
         # double-buffered host images: one written this step, one read
         self.host_p = [pinned(L * self.layer_prompt) for _ in range(2)]
         self.host_s = [pinned(L * self.layer_full) for _ in range(2)]
@@ -260,6 +270,7 @@ class RingStep:
         self.ring_host = _pinned(torch, w.decode_steps * self.slot)
         self.ring = kv.KvRing(self.lay, R, _bank(torch, R * self.slot), _bank(torch, R * self.slot),
                               self.ring_host, copy_stream=self.s["d2h"], transport=transport)
+        self.ring.set_gather(RING_GATHER)
 
     def link_bytes(self):
         return 2 * self.w.decode_steps * self.slot
@@ -523,6 +534,7 @@ class LongStep:
         self.ring_host = _pinned(torch, w.decode_steps * self.slot)
         self.ring = kv.KvRing(self.lay, R, _bank(torch, R * self.slot), _bank(torch, R * self.slot),
                               self.ring_host, copy_stream=self.s["d2h"], transport=transport)
+        self.ring.set_gather(RING_GATHER)
         self.k = 0
 
     def link_bytes(self):
@@ -707,23 +719,37 @@ def paged_slices(step, kv, reps=3):
     return out
 
 
-def decode_push_us(step, reps=3):
-    torch = step.torch
+def decode_step_us(step, kv, reps=3):
+    """GPU time per decode step on the compute stream for the workload's decode
+    steps, with a ring of one bank holding them all (no bank reuse, so no wait
+    for a flush copy): each step packed as it is pushed, or all packed in one
+    pass at the flush."""
+    torch, w = step.torch, step.w
     st = step.s["t"]
     Bc = step.caches["B"]
-    times = []
-    for _ in range(reps):
-        step.ring.reset()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(st)
-        for pos in step.positions:
-            step.ring.push(Bc[0], Bc[1], pos, st)
-        b.record(st)
-        step.ring.flush(st)
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b) * 1000 / len(step.positions))
-    return min(times)
+    n = len(step.positions)
+    bank = [torch.empty(n * step.slot // 2, dtype=torch.int16, device="cuda") for _ in range(2)]
+    hostbuf = _pinned(torch, n * step.slot)
+    ring = kv.KvRing(step.lay, n, bank[0], bank[1], hostbuf, copy_stream=step.s["d2h"])
+    out = {}
+    for name, mode in (("each_step", kv.KV_RING_GATHER_EACH_STEP),
+                       ("at_flush", kv.KV_RING_GATHER_AT_FLUSH)):
+        ring.set_gather(mode)
+        times = []
+        for _ in range(reps):
+            ring.reset()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            for pos in step.positions:
+                ring.push(Bc[0], Bc[1], pos, st)
+            ring.flush(st)
+            b.record(st)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1000 / n)
+        out[name] = round(min(times), 2)
+    ring.close()
+    return out
 
 
 def read_counters(workload, kernel_name):
@@ -836,6 +862,9 @@ def main():
     import synth
     w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    global RING_GATHER
+    RING_GATHER = {"flush": kv.KV_RING_GATHER_AT_FLUSH, "each": kv.KV_RING_GATHER_EACH_STEP}[
+        args.ring_gather]
     step = STEPS[w.name](w, args.swap_bank_mib << 20,
                 {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3, "dma_out": 4}[args.transport])
     torch.cuda.synchronize()
@@ -895,10 +924,10 @@ def main():
 
     detail = {"kernels": kernels, "link_bytes_per_step": link,
               "link_peak_per_direction_GBps": PCIE_PEAK_GBPS}
-    if not args.no_profile:
+    if not args.no_profile and not args.no_detail:
         detail["link_ceiling_GBps"] = {k: round(v, 2) for k, v in link_ceiling(torch).items()}
         if isinstance(step, StreamStep):
-            detail["decode_push_us"] = round(decode_push_us(step), 2)
+            detail["decode_step_us"] = decode_step_us(step, kv)
             detail["hbm_copy_ceiling_GBps"] = round(hbm_copy_ceiling(torch), 1)
             detail["large_slices"] = large_slices(step, kv)
             if step.w.B * step.w.Smax >= 4096:
@@ -922,7 +951,7 @@ def main():
                        "decode_steps": w.decode_steps, "ring_slots": w.ring_slots,
                        "chunk_tokens": w.chunk_tokens, "microbatches": w.microbatches,
                        "swap_bank_mib": args.swap_bank_mib,
-                       "transport": args.transport,
+                       "transport": args.transport, "ring_gather": args.ring_gather,
                        "hw_queues": int(os.environ["GPU_MAX_HW_QUEUES"])},
             "roofline": roofline, "cpu_baseline": cpu, "detail": detail}
     print(json.dumps(line), flush=True)
