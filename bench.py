@@ -63,6 +63,7 @@ HBM_PEAK_GBPS = 8000.0
 PCIE_PEAK_GBPS = 63.0          # PCIe 5.0 x16, per direction
 
 RING_GATHER = 1   # kv_ring_gather of the rings the steps use (set from --ring-gather)
+WHOLE_CALLS = True   # swaps of complete images as one call each (set from --swap-calls)
 
 
 def counters_file(workload):
@@ -82,6 +83,12 @@ def parse_args():
     ap.add_argument("--ring-gather", choices=("flush", "each"), default="flush",
                     help="rings pack a bank's decode steps at flush time in one pass (flush) or "
                          "each step as it is pushed (each); see kv_ring_set_gather")
+    ap.add_argument("--swap-calls", choices=("whole", "layer"), default="whole",
+                    help="gpt2 shapes: a complete host image (prompt load, microbatch swap) moves "
+                         "in one call the engine chunks by bank (whole) or in one call per layer")
+    ap.add_argument("--compute-streams", type=int, choices=(1, 2), default=2,
+                    help="gpt2 shapes: packs and unpacks of the two link directions on one "
+                         "compute stream (1) or one each (2)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true",
@@ -166,11 +173,17 @@ class StreamStep:
         hs_out, hs_in = self.host_s[out].data_ptr(), self.host_s[inn].data_ptr()
         lp, lf = self.layer_prompt, self.layer_full
         # 1+2: prompt streaming out of A || loading an earlier prompt into B
+        if WHOLE_CALLS:
+            # the earlier prompt is complete on the host: one call, chunked by
+            # the engine into bank-sized pieces
+            self.eng_t.swap_in(Bc[0], Bc[1], 0, L, self.rows_start, self.rows_prompt, hp_in,
+                               L * lp, st)
         for l in range(L):
             self.eng_p.stream_prompt_layer(A[0], A[1], l, 0, self.prompt, None,
                                            hp_out + l * lp, lp, sp)
-            self.eng_t.swap_in(Bc[0], Bc[1], l, 1, self.rows_start, self.rows_prompt,
-                               hp_in + l * lp, lp, st)
+            if not WHOLE_CALLS:
+                self.eng_t.swap_in(Bc[0], Bc[1], l, 1, self.rows_start, self.rows_prompt,
+                                   hp_in + l * lp, lp, st)
         # 3: decode steps of B into the staging ring
         self.ring.reset()
         for pos in self.positions:
@@ -179,11 +192,52 @@ class StreamStep:
         # 4: restore the ring into D
         self.ring.restore(Dc[0], Dc[1], st)
         # 5: swap out microbatch x-1 (B) || swap in microbatch x+1 (into C)
-        for l in range(L):
-            self.eng_o.swap_out(Bc[0], Bc[1], l, 1, self.rows_start, self.rows_full,
-                                hs_out + l * lf, lf, st)
-            self.eng_i.swap_in(Cc[0], Cc[1], l, 1, self.rows_start, self.rows_full,
-                               hs_in + l * lf, lf, sp)
+        if WHOLE_CALLS:
+            self.eng_o.swap_out(Bc[0], Bc[1], 0, L, self.rows_start, self.rows_full, hs_out,
+                                L * lf, st)
+            self.eng_i.swap_in(Cc[0], Cc[1], 0, L, self.rows_start, self.rows_full, hs_in,
+                               L * lf, sp)
+        else:
+            for l in range(L):
+                self.eng_o.swap_out(Bc[0], Bc[1], l, 1, self.rows_start, self.rows_full,
+                                    hs_out + l * lf, lf, st)
+                self.eng_i.swap_in(Cc[0], Cc[1], l, 1, self.rows_start, self.rows_full,
+                                   hs_in + l * lf, lf, sp)
+        torch.cuda.synchronize()
+
+    def run_one_stream(self):
+        """The same step with every pack and unpack on one compute stream: a
+        direction's pack (or unpack) of layer l+1 is enqueued before the other
+        direction's unpack of layer l, so each link keeps a bank ready while
+        the HBM kernels run one at a time instead of splitting the bandwidth."""
+        torch, w = self.torch, self.w
+        L = w.L
+        A, Bc, Cc, Dc = (self.caches[n] for n in "ABCD")
+        c = self.s["p"]
+        out, inn = self.k % 2, (self.k + 1) % 2
+        self.k += 1
+        hp_out, hp_in = self.host_p[out].data_ptr(), self.host_p[inn].data_ptr()
+        hs_out, hs_in = self.host_s[out].data_ptr(), self.host_s[inn].data_ptr()
+        lp, lf = self.layer_prompt, self.layer_full
+        for l in range(L + 1):
+            if l < L:
+                self.eng_p.stream_prompt_layer(A[0], A[1], l, 0, self.prompt, None,
+                                               hp_out + l * lp, lp, c)
+            if l >= 1:
+                self.eng_t.swap_in(Bc[0], Bc[1], l - 1, 1, self.rows_start, self.rows_prompt,
+                                   hp_in + (l - 1) * lp, lp, c)
+        self.ring.reset()
+        for pos in self.positions:
+            self.ring.push(Bc[0], Bc[1], pos, c)
+        self.ring.flush(c)
+        self.ring.restore(Dc[0], Dc[1], c)
+        for l in range(L + 1):
+            if l < L:
+                self.eng_o.swap_out(Bc[0], Bc[1], l, 1, self.rows_start, self.rows_full,
+                                    hs_out + l * lf, lf, c)
+            if l >= 1:
+                self.eng_i.swap_in(Cc[0], Cc[1], l - 1, 1, self.rows_start, self.rows_full,
+                                   hs_in + (l - 1) * lf, lf, c)
         torch.cuda.synchronize()
 
 
@@ -752,9 +806,10 @@ def decode_step_us(step, kv, reps=3):
     return out
 
 
-def read_counters(workload, kernel_name):
+def read_counters(workload, kernel_name, algorithmic):
     """Per-launch HBM traffic of `kernel_name` from the committed counter summary
-    of the workload, or None when absent or taken on a different kernel source."""
+    of the workload, or None when absent, taken on a different kernel source or
+    on a different mix of launches (another algorithmic size per launch)."""
     path = counters_file(workload)
     if not os.path.exists(path):
         return None
@@ -767,6 +822,8 @@ def read_counters(workload, kernel_name):
     src = os.path.join(ROOT, "kv_cache_streaming_amd", "csrc", "kernels.hip")
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     if fields.get("kernels_sha256_16") != digest or fields.get("kernel") != kernel_name:
+        return None
+    if fields.get("algorithmic_bytes_per_launch") != str(algorithmic):
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])
@@ -862,7 +919,8 @@ def main():
     import synth
     w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
-    global RING_GATHER
+    global RING_GATHER, WHOLE_CALLS
+    WHOLE_CALLS = args.swap_calls == "whole"
     RING_GATHER = {"flush": kv.KV_RING_GATHER_AT_FLUSH, "each": kv.KV_RING_GATHER_EACH_STEP}[
         args.ring_gather]
     step = STEPS[w.name](w, args.swap_bank_mib << 20,
@@ -879,6 +937,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if isinstance(step, StreamStep) and args.compute_streams == 1:
+        step.run = step.run_one_stream
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -915,7 +975,7 @@ def main():
         hbm = [k for k in kernels if not k.startswith("link_copy")]
         dom = max(hbm, key=lambda k: kernels[k]["gpu_ms_per_step"])
         d = kernels[dom]
-        traffic = read_counters(w.name, dom)
+        traffic = read_counters(w.name, dom, d["algorithmic_bytes_per_launch"])
         roofline = {"bound": "hbm", "kernel": dom, "achieved": d["GBps"], "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(d["GBps"] / HBM_PEAK_GBPS, 4),
                     "traffic": traffic,
@@ -952,6 +1012,7 @@ def main():
                        "chunk_tokens": w.chunk_tokens, "microbatches": w.microbatches,
                        "swap_bank_mib": args.swap_bank_mib,
                        "transport": args.transport, "ring_gather": args.ring_gather,
+                       "compute_streams": args.compute_streams, "swap_calls": args.swap_calls,
                        "hw_queues": int(os.environ["GPU_MAX_HW_QUEUES"])},
             "roofline": roofline, "cpu_baseline": cpu, "detail": detail}
     print(json.dumps(line), flush=True)
