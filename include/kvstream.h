@@ -241,8 +241,9 @@ int64_t kv_stream_bytes(const kv_layout *lay, const kv_part *self, const kv_part
 /* stream_out: pack the piece of src's cache (k, v; layout `lay`) that `dst`
  * holds into `staging` (device memory).  start/count: int32[src->rows], the
  * token range [start_b, start_b + count_b) of each local row (count NULL:
- * one token per row); rows outside dst are not read.  Errors as
- * kv_pack_tokens; an empty intersection enqueues nothing. */
+ * one token per row).  Every row's range is checked (KV_ERANGE); only the
+ * rows dst holds are moved.  Errors as kv_pack_tokens; an empty intersection
+ * enqueues nothing (staging may then be NULL). */
 int kv_stream_out(const kv_layout *lay, const kv_part *src, const void *k, const void *v,
                   const kv_part *dst, const int32_t *start, const int32_t *count,
                   void *staging, int64_t staging_bytes, hipStream_t s);
