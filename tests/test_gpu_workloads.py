@@ -129,26 +129,44 @@ def test_gpt2_1p5b_full_flow(kv):
     for l in range(w.L):
         want = oracle.pack(w.dims, K, V, l, 1, [0] * B, prompt)
         assert np.array_equal(hv[l * want.size:(l + 1) * want.size], want), f"prompt layer {l}"
-    # decode ring
+    # the streamed prompt loaded back as one call through one-layer banks
+    # (the token worker's load in the bench step), into a sentinel cache
+    ein = kv.KvSwap(lay, bank(layer_bytes), bank(layer_bytes), layer_bytes, copy_in)
+    pk = torch.full_like(dk, 0x0F0F)
+    pv = torch.full_like(dv, 0x0F0F)
+    ein.swap_in(pk, pv, 0, w.L, [0] * B, prompt, host, w.L * layer_bytes)
+    torch.cuda.synchronize()
+    ek = np.full_like(K, 0x0F0F)
+    ev = np.full_like(V, 0x0F0F)
+    oracle.unpack(w.dims, ek, ev, 0, w.L, [0] * B, prompt, hv)
+    assert np.array_equal(pk.cpu().numpy().view(np.uint16), ek), "prompt load K"
+    assert np.array_equal(pv.cpu().numpy().view(np.uint16), ev), "prompt load V"
+    del pk, pv, ek, ev
+    ein.close()
+    # decode ring, each step packed when pushed and a bank gathered at its flush
     pos = synth.decode_positions(w)
     slot = kv.kv_pack_bytes(lay, w.L, None, 1)
     R = w.ring_slots
-    rhost = pinned(w.decode_steps * slot // 2)
-    ring = kv.KvRing(lay, R, bank(R * slot), bank(R * slot), rhost, copy_stream=copy_out)
-    for p in pos:
-        ring.push(dk, dv, p)
-    ring.flush(None, done)
-    done.synchronize()
     want = oracle.ring_host([oracle.pack(w.dims, K, V, 0, w.L, p, [1] * B) for p in pos])
-    assert np.array_equal(pinned_host_view(rhost), want), "ring host image"
-    rk, rv = torch.zeros_like(dk), torch.zeros_like(dv)
-    ring.restore(rk, rv)
     ek, ev = np.zeros_like(K), np.zeros_like(V)
     oracle.ring_restore(w.dims, ek, ev, pos, want)
-    torch.cuda.synchronize()
-    assert np.array_equal(rk.cpu().numpy().view(np.uint16), ek), "restored K"
-    assert np.array_equal(rv.cpu().numpy().view(np.uint16), ev), "restored V"
-    del rk, rv, ek, ev
+    for gather in (kv.KV_RING_GATHER_EACH_STEP, kv.KV_RING_GATHER_AT_FLUSH):
+        rhost = pinned(w.decode_steps * slot // 2)
+        ring = kv.KvRing(lay, R, bank(R * slot), bank(R * slot), rhost, copy_stream=copy_out)
+        ring.set_gather(gather)
+        for p in pos:
+            ring.push(dk, dv, p)
+        ring.flush(None, done)
+        done.synchronize()
+        assert np.array_equal(pinned_host_view(rhost), want), f"ring host image (gather {gather})"
+        rk, rv = torch.zeros_like(dk), torch.zeros_like(dv)
+        ring.restore(rk, rv)
+        torch.cuda.synchronize()
+        assert np.array_equal(rk.cpu().numpy().view(np.uint16), ek), "restored K"
+        assert np.array_equal(rv.cpu().numpy().view(np.uint16), ev), "restored V"
+        ring.close()
+        del rk, rv
+    del ek, ev
     # microbatch swap-out of all 1024 positions, swap-in to a sentinel cache
     full = [w.Smax] * B
     total = kv.kv_pack_bytes(lay, w.L, full)
@@ -168,18 +186,19 @@ def test_gpt2_1p5b_full_flow(kv):
     ei.swap_in(sk, svv, 0, w.L, [0] * B, full, shost, total)
     torch.cuda.synchronize()
     assert torch.equal(sk, dk) and torch.equal(svv, dv), "swap-in of every position restores the cache"
-    ring.close()
     eng.close()
     eo.close()
     ei.close()
 
 
-def test_opt66b_slice_decode_ring(kv):
+@pytest.mark.parametrize("gather", [0, 1])
+def test_opt66b_slice_decode_ring(kv, gather):
     """Ragged decode positions (len_b + j), 64 steps into a ring of 16 flushed to
-    pinned host memory, restored into a second, zeroed cache."""
+    pinned host memory, restored into a second, zeroed cache; each step packed
+    when pushed, or a bank's 16 steps in one pass at its flush."""
     import torch
     w = synth.WORKLOADS["opt-66b-16l"]
-    note(f"workload {w.name} dims={w.dims}")
+    note(f"workload {w.name} dims={w.dims} gather={gather}")
     lay = kv.kv_layout_init(*w.dims, w.dtype)
     dk, dv = device_cache(w, w.value_seed)
     K = dk.cpu().numpy().view(np.uint16)
@@ -191,6 +210,7 @@ def test_opt66b_slice_decode_ring(kv):
     R = w.ring_slots
     host = pinned(w.decode_steps * slot // 2)
     ring = kv.KvRing(lay, R, bank(R * slot), bank(R * slot), host, copy_stream=torch.cuda.Stream())
+    ring.set_gather(gather)
     for p in pos:
         ring.push(dk, dv, p)
     done = torch.cuda.Event()
@@ -311,6 +331,7 @@ def test_gqa_100k_long_context(kv):
     R = w.ring_slots
     host = pinned(w.decode_steps * slot // 2)
     ring = kv.KvRing(lay, R, bank(R * slot), bank(R * slot), host, copy_stream=torch.cuda.Stream())
+    ring.set_gather(kv.KV_RING_GATHER_AT_FLUSH)       # as the bench step runs it
     for p in pos:
         ring.push(dk, dv, p)
     done = torch.cuda.Event()
