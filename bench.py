@@ -532,8 +532,9 @@ class SwapStep:
 class LongStep:
     """The 100K-context workload: 60 layers, 4 rows, 8 KV heads, D=128, bf16,
     current lengths U{20000..99936}.  One step = the row of the longest context
-    swapped out to pinned host memory layer by layer while its previous image
-    is swapped back in (both directions at once), the whole prompt of every
+    swapped out to pinned host memory while its previous image is swapped
+    into a free one-row slot (a cache of its own, as a swapped-in request
+    lands in a free slot; both directions at once), the whole prompt of every
     row streamed out in 4096-token chunks per layer, and 64 decode steps
     through a 16-slot staging ring restored into the cache."""
 
@@ -574,11 +575,15 @@ class LongStep:
         sb = max(swap_bank_bytes, -(-self.row_layer // (1 << 20)) << 20)
         self.eng_o = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb,
                                self.s["d2h_row"], transport)
-        self.eng_i = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb, self.s["h2d"],
+        # the one-row slot: the row's packed image is the same bytes in a cache
+        # of one row (the other rows move no tokens)
+        self.lay1 = kv.kv_layout_init(L, 1, w.H, w.D, w.Smax, w.dtype)
+        n1 = L * w.H * w.D * w.Smax
+        self.slot1 = (torch.empty(n1, dtype=torch.int16, device="cuda"),
+                      torch.empty(n1, dtype=torch.int16, device="cuda"))
+        self.eng_i = kv.KvSwap(self.lay1, _bank(torch, sb), _bank(torch, sb), sb, self.s["h2d"],
                                transport)
         self.row_host = [HostBuffer(kv, self.row_image) for _ in range(2)]
-        self.packed = [torch.cuda.Event() for _ in range(L)]
-        self.row_in = torch.cuda.Event()
         torch.cuda.synchronize()
         self.eng_o.swap_out(self.A[0], self.A[1], 0, L, self.row_start, self.row_count,
                             self.row_host[1], self.row_image, torch.cuda.current_stream())
@@ -599,13 +604,10 @@ class LongStep:
         torch, w = self.torch, self.w
         out, inn = self.k % 2, (self.k + 1) % 2
         self.k += 1
-        _duplex_layers(self.eng_o, self.eng_i, self.A, self.A, w.L, self.row_start,
-                       self.row_count, self.row_host[out].data_ptr(),
-                       self.row_host[inn].data_ptr(), self.row_layer, self.s["out"],
-                       self.s["in"], self.packed)
-        # the prompt chunks read the swapped row too: start them once it is back
-        self.row_in.record(self.s["in"])
-        self.s["p"].wait_event(self.row_in)
+        self.eng_o.swap_out(self.A[0], self.A[1], 0, w.L, self.row_start, self.row_count,
+                            self.row_host[out], self.row_image, self.s["out"])
+        self.eng_i.swap_in(self.slot1[0], self.slot1[1], 0, w.L, [0], [max(self.row_count)],
+                           self.row_host[inn], self.row_image, self.s["in"])
         for l in range(w.L):
             off = self.prompt_host[l % 2].data_ptr()
             for c0, nb in self.chunks:
