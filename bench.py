@@ -66,8 +66,8 @@ RING_GATHER = 1   # kv_ring_gather of the rings the steps use (set from --ring-g
 WHOLE_CALLS = True   # swaps of complete images as one call each (set from --swap-calls)
 
 
-def counters_file(workload):
-    return os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+def counters_file(workload, kernel_name):
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_{workload}.txt")
 
 
 def parse_args():
@@ -812,7 +812,7 @@ def read_counters(workload, kernel_name, algorithmic):
     """Per-launch HBM traffic of `kernel_name` from the committed counter summary
     of the workload, or None when absent, taken on a different kernel source or
     on a different mix of launches (another algorithmic size per launch)."""
-    path = counters_file(workload)
+    path = counters_file(workload, kernel_name)
     if not os.path.exists(path):
         return None
     import hashlib
@@ -856,6 +856,23 @@ def cpu_baseline(step, budget_s):
             ops.append(("restore unpack", j, None))
     done_bytes, ran, last = 0, {}, None
     t0 = time.perf_counter()
+    passes = 0
+    # whole passes over the step's calls, repeated while the budget lasts
+    while time.perf_counter() - t0 < budget_s and passes < 4:
+        passes += 1
+        done_bytes, last = run_ops(ops, w, oracle, Bh, start, prompt, full, step, L, B,
+                                   done_bytes, ran, t0, budget_s)
+    elapsed = time.perf_counter() - t0
+    sample = ", ".join(f"{v} x {k}" for k, v in ran.items())
+    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{sample} ({passes} pass(es) over the step's calls): "
+                      f"{done_bytes / 1e9:.3f} GB of KV payload in {elapsed:.1f} s "
+                      f"(single-threaded C oracle)"}
+
+
+def run_ops(ops, w, oracle, Bh, start, prompt, full, step, L, B, done_bytes, ran, t0, budget_s):
+    last = None
     for name, idx, fn in ops:
         if time.perf_counter() - t0 > budget_s:
             break
@@ -869,12 +886,7 @@ def cpu_baseline(step, budget_s):
             oracle.unpack(w.dims, Bh[0], Bh[1], 0, L, step.positions[idx], [1] * B, last)
         done_bytes += last.nbytes
         ran[name] = ran.get(name, 0) + 1
-    elapsed = time.perf_counter() - t0
-    sample = ", ".join(f"{v} x {k}" for k, v in ran.items())
-    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{sample}: {done_bytes / 1e9:.3f} GB of KV payload in {elapsed:.1f} s "
-                      f"(single-threaded C oracle)"}
+    return done_bytes, last
 
 
 
