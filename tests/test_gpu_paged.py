@@ -136,17 +136,19 @@ def test_block_ids_outside_the_pool_are_skipped(kv):
     assert np.array_equal(host(gk), eK) and np.array_equal(host(gv), eV), "unpack with skipped blocks"
 
 
-def test_gpt2_1p5b_from_a_16_token_page_pool(kv):
+@pytest.mark.parametrize("P", [16, 256])
+def test_gpt2_1p5b_from_a_page_pool(kv, P):
     """48 layers x 25 heads x 64 dims, 8 rows of 1000 prompt tokens in
-    16-token pages scattered over the pool: every prompt layer packed from the
-    pool, and one decode step (positions 1000) unpacked into it."""
+    P-token pages scattered over the pool: every prompt layer packed from the
+    pool one call per layer and all layers in one call (as the bench times
+    it), and one decode step (positions 1000) unpacked into it."""
     import torch
     w = synth.WORKLOADS["gpt2-1.5b"]
     L, B, H, D = w.L, w.B, w.H, w.D
-    P, stride = 16, w.Smax // 16
+    stride = w.Smax // P
     NB = B * stride + 40
     pd = (L, NB, H, D, P)
-    note(f"paged gpt2-1.5b pool {pd}")
+    note(f"paged gpt2-1.5b pool {pd} P={P}")
     pg = kv.kv_paged_init(L, NB, H, D, P, 0)
     n = L * NB * H * D * P
     rng = np.random.default_rng(16)
@@ -167,6 +169,10 @@ def test_gpt2_1p5b_from_a_16_token_page_pool(kv):
     torch.cuda.synchronize()
     want = oracle.pack_paged(pd, Kp, Vp, 0, L, table, start, count)
     assert np.array_equal(host(st), want), "prompt layers from the page pool"
+    st.fill_(0x7A7A)
+    kv.kv_pack_paged(pg, dk, dv, 0, L, dt, start, count, st, nbytes)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(st), want), "all layers from the page pool in one call"
     pos = np.full(B, w.prompt_len, np.int32)
     new = synth.random_bits(2 * L * H * D * B, 17)
     kv.kv_unpack_paged(pg, dk, dv, 0, L, dt, pos, None, dev(new), new.nbytes)

@@ -186,6 +186,12 @@ def test_gpt2_1p5b_full_flow(kv):
     ei.swap_in(sk, svv, 0, w.L, [0] * B, full, shost, total)
     torch.cuda.synchronize()
     assert torch.equal(sk, dk) and torch.equal(svv, dv), "swap-in of every position restores the cache"
+    # the isolated large slice: one pack call over every layer and position
+    big = torch.empty(total // 2, dtype=torch.int16, device="cuda")
+    kv.kv_pack_tokens(lay, dk, dv, 0, w.L, [0] * B, full, big, total)
+    torch.cuda.synchronize()
+    assert np.array_equal(big.cpu().numpy().view(np.uint16), sv), "48-layer pack in one call"
+    del big
     eng.close()
     eo.close()
     ei.close()
