@@ -52,8 +52,11 @@
  *     hipHostMalloc).  Staging must not overlap either cache.
  *   - Per-row arrays (start, count, pos, row_len) are host int32[B], read
  *     during the call only.  B <= KV_MAX_ROWS.
- *   - Every call validates synchronously.  On error it returns a negative
- *     kv_status, enqueues nothing, and sets the thread-local kv_last_error().
+ *   - Every call validates its arguments synchronously.  A call rejected by
+ *     these checks returns a negative kv_status, enqueues nothing, and sets
+ *     the thread-local kv_last_error().  A call that enqueues several
+ *     launches or copies and then meets a HIP runtime failure (KV_EHIP)
+ *     leaves the part before the failure enqueued; destroy the handle then.
  *   - On success it returns once the work is enqueued (asynchronous).  Buffers
  *     must stay alive until the stream (or the `done` event) passes them.
  *   - No C++ exception crosses this ABI.  Device faults surface at the
