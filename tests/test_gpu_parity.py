@@ -114,6 +114,27 @@ def test_empty_and_degenerate(kv):
     assert np.all(host(st) == 0x7A7A)
 
 
+def test_maximum_rows(kv):
+    """KV_MAX_ROWS = 256 rows in one call (the row table travels in the kernel
+    arguments): ragged and empty rows with the tile kernel, one token per row
+    with the small kernel, and a ring of 256-row decode steps gathered at
+    flush."""
+    rng = np.random.default_rng(256)
+    dims = (2, kv.KV_MAX_ROWS, 2, 16, 40)
+    L, B, H, D, S = dims
+    st, ct = random_ranges(rng, B, S)
+    ct[0], st[0] = S, 0
+    ct[1], ct[2] = 0, 9
+    st[2] = min(st[2], S - 9)
+    check_pack_unpack(kv, dims, 0, L, st, ct, seed=256)
+    check_pack_unpack(kv, dims, 1, 1, [int(x) for x in rng.integers(0, S, size=B)], [1] * B,
+                      seed=257)
+    pos = [[int(p0) + j for p0 in rng.integers(0, S - 10, size=B)] for j in range(10)]
+    for j in range(1, 10):
+        pos[j] = [p + j for p in pos[0]]
+    run_ring(kv, dims, 4, pos, seed=258, gather=1)
+
+
 def test_fp16_and_bf16_values(kv):
     dims = (2, 2, 3, 64, 300)
     check_pack_unpack(kv, dims, 0, 2, [0, 17], [300, 250], seed=5, bits=False, dtype=0)
