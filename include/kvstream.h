@@ -159,8 +159,9 @@ int kv_unpack_prompt_layer(const kv_layout *lay, void *k, void *v,
 
 /* ---------------------------------------------------------------------------
  * Paged pools.  The pages name vLLM's paged KV memory and Mooncake's
- * chunk-organised KV ([DV, Related work]; [PD], KV Cache Pool) without giving
- * a layout; the one taken here is the contiguous layout with (row, Smax)
+ * chunk-organised KV ([DV, Related work]; [KV, KV Cache transfer: Mooncake,
+ * KV Cache Pool]) without giving a layout; the one taken here is the
+ * contiguous layout with (row, Smax)
  * replaced by (physical block, block_tokens P): key
  * [L, blocks, H, D/8, P, 8], value [L, blocks, H, P, D].  A row's tokens
  * live in the blocks its table names: token s of row b is slot s % P of
