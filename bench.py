@@ -372,18 +372,8 @@ class RingStep:
                     else:
                         kv.kv_stream_in(dlay, d, caches[i][0], caches[i][1], src, start, lens,
                                         st[i], nbytes, s)
-            run()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(s)
-            for _ in range(reps):
-                run()
-            e1.record(s)
-            torch.cuda.synchronize()
-            sec = e0.elapsed_time(e1) / 1000 / reps / len(dsts)
-            out[name + "_us_per_piece"] = round(sec * 1e6, 1)
-            out[name + "_hbm_GBps"] = round(2 * nbytes / sec / 1e9, 1)
-            out[name + "_frac_of_peak"] = round(2 * nbytes / sec / 1e9 / HBM_PEAK_GBPS, 4)
+            secs = [x / len(dsts) for x in rep_seconds(torch, run, s)]
+            rate_entry(out, name + "_per_piece", secs, 2 * nbytes, HBM_PEAK_GBPS, "_hbm_GBps")
         del caches, st
         return out
 
@@ -683,10 +673,52 @@ def hbm_copy_ceiling(torch, nbytes=1 << 30, reps=4):
     return gbps
 
 
-def large_slices(step, kv, reps=3):
-    """Isolated rates on the workload's largest slices: one pack and one unpack
-    of every layer and position of cache B (2.5 GB of payload in one call), and
-    one whole-cache swap per link direction alone."""
+def rep_seconds(torch, fn, s=None, warm=5, reps=20):
+    """Seconds of each of `reps` back-to-back calls of `fn` after `warm` untimed
+    ones: events on stream `s` between calls, or (s None: work that spans
+    streams) the host clock around each call and a synchronisation."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    if s is None:
+        out = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            out.append(time.perf_counter() - t0)
+        return out
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(s)
+    for i in range(reps):
+        fn()
+        ev[i + 1].record(s)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) / 1000 for i in range(reps)]
+
+
+def spread(secs):
+    """median, p10, p90 of a list of seconds, in microseconds."""
+    import numpy as np
+    a = np.asarray(secs) * 1e6
+    return float(np.median(a)), float(np.percentile(a, 10)), float(np.percentile(a, 90))
+
+
+def rate_entry(out, name, secs, nbytes, peak, unit_key):
+    med, p10, p90 = spread(secs)
+    out[name + "_us"] = {"median": round(med, 1), "p10": round(p10, 1), "p90": round(p90, 1),
+                         "reps": len(secs)}
+    rate = nbytes / (med / 1e6) / 1e9
+    out[name + unit_key] = round(rate, 2)
+    out[name + "_frac_of_peak"] = round(rate / peak, 4)
+
+
+def large_slices(step, kv):
+    """Isolated rates on the workload's largest slices (median of 20 timed calls
+    after 5 warm-up ones, with p10/p90): one pack and one unpack of every layer
+    and position of a cache (2.5 GB of payload in one call, past the 256 MB
+    Infinity Cache), and one whole-cache swap per link direction alone, in
+    one call each as the step issues them."""
     torch, w = step.torch, step.w
     L, B = w.L, w.B
     full = [w.Smax] * B
@@ -699,44 +731,25 @@ def large_slices(step, kv, reps=3):
                                                        st, payload, s)),
                      ("unpack", lambda: kv.kv_unpack_tokens(step.lay, Cc[0], Cc[1], 0, L, [0] * B,
                                                            full, st, payload, s))):
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(s)
-        for _ in range(reps):
-            fn()
-        e1.record(s)
-        torch.cuda.synchronize()
-        sec = e0.elapsed_time(e1) / 1000 / reps
-        out[name + "_us"] = round(sec * 1e6, 1)
-        out[name + "_hbm_GBps"] = round(2 * payload / sec / 1e9, 1)
-        out[name + "_frac_of_peak"] = round(2 * payload / sec / 1e9 / HBM_PEAK_GBPS, 4)
+        rate_entry(out, name, rep_seconds(torch, fn, s), 2 * payload, HBM_PEAK_GBPS, "_hbm_GBps")
     del st
-    lf = step.layer_full
     hs = step.host_s[0].data_ptr()
-    for name, fn in (("swap_out", lambda: [step.eng_o.swap_out(Bc[0], Bc[1], l, 1, step.rows_start,
-                                                              step.rows_full, hs + l * lf, lf, s)
-                                           for l in range(L)]),
-                     ("swap_in", lambda: [step.eng_i.swap_in(Cc[0], Cc[1], l, 1, step.rows_start,
-                                                            step.rows_full, hs + l * lf, lf, s)
-                                          for l in range(L)])):
-        fn()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            fn()
-        torch.cuda.synchronize()
-        sec = (time.perf_counter() - t0) / reps
-        out[name + "_link_GBps"] = round(L * lf / sec / 1e9, 2)
-        out[name + "_frac_of_pcie"] = round(L * lf / sec / 1e9 / PCIE_PEAK_GBPS, 4)
+    total = L * step.layer_full
+    for name, fn in (("swap_out", lambda: step.eng_o.swap_out(Bc[0], Bc[1], 0, L, step.rows_start,
+                                                              step.rows_full, hs, total, s)),
+                     ("swap_in", lambda: step.eng_i.swap_in(Cc[0], Cc[1], 0, L, step.rows_start,
+                                                            step.rows_full, hs, total, s))):
+        rate_entry(out, name, rep_seconds(torch, fn, None, warm=2, reps=10), total,
+                   PCIE_PEAK_GBPS, "_link_GBps")
     return out
 
 
-def paged_slices(step, kv, reps=3):
+def paged_slices(step, kv):
     """Isolated rates of the paged pool kernels on the workload's prompt: every
     layer's 1000 prompt tokens of 8 rows packed from (and unpacked into) a pool
     of 16-token pages and one of 256-token chunks, the rows' blocks scattered
-    at random over the pool; HBM bytes = read + write of the payload."""
+    at random over the pool; HBM bytes = read + write of the payload; median
+    of 20 timed calls after 5 warm-up ones."""
     import numpy as np
     torch, w = step.torch, step.w
     L, B, H, D = w.L, w.B, w.H, w.D
@@ -757,18 +770,9 @@ def paged_slices(step, kv, reps=3):
         st = torch.empty(payload // 2, dtype=torch.int16, device="cuda")
         row = {"block_tokens": P, "payload_bytes": payload}
         for name, fn in (("pack", kv.kv_pack_paged), ("unpack", kv.kv_unpack_paged)):
-            fn(pg, k, v, 0, L, table, start, count, st, payload, s)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(s)
-            for _ in range(reps):
-                fn(pg, k, v, 0, L, table, start, count, st, payload, s)
-            e1.record(s)
-            torch.cuda.synchronize()
-            sec = e0.elapsed_time(e1) / 1000 / reps
-            row[name + "_us"] = round(sec * 1e6, 1)
-            row[name + "_hbm_GBps"] = round(2 * payload / sec / 1e9, 1)
-            row[name + "_frac_of_peak"] = round(2 * payload / sec / 1e9 / HBM_PEAK_GBPS, 4)
+            secs = rep_seconds(torch, lambda: fn(pg, k, v, 0, L, table, start, count, st, payload, s),
+                               s)
+            rate_entry(row, name, secs, 2 * payload, HBM_PEAK_GBPS, "_hbm_GBps")
         out[f"pages_{P}"] = row
         del k, v, st, table
         torch.cuda.empty_cache()
