@@ -27,8 +27,7 @@
  *    the KV bytes of B rows, S tokens, H heads of D dims, P bytes per element
  *    and N layers are 2 x B x S x H x D x P x N.
  *
- * Readings taken where the pages are silent (each is also listed in the
- * design notes):
+ * Readings taken where the pages are silent:
  *  - Cache layouts: key [L,B,H,D/8,Smax,8], value [L,B,H,Smax,D]; an element
  *    is 16 bits (fp16 or bf16, moved as raw bits, never converted).
  *  - Packed (staging) order: the selected elements in lexicographic order of
