@@ -185,6 +185,113 @@ __device__ __forceinline__ int lds_slot(int i, int c, int C)
 // (arrays of the uint4 struct end up in scratch).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// The same R steps, one wave per (layer, row, head) unit, through LDS: a
+// wave reads the unit's key chunk rows (R contiguous vectors each) and its
+// value run (R*C contiguous vectors), transposes the key through its own LDS
+// region, and writes step t's C key vectors and C value vectors (contiguous)
+// into slot t, four vectors in flight per lane.  Used when a unit's R*C
+// vectors fit the wave's LDS region.
+constexpr int kStepWaves = 4;                 // waves (units) per workgroup
+constexpr int kStepMaxVecs = 1024;            // R*C limit: 16 KiB of LDS per wave
+
+__device__ __forceinline__ int step_slot(int t, int c, int C)
+{
+    // token-major with the chunk XOR-ed by the token when C is a power of two,
+    // so the chunk-major writes of consecutive tokens spread over the banks
+    return (C & (C - 1)) == 0 ? t * C + (c ^ (t & (C - 1))) : t * C + c;
+}
+
+template <bool kPack>
+__global__ __launch_bounds__(kThreads) void copy_steps_lds(Geometry g, RowTable rt, int32_t n,
+                                                           int64_t slot_vecs, int64_t units)
+{
+    extern __shared__ u32x4 step_lds[];
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int32_t C = g.C;
+    const int32_t nv = n * C;                                   // vectors of K (and of V) per unit
+    u32x4 *lds = step_lds + wave * nv;
+    const int64_t u = (int64_t)blockIdx.x * kStepWaves + wave;
+    const bool active = u < units;
+    // unit u = ((li * B) + b) * H + h
+    const int32_t h = active ? (int32_t)(u % g.H) : 0;
+    const int32_t b = active ? (int32_t)((u / g.H) % g.B) : 0;
+    const int32_t li = active ? (int32_t)(u / ((int64_t)g.H * g.B)) : 0;
+    const int32_t s0 = rt.start[b];
+    const int64_t unit = ((int64_t)(g.l0 + li) * g.B + b) * g.H + h;
+    u32x4 *kc = (u32x4 *)(g.k + unit * C * g.Smax + s0);       // chunk c, step t: kc[c*Smax + t]
+    u32x4 *vc = (u32x4 *)(g.v + (unit * g.Smax + s0) * C);     // step t, chunk c: vc[t*C + c]
+    const int64_t blk = (int64_t)g.H * g.B * C;
+    u32x4 *ks = (u32x4 *)(g.stage + 2 * (int64_t)li * blk + ((int64_t)g.H * b + h) * C);
+    u32x4 *vs = ks + blk;                                       // step t, chunk c: ks[t*slot + c]
+    constexpr int kB = 4;                                       // vectors in flight per lane
+    if (kPack) {
+        if (active) {
+            for (int32_t e0 = lane; e0 < nv; e0 += 64 * kB) {   // key, chunk-major reads
+                u32x4 r[kB];
+#pragma unroll
+                for (int j = 0; j < kB; ++j) {
+                    const int32_t e = e0 + 64 * j, c = e / n, t = e - c * n;
+                    if (e < nv)
+                        r[j] = kc[(int64_t)c * g.Smax + t];
+                }
+#pragma unroll
+                for (int j = 0; j < kB; ++j) {
+                    const int32_t e = e0 + 64 * j, c = e / n, t = e - c * n;
+                    if (e < nv)
+                        lds[step_slot(t, c, C)] = r[j];
+                }
+            }
+            for (int32_t e0 = lane; e0 < nv; e0 += 64 * kB) {   // value: straight, per step
+                u32x4 r[kB];
+#pragma unroll
+                for (int j = 0; j < kB; ++j)
+                    if (e0 + 64 * j < nv)
+                        r[j] = vc[e0 + 64 * j];
+#pragma unroll
+                for (int j = 0; j < kB; ++j) {
+                    const int32_t e = e0 + 64 * j, t = e / C, c = e - t * C;
+                    if (e < nv)
+                        vs[t * slot_vecs + c] = r[j];
+                }
+            }
+        }
+        __syncthreads();
+        if (active)
+            for (int32_t e = lane; e < nv; e += 64) {           // key, token-major writes
+                const int32_t t = e / C, c = e - t * C;
+                ks[t * slot_vecs + c] = lds[step_slot(t, c, C)];
+            }
+    } else {
+        if (active) {
+            for (int32_t e0 = lane; e0 < nv; e0 += 64 * kB) {
+                u32x4 a[kB], d[kB];
+#pragma unroll
+                for (int j = 0; j < kB; ++j) {
+                    const int32_t e = e0 + 64 * j, t = e / C, c = e - t * C;
+                    if (e < nv) {
+                        a[j] = ks[t * slot_vecs + c];
+                        d[j] = vs[t * slot_vecs + c];
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < kB; ++j) {
+                    const int32_t e = e0 + 64 * j, t = e / C, c = e - t * C;
+                    if (e < nv) {
+                        lds[step_slot(t, c, C)] = a[j];
+                        vc[e] = d[j];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (active)
+            for (int32_t e = lane; e < nv; e += 64) {
+                const int32_t c = e / n, t = e - c * n;
+                kc[(int64_t)c * g.Smax + t] = lds[step_slot(t, c, C)];
+            }
+    }
+}
+
 // One tile = kThreads * PER vectors of K (and as many of V); TT = tile / C
 // tokens.  Element e = tid + p*kThreads of the tile is read as (chunk e/TT,
 // token e%TT) on the cache side (chunk-major) and as (token e/C, chunk e%C)
@@ -660,11 +767,21 @@ int launch_steps(bool pack, const Geometry &g0, const RowTable &rt, int32_t n,
         const int64_t payload = 2 * (int64_t)gl.nl * blk * 16 * n;
         const int64_t threads = (int64_t)gl.nl * per_layer;
         void *tok = profiling_enabled() ? profile_start(s) : nullptr;
-        const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads)), block(kThreads);
-        if (pack)
-            copy_steps<true><<<grid, block, 0, s>>>(gl, rt, n, slot_vecs);
-        else
-            copy_steps<false><<<grid, block, 0, s>>>(gl, rt, n, slot_vecs);
+        if ((int64_t)n * g0.C <= kStepMaxVecs) {
+            const int64_t units = (int64_t)gl.nl * g0.B * g0.H;
+            const dim3 grid((unsigned)((units + kStepWaves - 1) / kStepWaves)), block(kThreads);
+            const size_t lds = (size_t)kStepWaves * n * g0.C * sizeof(u32x4);
+            if (pack)
+                copy_steps_lds<true><<<grid, block, lds, s>>>(gl, rt, n, slot_vecs, units);
+            else
+                copy_steps_lds<false><<<grid, block, lds, s>>>(gl, rt, n, slot_vecs, units);
+        } else {
+            const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads)), block(kThreads);
+            if (pack)
+                copy_steps<true><<<grid, block, 0, s>>>(gl, rt, n, slot_vecs);
+            else
+                copy_steps<false><<<grid, block, 0, s>>>(gl, rt, n, slot_vecs);
+        }
         const hipError_t e = hipGetLastError();
         if (tok)
             profile_stop(tok, s, name, 2 * payload);
