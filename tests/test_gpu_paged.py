@@ -179,3 +179,33 @@ def test_gpt2_1p5b_from_a_page_pool(kv, P):
     oracle.unpack_paged(pd, Kp, Vp, 0, L, table, pos, np.ones(B, np.int32), new)
     torch.cuda.synchronize()
     assert np.array_equal(host(dk), Kp) and np.array_equal(host(dv), Vp), "decode step into the pool"
+
+
+def test_error_paths(kv):
+    """A pageable block table, a table that is too short for the ranges,
+    staging overlapping the table, and host memory as a pool are rejected
+    before anything is enqueued."""
+    import torch
+    L, NB, H, D, P = 2, 8, 2, 64, 16
+    note(f"paged error paths pool={(L, NB, H, D, P)}")
+    pg = kv.kv_paged_init(L, NB, H, D, P, 0)
+    n = L * NB * H * D * P
+    dk, dv = dev(synth.random_bits(n, 1)), dev(synth.random_bits(n, 2))
+    table = np.arange(8, dtype=np.int32).reshape(2, 4)
+    dt = dev_table(table)
+    need = kv.kv_paged_pack_bytes(pg, L, 2, [20, 30])
+    st = empty(need // 2 + 64)
+    with pytest.raises(kv.KvError) as e:                   # the table in pageable host memory
+        kv.kv_pack_paged(pg, dk, dv, 0, L, table, [0, 0], [20, 30], st, need)
+    assert e.value.status == kv.KV_EINVAL
+    with pytest.raises(kv.KvError) as e:                   # tokens past the table's 4 blocks
+        kv.kv_pack_paged(pg, dk, dv, 0, L, dt, [0, 40], [20, 30], st, need)
+    assert e.value.status == kv.KV_ERANGE
+    with pytest.raises(kv.KvError) as e:                   # staging on top of the value pool
+        kv.kv_pack_paged(pg, dk, dv, 0, L, dt, [0, 0], [20, 30], dv, need)
+    assert e.value.status == kv.KV_EINVAL
+    with pytest.raises(kv.KvError) as e:                   # host memory as the key pool
+        kv.kv_unpack_paged(pg, np.zeros(n, np.uint16), dv, 0, L, dt, [0, 0], [20, 30], st, need)
+    assert e.value.status == kv.KV_EINVAL
+    torch.cuda.synchronize()
+    assert np.all(host(st) == 0x7A7A), "a rejected call wrote staging"

@@ -175,3 +175,34 @@ def test_opt66b_slice_to_two_stages_by_two_ranks(kv):
             assert np.array_equal(dvv.view(L // 2, -1)[ll].cpu().numpy().view(np.uint16), ev), \
                 f"merged V {dst} layer {gl}"
         del st, dk, dvv
+
+
+def test_error_paths(kv):
+    """Host memory in place of a cache or staging, overlapping staging and a
+    short staging buffer are rejected before anything is enqueued."""
+    import torch
+    D, S = 64, 32
+    src, dst = (0, 2, 0, 2, 0, 2), (1, 1, 1, 1, 0, 2)
+    dims = oracle.part_dims(src, D, S)
+    note(f"stream_out/in error paths src={src} dst={dst}")
+    lay = kv.kv_layout_init(*dims, 0)
+    K, V = synth.cache_pair(dims, 3)
+    dk, dv = dev(K), dev(V)
+    need = kv.kv_stream_bytes(lay, src, dst, [4, 4])
+    st = empty(need // 2 + 64)
+    pageable = np.zeros(K.size, np.uint16)
+    with pytest.raises(kv.KvError) as e:                   # pageable host memory as the cache
+        kv.kv_stream_out(lay, src, pageable, dv, dst, [0, 0], [4, 4], st, need)
+    assert e.value.status == kv.KV_EINVAL
+    with pytest.raises(kv.KvError) as e:                   # staging inside the key cache
+        kv.kv_stream_out(lay, src, dk, dv, dst, [0, 0], [4, 4], dk, need)
+    assert e.value.status == kv.KV_EINVAL
+    with pytest.raises(kv.KvError) as e:                   # staging one vector short
+        kv.kv_stream_in(lay, src, dk, dv, dst, [0, 0], [4, 4], st, need - 16)
+    assert e.value.status == kv.KV_ESIZE
+    with pytest.raises(kv.KvError) as e:                   # layout of another partition
+        kv.kv_stream_out(lay, dst, dk, dv, src, [0, 0], [4, 4], st, need)
+    assert e.value.status == kv.KV_EINVAL
+    torch.cuda.synchronize()
+    assert np.all(host(st) == 0x7A7A), "a rejected call wrote staging"
+    assert np.array_equal(host(dk), K) and np.array_equal(host(dv), V)
