@@ -1033,6 +1033,13 @@ def main():
                        "compute_streams": args.compute_streams, "swap_calls": args.swap_calls,
                        "hw_queues": int(os.environ["GPU_MAX_HW_QUEUES"])},
             "roofline": roofline, "cpu_baseline": cpu, "detail": detail}
+    # the metric names two figures: the in-step pack/unpack rate of the busiest
+    # HBM kernel (and its share of the HBM peak), and the host-link rate (value)
+    line["metric_parts"] = {
+        "swap_host_link_GBps": line["value"],
+        "pack_unpack_GBps": roofline["achieved"] if roofline else None,
+        "pack_unpack_hbm_frac": roofline["frac"] if roofline else None,
+        "pack_unpack_kernel": roofline["kernel"] if roofline else None}
     print(json.dumps(line), flush=True)
 
 
