@@ -275,6 +275,56 @@ class HostBuffer:
     __del__ = close
 
 
+class TimingEvent:
+    """A HIP event for timing only: created with hipEventDisableSystemFence, so
+    recording it does not write back and invalidate the caches (a default
+    event does, which adds that cost to the interval it closes and slows the
+    work after it).  Same use as torch.cuda.Event(enable_timing=True)."""
+
+    _lib = None
+
+    def __init__(self):
+        import kv_cache_streaming_amd as kv
+        lib = TimingEvent._lib
+        if lib is None:
+            lib = kv._lib      # resolves to the HIP runtime the library and torch share
+            lib.hipEventCreateWithFlags.restype = ctypes.c_int
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.restype = ctypes.c_int
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.restype = ctypes.c_int
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.restype = ctypes.c_int
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            TimingEvent._lib = lib
+        e = ctypes.c_void_p()
+        r = lib.hipEventCreateWithFlags(ctypes.byref(e), 0x20000000)   # hipEventDisableSystemFence
+        if r != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed (hipError {r})")
+        self.e = e.value
+
+    def record(self, stream=None):
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        r = self._lib.hipEventRecord(self.e, s.cuda_stream)
+        if r != 0:
+            raise RuntimeError(f"hipEventRecord failed (hipError {r})")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both complete)."""
+        ms = ctypes.c_float()
+        r = self._lib.hipEventElapsedTime(ctypes.byref(ms), self.e, end.e)
+        if r != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed (hipError {r})")
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "e", None) and self._lib is not None:
+            self._lib.hipEventDestroy(self.e)
+            self.e = None
+
+
 def _bank(torch, nbytes):
     return torch.empty((nbytes + 1) // 2, dtype=torch.int16, device="cuda")
 
@@ -662,7 +712,7 @@ def hbm_copy_ceiling(torch, nbytes=1 << 30, reps=4):
     n = nbytes // 2
     b[:n].copy_(a[:n])
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = TimingEvent(), TimingEvent()
     e0.record()
     for r in range(reps):           # rotate over 4 GiB: more than the Infinity Cache
         b[r % 4 * n:(r % 4 + 1) * n].copy_(a[r % 4 * n:(r % 4 + 1) * n])
@@ -688,7 +738,7 @@ def rep_seconds(torch, fn, s=None, warm=5, reps=20):
             torch.cuda.synchronize()
             out.append(time.perf_counter() - t0)
         return out
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev = [TimingEvent() for _ in range(reps + 1)]
     ev[0].record(s)
     for i in range(reps):
         fn()
@@ -799,7 +849,7 @@ def decode_step_us(step, kv, reps=3):
         for _ in range(reps):
             ring.reset()
             torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a, b = TimingEvent(), TimingEvent()
             a.record(st)
             for pos in step.positions:
                 ring.push(Bc[0], Bc[1], pos, st)

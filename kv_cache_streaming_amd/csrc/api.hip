@@ -263,8 +263,12 @@ hipEvent_t take_event(ProfileState &ps)
         ps.pool.pop_back();
         return e;
     }
+    // Timing only: no system-scope fence when recorded.  A default event's
+    // record writes back and invalidates the caches, which would add that
+    // cost to every bracketed launch (and slow the work after it); ordering
+    // between streams never uses these events.
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) {
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
         (void)hipGetLastError();
         return nullptr;
     }
