@@ -1018,6 +1018,7 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     stats = {} if args.no_profile else kv.kv_profile_end()
+    window = None if args.no_profile else kv.kv_profile_last_window()
     ms = elapsed / args.steps * 1000
     link = step.link_bytes()
     value = link / (ms / 1000) / 1e9
@@ -1052,6 +1053,18 @@ def main():
 
     detail = {"kernels": kernels, "link_bytes_per_step": link,
               "link_peak_per_direction_GBps": PCIE_PEAK_GBPS}
+    together = None
+    if window and window["hbm_busy_ms"] > 0:
+        # kernels of different streams overlap: the union of their brackets is
+        # the time the pack/unpack kernels kept HBM busy, and their bytes over
+        # that time the rate they reached together
+        gbps = window["hbm_bytes"] / (window["hbm_busy_ms"] / 1000) / 1e9
+        together = {"busy_ms_per_step": round(window["hbm_busy_ms"] / args.steps, 3),
+                    "busy_share_of_step": round(window["hbm_busy_ms"] / (elapsed * 1000), 4),
+                    "algorithmic_bytes_per_step": window["hbm_bytes"] // args.steps,
+                    "GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                    "link_busy_share_of_step": round(window["link_busy_ms"] / (elapsed * 1000), 4)}
+        detail["hbm_kernels_together"] = together
     if not args.no_profile and not args.no_detail:
         detail["link_ceiling_GBps"] = {k: round(v, 2) for k, v in link_ceiling(torch).items()}
         if isinstance(step, StreamStep):
@@ -1083,13 +1096,16 @@ def main():
                        "compute_streams": args.compute_streams, "swap_calls": args.swap_calls,
                        "hw_queues": int(os.environ["GPU_MAX_HW_QUEUES"])},
             "roofline": roofline, "cpu_baseline": cpu, "detail": detail}
-    # the metric names two figures: the in-step pack/unpack rate of the busiest
-    # HBM kernel (and its share of the HBM peak), and the host-link rate (value)
+    # the metric names two figures: the in-step pack/unpack rate (of the
+    # busiest HBM kernel, and of all of them together, with their shares of
+    # the HBM peak) and the host-link rate (value)
     line["metric_parts"] = {
         "swap_host_link_GBps": line["value"],
         "pack_unpack_GBps": roofline["achieved"] if roofline else None,
         "pack_unpack_hbm_frac": roofline["frac"] if roofline else None,
-        "pack_unpack_kernel": roofline["kernel"] if roofline else None}
+        "pack_unpack_kernel": roofline["kernel"] if roofline else None,
+        "pack_unpack_together_GBps": together["GBps"] if together else None,
+        "pack_unpack_together_hbm_frac": together["frac_of_peak"] if together else None}
     print(json.dumps(line), flush=True)
 
 

@@ -528,6 +528,27 @@ typedef struct kv_kernel_stat {
 int kv_profile_begin(void);
 int kv_profile_end(kv_kernel_stat *out, int32_t max);
 
+/* The window kv_profile_end last closed, all streams together.  Kernels of
+ * different streams run at the same time, so per-kernel durations do not
+ * add up to the GPU time the path took; these are the unions of the
+ * bracketed intervals instead: `hbm_busy_ms` is the time during which at
+ * least one pack or unpack kernel ran and `hbm_bytes` the algorithmic bytes
+ * those kernels moved (their rate together is hbm_bytes / hbm_busy_ms);
+ * `link_*` the same for the link-copy kernels (bytes crossing the host
+ * link).  `span_ms` runs from the first bracket's start to the last one's
+ * end.  All zero when nothing was bracketed.  KV_EINVAL for a NULL `out`. */
+typedef struct kv_profile_window {
+    double span_ms;
+    double hbm_busy_ms;
+    int64_t hbm_bytes;
+    int64_t hbm_launches;
+    double link_busy_ms;
+    int64_t link_bytes;
+    int64_t link_launches;
+} kv_profile_window;
+
+int kv_profile_last_window(kv_profile_window *out);
+
 /* Thread-local text of the last error; never NULL. */
 const char *kv_last_error(void);
 int kv_version(void);

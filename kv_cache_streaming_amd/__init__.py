@@ -81,6 +81,13 @@ class kv_kernel_stat(ctypes.Structure):
                 ("ms", ctypes.c_double), ("bytes", ctypes.c_int64)]
 
 
+class kv_profile_window(ctypes.Structure):
+    _fields_ = [("span_ms", ctypes.c_double), ("hbm_busy_ms", ctypes.c_double),
+                ("hbm_bytes", ctypes.c_int64), ("hbm_launches", ctypes.c_int64),
+                ("link_busy_ms", ctypes.c_double), ("link_bytes", ctypes.c_int64),
+                ("link_launches", ctypes.c_int64)]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -141,6 +148,7 @@ _SIGNATURES = {
     "kv_ring_reset": (ctypes.c_int, [_P]),
     "kv_profile_begin": (ctypes.c_int, []),
     "kv_profile_end": (ctypes.c_int, [ctypes.POINTER(kv_kernel_stat), _I32]),
+    "kv_profile_last_window": (ctypes.c_int, [ctypes.POINTER(kv_profile_window)]),
 }
 
 
@@ -694,3 +702,12 @@ def kv_profile_end(max_entries: int = 16):
     n = _check(_lib.kv_profile_end(arr, max_entries), "kv_profile_end")
     return {arr[i].name.decode(): (arr[i].launches, arr[i].ms, arr[i].bytes)
             for i in range(min(n, max_entries))}
+
+
+def kv_profile_last_window() -> dict:
+    """Union of the bracketed intervals of the window kv_profile_end last
+    closed: {span_ms, hbm_busy_ms, hbm_bytes, hbm_launches, link_busy_ms,
+    link_bytes, link_launches}."""
+    w = kv_profile_window()
+    _check(_lib.kv_profile_last_window(ctypes.byref(w)), "kv_profile_last_window")
+    return {name: getattr(w, name) for name, _ in kv_profile_window._fields_}

@@ -7,6 +7,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 namespace kvs {
@@ -248,7 +249,30 @@ struct ProfileState {
     bool on = false;
     std::vector<Pending> pending;
     std::vector<hipEvent_t> pool;
+    kv_profile_window last{};
 };
+
+// Length of the union of [start, end) intervals (sorted in place).
+double union_ms(std::vector<std::pair<double, double>> &iv)
+{
+    std::sort(iv.begin(), iv.end());
+    double total = 0.0, lo = 0.0, hi = 0.0;
+    bool open = false;
+    for (const auto &x : iv) {
+        if (open && x.first <= hi) {
+            hi = std::max(hi, x.second);
+            continue;
+        }
+        if (open)
+            total += hi - lo;
+        lo = x.first;
+        hi = x.second;
+        open = true;
+    }
+    if (open)
+        total += hi - lo;
+    return total;
+}
 
 ProfileState &prof()
 {
@@ -501,15 +525,32 @@ int kv_profile_end(kv_kernel_stat *out, int32_t max)
     ps.on = false;
     std::vector<kv_kernel_stat> stats;
     int status = KV_OK;
+    // every bracket's interval, as offsets from the first bracket's start
+    std::vector<std::pair<double, double>> hbm_iv, link_iv;
+    kv_profile_window win{};
+    double first = 0.0, last = 0.0;
     for (auto &p : ps.pending) {
-        float ms = 0.f;
+        float ms = 0.f, t0 = 0.f;
         hipError_t e = hipEventSynchronize(p.b);
         if (e == hipSuccess)
             e = hipEventElapsedTime(&ms, p.a, p.b);
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&t0, ps.pending.front().a, p.a);
         if (e != hipSuccess) {
             status = hip_fail(e, "kv_profile_end");
             (void)hipGetLastError();
         }
+        const bool link = p.name.compare(0, 9, "link_copy") == 0;
+        (link ? link_iv : hbm_iv).emplace_back((double)t0, (double)t0 + ms);
+        if (link) {
+            win.link_bytes += p.bytes;
+            win.link_launches += 1;
+        } else {
+            win.hbm_bytes += p.bytes;
+            win.hbm_launches += 1;
+        }
+        first = std::min(first, (double)t0);
+        last = std::max(last, (double)t0 + ms);
         auto it = std::find_if(stats.begin(), stats.end(), [&](const kv_kernel_stat &s) {
             return p.name == s.name;
         });
@@ -526,12 +567,28 @@ int kv_profile_end(kv_kernel_stat *out, int32_t max)
         ps.pool.push_back(p.a);
         ps.pool.push_back(p.b);
     }
+    if (!ps.pending.empty()) {
+        win.span_ms = last - first;
+        win.hbm_busy_ms = union_ms(hbm_iv);
+        win.link_busy_ms = union_ms(link_iv);
+    }
+    ps.last = win;
     ps.pending.clear();
     if (status != KV_OK)
         return status;
     for (int32_t i = 0; out && i < max && i < (int32_t)stats.size(); ++i)
         out[i] = stats[i];
     return (int)stats.size();
+}
+
+int kv_profile_last_window(kv_profile_window *out)
+{
+    if (!out)
+        return set_error(KV_EINVAL, "output pointer is NULL");
+    ProfileState &ps = prof();
+    std::lock_guard<std::mutex> g(ps.mu);
+    *out = ps.last;
+    return KV_OK;
 }
 
 }  // extern "C"

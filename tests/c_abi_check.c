@@ -40,6 +40,13 @@ int main(void)
     kv_ack_restart_point(a, &j, &t);
     printf("restart_point %d %lld\n", j, (long long)t);
     kv_acklog_destroy(a);
+    kv_profile_window win;
+    win.span_ms = -1.0;
+    win.hbm_launches = -1;
+    const int win_st = kv_profile_last_window(&win);
+    const int win_null = kv_profile_last_window(NULL);
+    printf("profile_window %d %.1f %lld %d\n", win_st, win.span_ms, (long long)win.hbm_launches,
+           win_null);
     printf("version %d\n", kv_version());
     return 0;
 }

@@ -493,3 +493,52 @@ def test_profiler_counts_launches(kv):
     assert stats["unpack_tiles"][0] == 1
     assert stats["pack_tiles"][2] == 2 * 2 * (2 * 2 * 2 * 64 * 256)
     assert all(v[1] > 0 for v in stats.values())
+    win = kv.kv_profile_last_window()
+    assert win["hbm_launches"] == 3 and win["link_launches"] == 0
+    assert win["hbm_bytes"] == sum(v[2] for v in stats.values())
+    total = sum(v[1] for v in stats.values())
+    # one stream: the brackets follow one another, so their union is at most
+    # their sum and at least the longest of them, and fits in the span
+    assert max(v[1] for v in stats.values()) <= win["hbm_busy_ms"] <= total * (1 + 1e-6)
+    assert win["hbm_busy_ms"] <= win["span_ms"] * (1 + 1e-6)
+    assert win["link_busy_ms"] == 0.0 and win["link_bytes"] == 0
+
+
+def test_profile_window_overlapping_streams(kv):
+    """Two streams packing at once, and a ring flush's link copy: the window
+    holds the union of the brackets of each class."""
+    import torch
+    dims = (4, 4, 4, 128, 1024)
+    L, B, H, D, S = dims
+    K, V = synth.cache_pair(dims, 53)
+    lay = kv.kv_layout_init(*dims, 0)
+    dk, dv = dev(K), dev(V)
+    n = kv.kv_pack_bytes(lay, L, [S] * B)
+    st = [empty(n // 2), empty(n // 2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    slot = kv.kv_pack_bytes(lay, L, None, 1)
+    hostbuf = pinned(2 * slot // 2)
+    ring = kv.KvRing(lay, 2, empty(2 * slot // 2), empty(2 * slot // 2), hostbuf,
+                     copy_stream=torch.cuda.Stream(), transport=1)
+    torch.cuda.synchronize()
+    kv.kv_profile_begin()
+    for i in range(3):
+        for j in range(2):
+            kv.kv_pack_tokens(lay, dk, dv, 0, L, [0] * B, [S] * B, st[j], stream=streams[j])
+    ring.push(dk, dv, [3] * B)
+    ring.push(dk, dv, [4] * B)      # fills the bank: one link copy
+    stats = kv.kv_profile_end()
+    torch.cuda.synchronize()
+    win = kv.kv_profile_last_window()
+    hbm = {k: v for k, v in stats.items() if not k.startswith("link_copy")}
+    link = {k: v for k, v in stats.items() if k.startswith("link_copy")}
+    assert win["hbm_launches"] == sum(v[0] for v in hbm.values()) == 8
+    assert win["link_launches"] == sum(v[0] for v in link.values()) == 1
+    assert win["hbm_bytes"] == sum(v[2] for v in hbm.values())
+    assert win["link_bytes"] == 2 * slot
+    assert max(v[1] for v in hbm.values()) / max(v[0] for v in hbm.values()) <= \
+        win["hbm_busy_ms"] * (1 + 1e-6)
+    assert win["hbm_busy_ms"] <= sum(v[1] for v in hbm.values()) * (1 + 1e-6)
+    assert 0 < win["link_busy_ms"] <= win["span_ms"] * (1 + 1e-6)
+    assert win["hbm_busy_ms"] <= win["span_ms"] * (1 + 1e-6)
+    ring.close()
