@@ -286,16 +286,19 @@ typedef struct kv_swap kv_swap;
  *                      host<->device kinds (the runtime picks the engine).
  *   KV_XFER_DMA     -- both directions by hipMemcpyAsync between the bank and
  *                      the host buffer's device-visible address with
- *                      hipMemcpyDeviceToDeviceNoCU: the DMA engines, never the
- *                      compute units.
+ *                      hipMemcpyDeviceToDeviceNoCU, which asks the runtime
+ *                      for the DMA engines (it may still run a copy as its
+ *                      own copy kernel, and it picks the engine).
  *   KV_XFER_DMA_OUT -- device->host as KV_XFER_DMA, host->device as
  *                      KV_XFER_RUNTIME.
- * On MI355X a DMA copy that must wait for a kernel on another stream pays a
- * long hand-off per dependency, which a layer-by-layer pipeline pays once per
- * layer; a kernel copy waits through a queue barrier instead.  GPU-initiated
- * reads of host memory, however, keep the two link directions from running
- * at once, while DMA reads do not -- hence AUTO.  All three produce identical
- * bytes. */
+ * Measured on MI355X: DMA copies in both directions at once run at full
+ * duplex when one direction moves large (bank-sized) chunks, but fall to
+ * about one direction's rate when both move small dependent chunks (one
+ * layer each), and device->host DMA copies can drop to a fraction of the
+ * link for the rest of the process; GPU-initiated reads of host memory keep
+ * the two directions from running at once.  GPU-initiated writes (the
+ * link-copy kernel) and DMA reads overlap in every pattern -- hence AUTO.
+ * All transports produce identical bytes. */
 typedef enum kv_transport {
     KV_XFER_AUTO = 0,
     KV_XFER_KERNEL = 1,
