@@ -462,10 +462,12 @@ class SwapStep:
                                transport)
         self.packed = [torch.cuda.Event() for _ in range(L)]
         # every microbatch's host image, written through a swap-out of a slot
-        # filled with that microbatch's values
+        # filled with that microbatch's values; the slots end as round 0
+        # expects them: microbatch 0 in slot 0 (computing), N-1 in slot 1
+        # (to be swapped out while 1 comes in)
         import synth
-        for x in range(self.N):
-            k, v = self.slots[x % 2]
+        for x in list(range(1, self.N)) + [0]:
+            k, v = self.slots[0 if x == 0 else 1]
             synth.fill_device_cache(k, w.value_seed + 40 * x, w.dtype)
             synth.fill_device_cache(v, w.value_seed + 40 * x + 1, w.dtype)
             torch.cuda.synchronize()
