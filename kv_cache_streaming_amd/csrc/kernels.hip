@@ -640,9 +640,9 @@ int tile_tokens_for(int32_t C)
 // Device->host stores go through a bounds-checked buffer resource with the
 // system-coherent, non-temporal cache policy (sc0 sc1 nt), from a small grid
 // (8 workgroups by default).  Measured on MI355X: that keeps the host link at
-// ~56 GB/s while leaving co-running HBM kernels at their own speed; ordinary
-// stores to host memory from many workgroups hold up other kernels' HBM
-// traffic several-fold.  Host->device reads use non-temporal loads.
+// ~56 GB/s while co-running HBM kernels lose about a third of their speed;
+// ordinary stores to host memory, or many workgroups, hold up other kernels'
+// HBM traffic several-fold.  Host->device reads use non-temporal loads.
 constexpr int kHostStorePolicy = 1 | 2 | 16;   // sc0 | nt | sc1
 
 template <bool kToHost>
