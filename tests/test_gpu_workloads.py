@@ -293,6 +293,45 @@ def test_bloom_slice_microbatch_swap(kv):
     ei.close()
 
 
+def test_bloom_slice_one_call_past_4gib(kv):
+    """One pack and one unpack call over all 10 layers of the BLOOM slice with
+    ragged rows: a 13.9 GB packed buffer, so every offset past 4 GiB in the
+    staging buffer is exercised in a single launch sequence."""
+    import torch
+    w = synth.WORKLOADS["bloom-176b-10l"]
+    L, B, H, D, S = w.dims
+    lay = kv.kv_layout_init(*w.dims, w.dtype)
+    rng = np.random.default_rng(4)
+    count = rng.integers(1200, S + 1, size=B).astype(np.int32)
+    start = np.array([int(rng.integers(0, S - c + 1)) for c in count], np.int32)
+    total = kv.kv_pack_bytes(lay, L, count)
+    assert total > 1 << 32
+    note(f"workload {w.name} one call of {total} bytes, start={start.tolist()} count={count.tolist()}")
+    src = device_cache(w, w.value_seed + 7)
+    st = torch.full((total // 2 + 64,), 0x7A7A, dtype=torch.int16, device="cuda")
+    kv.kv_pack_tokens(lay, src[0], src[1], 0, L, start, count, st, total)
+    torch.cuda.synchronize()
+    per = total // 2 // L
+    got = st.view(-1)
+    assert np.all(got[total // 2:].cpu().numpy() == 0x7A7A), "wrote past the packed bytes"
+    for l in (0, L // 2, L - 1):
+        Kl, Vl = layer_host(src[0], w, l), layer_host(src[1], w, l)
+        want = oracle.pack(one_layer(w), Kl, Vl, 0, 1, start, count)
+        assert np.array_equal(got[l * per:(l + 1) * per].cpu().numpy().view(np.uint16), want), \
+            f"pack layer {l}"
+    dst = (torch.full_like(src[0], 0x1F1F), torch.full_like(src[1], 0x1F1F))
+    del src
+    kv.kv_unpack_tokens(lay, dst[0], dst[1], 0, L, start, count, st, total)
+    torch.cuda.synchronize()
+    for l in (0, L - 1):
+        ek = np.full(B * H * D * S, 0x1F1F, np.uint16)
+        ev = ek.copy()
+        oracle.unpack(one_layer(w), ek, ev, 0, 1, start, count,
+                      got[l * per:(l + 1) * per].cpu().numpy().view(np.uint16))
+        assert np.array_equal(layer_host(dst[0], w, l), ek), f"unpack K layer {l}"
+        assert np.array_equal(layer_host(dst[1], w, l), ev), f"unpack V layer {l}"
+
+
 def test_gqa_100k_long_context(kv):
     """bf16, Smax = 100000, ragged rows: 4096-token prompt chunks per layer, 64
     ragged decode steps into a ring of 16, swap-out/in of the longest row."""
