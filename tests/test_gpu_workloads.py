@@ -332,6 +332,44 @@ def test_bloom_slice_one_call_past_4gib(kv):
         assert np.array_equal(layer_host(dst[1], w, l), ev), f"unpack V layer {l}"
 
 
+@pytest.mark.parametrize("transport", [1, 0])
+def test_swap_through_banks_past_1gib(kv, transport):
+    """Swap-out and swap-in of every GPT-2-1.5B layer and position through
+    1.5 GiB banks (30 layers per chunk): each link copy of a chunk is cut into
+    launches of at most 1 GiB, in both directions with the kernel transport."""
+    import torch
+    w = synth.WORKLOADS["gpt2-1.5b"]
+    L, B = w.L, w.B
+    note(f"workload {w.name} 1.5 GiB banks transport={transport}")
+    lay = kv.kv_layout_init(*w.dims, w.dtype)
+    full = [w.Smax] * B
+    total = kv.kv_pack_bytes(lay, L, full)
+    sb = 1536 * MiB
+    plan = kv.kv_swap_plan(lay, 0, L, [0] * B, full, sb)
+    assert [c["layer_count"] for c in plan] == [30, 18]
+    src = device_cache(w, w.value_seed + 11)
+    copy_out, copy_in = torch.cuda.Stream(), torch.cuda.Stream()
+    eo = kv.KvSwap(lay, bank(sb), bank(sb), sb, copy_out, transport)
+    ei = kv.KvSwap(lay, bank(sb), bank(sb), sb, copy_in, transport)
+    host = pinned(total // 2 + 64)
+    done = torch.cuda.Event()
+    eo.swap_out(src[0], src[1], 0, L, [0] * B, full, host, total, None, done)
+    done.synchronize()
+    hv = pinned_host_view(host)
+    assert np.all(hv[total // 2:] == 0x5C5C), "wrote past the host image"
+    per = total // 2 // L
+    for l in (0, 29, 30, L - 1):
+        want = oracle.pack(one_layer(w), layer_host(src[0], w, l), layer_host(src[1], w, l), 0, 1,
+                           [0] * B, full)
+        assert np.array_equal(hv[l * per:(l + 1) * per], want), f"swap-out layer {l}"
+    dk, dv = torch.full_like(src[0], 0x2E2E), torch.full_like(src[1], 0x2E2E)
+    ei.swap_in(dk, dv, 0, L, [0] * B, full, host, total)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, src[0]) and torch.equal(dv, src[1]), "swap-in restores every position"
+    eo.close()
+    ei.close()
+
+
 def test_gqa_100k_long_context(kv):
     """bf16, Smax = 100000, ragged rows: 4096-token prompt chunks per layer, 64
     ragged decode steps into a ring of 16, swap-out/in of the longest row."""
