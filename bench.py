@@ -78,7 +78,8 @@ def parse_args():
     ap.add_argument("--workload", default="gpt2-1.5b", choices=sorted(STEPS),
                     help="gpt2-1.5b is the headline; the others measure the remaining workloads")
     ap.add_argument("--swap-bank-mib", type=int, default=256)
-    ap.add_argument("--transport", choices=("auto", "kernel", "runtime", "dma", "dma_out"), default="auto",
+    ap.add_argument("--transport", choices=("auto", "kernel", "runtime", "dma", "dma_out", "engine"),
+                    default="auto",
                     help="bank<->host transfers (see kv_transport in include/kvstream.h)")
     ap.add_argument("--ring-gather", choices=("flush", "each"), default="flush",
                     help="rings pack a bank's decode steps at flush time in one pass (flush) or "
@@ -994,7 +995,8 @@ def main():
     RING_GATHER = {"flush": kv.KV_RING_GATHER_AT_FLUSH, "each": kv.KV_RING_GATHER_EACH_STEP}[
         args.ring_gather]
     step = STEPS[w.name](w, args.swap_bank_mib << 20,
-                {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3, "dma_out": 4}[args.transport])
+                {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3, "dma_out": 4,
+                 "engine": 5}[args.transport])
     torch.cuda.synchronize()
 
     if args.calibrate_copy_mib:

@@ -291,6 +291,15 @@ typedef struct kv_swap kv_swap;
  *                      own copy kernel, and it picks the engine).
  *   KV_XFER_DMA_OUT -- device->host as KV_XFER_DMA, host->device as
  *                      KV_XFER_RUNTIME.
+ *   KV_XFER_ENGINE  -- device->host on one named DMA engine (one of the
+ *                      engines 0-3 that write host memory at full speed,
+ *                      chosen per handle through the HSA runtime), submitted
+ *                      by a worker thread of the handle once the copy stream
+ *                      has reached the copy, with the stream then waiting on
+ *                      the copy's completion signal; host->device as
+ *                      KV_XFER_RUNTIME.  Needs stream memory waits
+ *                      (KV_EINVAL at create time otherwise).  Destroying the
+ *                      handle waits until its copies are done.
  * Measured on MI355X: DMA copies in both directions at once run at full
  * duplex when one direction moves large (bank-sized) chunks, but fall to
  * about one direction's rate when both move small dependent chunks (one
@@ -304,7 +313,8 @@ typedef enum kv_transport {
     KV_XFER_KERNEL = 1,
     KV_XFER_RUNTIME = 2,
     KV_XFER_DMA = 3,
-    KV_XFER_DMA_OUT = 4
+    KV_XFER_DMA_OUT = 4,
+    KV_XFER_ENGINE = 5
 } kv_transport;
 
 /* bank0/bank1: caller-owned device banks of bank_bytes each; `copy`: the

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libkvstream.so")
 
 KV_OK, KV_EINVAL, KV_ERANGE, KV_ESIZE, KV_EHIP, KV_EBUSY = 0, -1, -2, -3, -4, -5
 KV_F16, KV_BF16 = 0, 1
-KV_XFER_AUTO, KV_XFER_KERNEL, KV_XFER_RUNTIME, KV_XFER_DMA, KV_XFER_DMA_OUT = 0, 1, 2, 3, 4
+KV_XFER_AUTO, KV_XFER_KERNEL, KV_XFER_RUNTIME, KV_XFER_DMA, KV_XFER_DMA_OUT, KV_XFER_ENGINE = 0, 1, 2, 3, 4, 5
 KV_RING_GATHER_EACH_STEP, KV_RING_GATHER_AT_FLUSH = 0, 1
 KV_MAX_ROWS = 256
 STATUS_NAMES = {0: "KV_OK", -1: "KV_EINVAL", -2: "KV_ERANGE", -3: "KV_ESIZE",

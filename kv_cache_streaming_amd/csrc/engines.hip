@@ -151,11 +151,13 @@ int create_events(hipEvent_t *ev, int n)
 // One contiguous transfer between a bank and pinned host memory on `s`, with
 // the engine's transport.  `host_dev` is the device-visible address of the
 // host side (used by the link-copy kernel).
-int transfer(int32_t transport, void *bank, void *host, void *host_dev, int64_t bytes,
-             bool to_host, hipStream_t s)
+int transfer(int32_t transport, EngineCopier *copier, void *bank, void *host, void *host_dev,
+             int64_t bytes, bool to_host, hipStream_t s)
 {
     if (bytes <= 0)
         return KV_OK;
+    if (transport == KV_XFER_ENGINE && to_host)
+        return engine_copy_to_host(copier, host, bank, bytes, s);
     const bool kernel = transport == KV_XFER_KERNEL || (transport == KV_XFER_AUTO && to_host);
     if (kernel)
         return to_host ? launch_link_copy(host_dev, bank, bytes, true, s)
@@ -172,7 +174,7 @@ int transfer(int32_t transport, void *bank, void *host, void *host_dev, int64_t 
 
 int check_transport(int32_t transport)
 {
-    if (transport < KV_XFER_AUTO || transport > KV_XFER_DMA_OUT)
+    if (transport < KV_XFER_AUTO || transport > KV_XFER_ENGINE)
         return set_error(KV_EINVAL, "transport %d is not a kv_transport", transport);
     return KV_OK;
 }
@@ -185,6 +187,7 @@ struct kv_swap {
     int64_t bank_bytes;
     hipStream_t copy;
     int32_t transport;
+    EngineCopier *copier;        // KV_XFER_ENGINE: the device->host DMA engine
     hipEvent_t ev[4];            // free0, free1, filled0, filled1
     bool free_valid[2];
     int next;
@@ -202,6 +205,7 @@ struct kv_ring {
     void *host_dev;              // device-visible address of `host`
     hipStream_t copy;
     int32_t transport;
+    EngineCopier *copier;        // KV_XFER_ENGINE: the device->host DMA engine
     int64_t slot_bytes;
     int64_t steps, flushed;
     std::vector<int32_t> pos;    // steps * B positions, in step order
@@ -259,7 +263,7 @@ int swap_out_rows(kv_swap *e, const void *k, const void *v, int32_t l0, int32_t 
             (st = wait(e->copy, e->filled_ev(bk), "swap-out copy wait")))
             return st;
         for (int p = 0; p < c.pieces; ++p)
-            if ((st = transfer(e->transport, (char *)e->bank[bk] + c.bank_off[p],
+            if ((st = transfer(e->transport, e->copier, (char *)e->bank[bk] + c.bank_off[p],
                                (char *)host + c.host_off[p], (char *)host_dev + c.host_off[p],
                                c.bytes[p], true, e->copy)))
                 return st;
@@ -305,7 +309,14 @@ int kv_swap_create(kv_swap **out, const kv_layout *lay, void *bank0, void *bank1
     e->transport = transport;
     e->free_valid[0] = e->free_valid[1] = false;
     e->next = 0;
+    e->copier = nullptr;
     if ((st = create_events(e->ev, 4))) {
+        delete e;
+        return st;
+    }
+    if (transport == KV_XFER_ENGINE && (st = engine_copier_create(&e->copier))) {
+        for (hipEvent_t ev : e->ev)
+            (void)hipEventDestroy(ev);
         delete e;
         return st;
     }
@@ -317,6 +328,7 @@ int kv_swap_destroy(kv_swap *e)
 {
     if (!e)
         return KV_OK;
+    engine_copier_destroy(e->copier);
     for (hipEvent_t ev : e->ev)
         (void)hipEventDestroy(ev);
     delete e;
@@ -396,7 +408,7 @@ int kv_swap_in(kv_swap *e, void *k, void *v, int32_t layer_begin, int32_t layer_
         if (e->free_valid[bk] && (st = wait(e->copy, e->free_ev(bk), "swap-in bank wait")))
             return st;
         for (int p = 0; p < c.pieces; ++p)
-            if ((st = transfer(e->transport, (char *)e->bank[bk] + c.bank_off[p],
+            if ((st = transfer(e->transport, e->copier, (char *)e->bank[bk] + c.bank_off[p],
                                (char *)host + c.host_off[p], (char *)host_dev + c.host_off[p],
                                c.bytes[p], false, e->copy)))
                 return st;
@@ -506,7 +518,14 @@ int kv_ring_create(kv_ring **out, const kv_layout *lay, int32_t R, void *bank0, 
     r->gather = KV_RING_GATHER_EACH_STEP;
     r->wait_needed[0] = r->wait_needed[1] = false;
     r->free_valid[0] = r->free_valid[1] = false;
+    r->copier = nullptr;
     if ((st = create_events(r->ev, 4))) {
+        delete r;
+        return st;
+    }
+    if (transport == KV_XFER_ENGINE && (st = engine_copier_create(&r->copier))) {
+        for (hipEvent_t ev : r->ev)
+            (void)hipEventDestroy(ev);
         delete r;
         return st;
     }
@@ -518,6 +537,7 @@ int kv_ring_destroy(kv_ring *r)
 {
     if (!r)
         return KV_OK;
+    engine_copier_destroy(r->copier);
     for (hipEvent_t ev : r->ev)
         (void)hipEventDestroy(ev);
     for (auto &p : r->landing)
@@ -605,7 +625,7 @@ int ring_flush_range(kv_ring *r, int64_t first, int64_t n, hipStream_t compute)
     if ((st = record(r->filled_ev(bk), compute, "ring filled")) ||
         (st = wait(r->copy, r->filled_ev(bk), "ring flush wait")))
         return st;
-    if ((st = transfer(r->transport, (char *)r->bank[bk] + off,
+    if ((st = transfer(r->transport, r->copier, (char *)r->bank[bk] + off,
                        (char *)r->host + first * r->slot_bytes,
                        (char *)r->host_dev + first * r->slot_bytes, n * r->slot_bytes, true,
                        r->copy)))
@@ -725,7 +745,7 @@ int ring_restore_n(kv_ring *r, void *k, void *v, int64_t n_steps, hipStream_t co
         const int bk = (int)(g & 1);
         if (r->free_valid[bk] && (st = wait(r->copy, r->free_ev(bk), "ring restore bank wait")))
             return st;
-        if ((st = transfer(r->transport, r->bank[bk], (char *)r->host + j0 * r->slot_bytes,
+        if ((st = transfer(r->transport, r->copier, r->bank[bk], (char *)r->host + j0 * r->slot_bytes,
                            (char *)r->host_dev + j0 * r->slot_bytes, n * r->slot_bytes, false,
                            r->copy)))
             return st;

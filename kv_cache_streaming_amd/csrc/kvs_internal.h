@@ -105,6 +105,19 @@ int launch_link_copy(void *dst, const void *src, int64_t bytes, bool to_host, hi
 // KV_OK or KV_EINVAL.
 int host_device_address(const void *host, int64_t bytes, void **dev);
 
+// ---- device->host copies on a chosen DMA engine (engine_copy.hip) ----
+struct EngineCopier;
+// A copier on one of the DMA engines that write host memory at full speed,
+// for the current device; KV_EINVAL when the device or runtime cannot.
+int engine_copier_create(EngineCopier **out);
+// Waits until every copy is submitted and every stream is past it.
+void engine_copier_destroy(EngineCopier *c);
+// Enqueue on `s` a copy of `bytes` from device memory to pinned host memory
+// that starts once everything enqueued on `s` so far has run, and that later
+// work on `s` waits for.
+int engine_copy_to_host(EngineCopier *c, void *dst_host, const void *src_dev, int64_t bytes,
+                        hipStream_t s);
+
 // ---- profiling (api.hip) ----
 bool profiling_enabled();
 // Begin/end a bracketed launch; `tok` is opaque state handed back to profile_end.

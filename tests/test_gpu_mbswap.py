@@ -26,7 +26,7 @@ def kv():
     return kv
 
 
-@pytest.mark.parametrize("N,transport", [(4, 0), (4, 3), (3, 0), (2, 0)])
+@pytest.mark.parametrize("N,transport", [(4, 0), (4, 3), (4, 5), (3, 0), (2, 0)])
 def test_round_robin_schedule(kv, N, transport):
     import torch
     dims = (3, 2, 2, 64, 48)

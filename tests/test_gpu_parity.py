@@ -234,7 +234,7 @@ def test_error_paths(kv):
     assert ring.steps == 3
 
 
-TRANSPORTS = [0, 1, 2, 3]   # KV_XFER_AUTO, KV_XFER_KERNEL, KV_XFER_RUNTIME, KV_XFER_DMA
+TRANSPORTS = [0, 1, 2, 3, 5]   # KV_XFER_AUTO, _KERNEL, _RUNTIME, _DMA, _ENGINE
 
 
 def run_ring(kv, dims, R, positions, seed, bits=True, mutate=False, delay_cycles=0, transport=0,

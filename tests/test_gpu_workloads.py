@@ -332,7 +332,7 @@ def test_bloom_slice_one_call_past_4gib(kv):
         assert np.array_equal(layer_host(dst[1], w, l), ev), f"unpack V layer {l}"
 
 
-@pytest.mark.parametrize("transport", [1, 0])
+@pytest.mark.parametrize("transport", [1, 0, 5])
 def test_swap_through_banks_past_1gib(kv, transport):
     """Swap-out and swap-in of every GPT-2-1.5B layer and position through
     1.5 GiB banks (30 layers per chunk): each link copy of a chunk is cut into
