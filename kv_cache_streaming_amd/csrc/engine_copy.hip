@@ -133,15 +133,14 @@ struct Slot {
 
 struct EngineCopier {
     HsaAgents agents;
-    uint32_t engine[2] = {0, 0};       // a large copy is split in two halves, one per engine
+    uint32_t engine = 0;
     std::vector<Slot *> slots;
 };
 
-// Pairs of engines whose two halves of a device->host copy together reach
-// the link's rate on MI355X (engines 0 and 1 together do not).
-constexpr uint32_t kEnginePairs[2][2] = {{HSA_AMD_SDMA_ENGINE_0, HSA_AMD_SDMA_ENGINE_2},
-                                         {HSA_AMD_SDMA_ENGINE_1, HSA_AMD_SDMA_ENGINE_3}};
-constexpr int64_t kSplitBytes = 4 << 20;   // smaller copies run on the first engine alone
+// Engines whose host writes run at full speed on MI355X.  (Splitting a copy
+// over two of them was measured and dropped: it slowed the steps by 2-10%.)
+constexpr uint32_t kFastEngines[] = {HSA_AMD_SDMA_ENGINE_0, HSA_AMD_SDMA_ENGINE_1,
+                                     HSA_AMD_SDMA_ENGINE_2, HSA_AMD_SDMA_ENGINE_3};
 
 int engine_copier_create(EngineCopier **out)
 {
@@ -154,10 +153,18 @@ int engine_copier_create(EngineCopier **out)
     if (!c)
         return set_error(KV_EINVAL, "out of host memory for the copier");
     c->agents = a;
-    // alternate the pairs between copiers
-    const uint32_t pair = g_next_engine.fetch_add(1) % 2;
-    c->engine[0] = kEnginePairs[pair][0];
-    c->engine[1] = kEnginePairs[pair][1];
+    // spread copiers over the fast engines, preferring one the runtime reports free
+    uint32_t mask = 0;
+    if (hsa_amd_memory_copy_engine_status(a.cpu, a.gpu, &mask) != HSA_STATUS_SUCCESS)
+        mask = 0;
+    const uint32_t first = g_next_engine.fetch_add(1);
+    for (uint32_t i = 0; i < 4 && !c->engine; ++i) {
+        const uint32_t e = kFastEngines[(first + i) % 4];
+        if (mask & e)
+            c->engine = e;
+    }
+    if (!c->engine)   // the status is a snapshot of busy engines: use the next one anyway
+        c->engine = kFastEngines[first % 4];
     *out = c;
     return KV_OK;
 }
@@ -263,34 +270,18 @@ int engine_copy_to_host(EngineCopier *c, void *dst_host, const void *src_dev, in
     int st = take_slot(c, &slot);
     if (st)
         return st;
-    // one copy, or two halves (16-byte aligned) on the pair of engines; each
-    // completion takes one off `done`
-    const int parts = bytes >= kSplitBytes ? 2 : 1;
-    const int64_t first = parts == 2 ? (bytes / 2 + 15) / 16 * 16 : bytes;
     hsa_signal_store_relaxed(slot->gate, 1);
-    hsa_signal_store_relaxed(slot->done, parts);
+    hsa_signal_store_relaxed(slot->done, 1);
     hipError_t e = hipEventRecord(slot->ready, s);
     if (e != hipSuccess)
         return hip_fail(e, "hipEventRecord");
-    for (int p = 0; p < parts; ++p) {
-        const int64_t off = p ? first : 0, n = p ? bytes - first : first;
-        if (hsa_amd_memory_async_copy_on_engine((char *)dst_host + off, c->agents.cpu,
-                                                (const char *)src_dev + off, c->agents.gpu,
-                                                (size_t)n, 1, &slot->gate, slot->done,
-                                                (hsa_amd_sdma_engine_id_t)c->engine[p],
-                                                false) == HSA_STATUS_SUCCESS)
-            continue;
-        if (p == 0)
-            return set_error(KV_EHIP, "DMA engine %#x refused a copy of %lld bytes", c->engine[0],
-                             (long long)n);
-        // the first half is queued: let it finish and run out, then report
-        hsa_signal_subtract_screlease(slot->done, 1);
-        hsa_signal_store_screlease(slot->gate, 0);
-        slot->retired = true;
-        return set_error(KV_EHIP, "DMA engine %#x refused a copy of %lld bytes", c->engine[1],
-                         (long long)n);
-    }
-    // from here the engines hold the copy: every failure path must release it
+    if (hsa_amd_memory_async_copy_on_engine(dst_host, c->agents.cpu, src_dev, c->agents.gpu,
+                                            (size_t)bytes, 1, &slot->gate, slot->done,
+                                            (hsa_amd_sdma_engine_id_t)c->engine, false) !=
+        HSA_STATUS_SUCCESS)
+        return set_error(KV_EHIP, "DMA engine %#x refused a copy of %lld bytes", c->engine,
+                         (long long)bytes);
+    // from here the engine holds the copy: every failure path must release it
     e = hipStreamWriteValue64(s, (void *)slot->gate_value, 0, 0);
     if (e != hipSuccess) {
         hsa_signal_store_screlease(slot->gate, 0);   // let the engine move on
