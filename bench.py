@@ -79,8 +79,9 @@ def parse_args():
                     help="gpt2-1.5b is the headline; the others measure the remaining workloads")
     ap.add_argument("--swap-bank-mib", type=int, default=256)
     ap.add_argument("--transport", choices=("auto", "kernel", "runtime", "dma", "dma_out", "engine"),
-                    default="auto",
-                    help="bank<->host transfers (see kv_transport in include/kvstream.h)")
+                    default=None,
+                    help="bank<->host transfers (see kv_transport in include/kvstream.h); "
+                         "default: the workload's entry in DEFAULT_TRANSPORT")
     ap.add_argument("--ring-gather", choices=("flush", "each"), default="flush",
                     help="rings pack a bank's decode steps at flush time in one pass (flush) or "
                          "each step as it is pushed (each); see kv_ring_set_gather")
@@ -678,6 +679,16 @@ class LongStep:
 STEPS = {"gpt2-small-tiny": StreamStep, "gpt2-1.5b": StreamStep, "opt-66b-16l": RingStep,
          "bloom-176b-10l": SwapStep, "gqa-100k": LongStep}
 
+# The transport each step runs with unless --transport names one: the one
+# measured fastest for that step (ties go to the one that leaves the tile
+# kernels more of HBM).  GPT-2-1.5B: the named-engine device->host leg runs
+# the step as fast as the link-copy kernel (107 ms) with the tile kernels at
+# 0.58 of peak instead of 0.49; the OPT-66B ring runs 7% faster and the
+# 100K-context step 2% faster with the link-copy kernel.
+DEFAULT_TRANSPORT = {"gpt2-small-tiny": "auto", "gpt2-1.5b": "engine", "opt-66b-16l": "auto",
+                     "bloom-176b-10l": "auto", "gqa-100k": "auto"}
+TRANSPORTS = {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3, "dma_out": 4, "engine": 5}
+
 def link_ceiling(torch, nbytes=1 << 30, reps=3):
     """GB/s of one large contiguous pinned copy each way, and both at once."""
     d = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
@@ -994,9 +1005,9 @@ def main():
     WHOLE_CALLS = args.swap_calls == "whole"
     RING_GATHER = {"flush": kv.KV_RING_GATHER_AT_FLUSH, "each": kv.KV_RING_GATHER_EACH_STEP}[
         args.ring_gather]
-    step = STEPS[w.name](w, args.swap_bank_mib << 20,
-                {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3, "dma_out": 4,
-                 "engine": 5}[args.transport])
+    if args.transport is None:
+        args.transport = DEFAULT_TRANSPORT[w.name]
+    step = STEPS[w.name](w, args.swap_bank_mib << 20, TRANSPORTS[args.transport])
     torch.cuda.synchronize()
 
     if args.calibrate_copy_mib:

@@ -275,6 +275,21 @@ int engine_copy_to_host(EngineCopier *c, void *dst_host, const void *src_dev, in
     hipError_t e = hipEventRecord(slot->ready, s);
     if (e != hipSuccess)
         return hip_fail(e, "hipEventRecord");
+    // an engine with nothing queued, if one of the four is: a copy queued
+    // behind others (the runtime's host->device copies, gated on their own
+    // banks) would wait for all of them.  Consecutive copies of a stream may
+    // use different engines: each starts only after the stream is past the
+    // one before.
+    uint32_t idle = 0;
+    if (hsa_amd_memory_copy_engine_status(c->agents.cpu, c->agents.gpu, &idle) !=
+        HSA_STATUS_SUCCESS)
+        idle = 0;
+    if (!(idle & c->engine))
+        for (uint32_t e : kFastEngines)
+            if (idle & e) {
+                c->engine = e;
+                break;
+            }
     if (hsa_amd_memory_async_copy_on_engine(dst_host, c->agents.cpu, src_dev, c->agents.gpu,
                                             (size_t)bytes, 1, &slot->gate, slot->done,
                                             (hsa_amd_sdma_engine_id_t)c->engine, false) !=

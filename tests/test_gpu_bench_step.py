@@ -4,7 +4,7 @@ The workload tests run each call sequence on its own; here the step that
 bench.py times runs as it is timed (two compute streams and one copy stream
 per link direction, both directions at once, double-buffered host images,
 decode steps gathered at flush, whole images in one bank-chunked call,
-transport KV_XFER_AUTO), and everything it leaves behind is checked:
+the workload's transport), and everything it leaves behind is checked:
 
 * the prompt image streamed out of cache A, layer by layer;
 * cache B's prompt region against the image it loaded (streamed by an
@@ -62,11 +62,13 @@ def check_layers(dims, K, V, count, image, layer_bytes, what):
 
 
 @pytest.mark.timeout(900)
-def test_gpt2_stream_step(bench):
+@pytest.mark.parametrize("transport", ["bench default", "auto"])
+def test_gpt2_stream_step(bench, transport):
     import synth
     w = synth.WORKLOADS["gpt2-1.5b"]
-    note(f"bench step {w.name} dims={w.dims}")
-    step = bench.StreamStep(w, 256 << 20, 0)
+    name = bench.DEFAULT_TRANSPORT[w.name] if transport == "bench default" else transport
+    note(f"bench step {w.name} dims={w.dims} transport={name}")
+    step = bench.StreamStep(w, 256 << 20, bench.TRANSPORTS[name])
     dims = w.dims
     L, B = w.L, w.B
     A = [words(t) for t in step.caches["A"]]
@@ -115,7 +117,7 @@ def test_opt66b_ring_step(bench):
     import synth
     w = synth.WORKLOADS["opt-66b-16l"]
     note(f"bench step {w.name} dims={w.dims}")
-    step = bench.RingStep(w, 256 << 20, 0)
+    step = bench.RingStep(w, 256 << 20, bench.TRANSPORTS[bench.DEFAULT_TRANSPORT[w.name]])
     dims = w.dims
     L, B = w.L, w.B
     for k in range(2):
@@ -147,7 +149,7 @@ def test_bloom_swap_round(bench):
     import synth
     w = synth.WORKLOADS["bloom-176b-10l"]
     note(f"bench step {w.name} dims={w.dims}")
-    step = bench.SwapStep(w, 256 << 20, 0)
+    step = bench.SwapStep(w, 256 << 20, bench.TRANSPORTS[bench.DEFAULT_TRANSPORT[w.name]])
     dims, L, B = w.dims, w.L, w.B
     for r in range(2):
         x = r % step.N
@@ -172,7 +174,7 @@ def test_gqa_100k_long_step(bench):
     import synth
     w = synth.WORKLOADS["gqa-100k"]
     note(f"bench step {w.name} dims={w.dims}")
-    step = bench.LongStep(w, 256 << 20, 0)
+    step = bench.LongStep(w, 256 << 20, bench.TRANSPORTS[bench.DEFAULT_TRANSPORT[w.name]])
     L, B, H, D, S = w.dims
     one = (1, B, H, D, S)
     for k in range(2):
