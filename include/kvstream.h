@@ -299,7 +299,10 @@ typedef struct kv_swap kv_swap;
  *                      the copy's completion signal; host->device as
  *                      KV_XFER_RUNTIME.  Needs stream memory waits
  *                      (KV_EINVAL at create time otherwise).  Destroying the
- *                      handle waits until its copies are done.
+ *                      handle waits until its copies are done.  A profiler
+ *                      that runs one dispatch at a time (hardware counter
+ *                      collection) cannot order these copies: collect
+ *                      counters with another transport.
  * Measured on MI355X: DMA copies in both directions at once run at full
  * duplex when one direction moves large (bank-sized) chunks, but fall to
  * about one direction's rate when both move small dependent chunks (one
