@@ -20,7 +20,9 @@ dataflow of the DejaVu workers, emulated on one GPU:
      its host image, duplex.
 
 Host images are double-buffered across steps, so each step's inbound
-transfers read what an earlier step wrote.  Inputs are resident in HBM
+transfers read what an earlier step wrote.  Each workload's step runs with
+the transport listed in DEFAULT_TRANSPORT (this one: device-to-host copies
+on named DMA engines) unless --transport names another.  Inputs are resident in HBM
 before the timed region.  `value` is the KV payload the step moves across
 the host link (both directions) per second.  `roofline` describes the
 pack/unpack kernel with the most GPU time: algorithmic bytes (payload read +
