@@ -27,7 +27,8 @@ before the timed region.  `value` is the KV payload the step moves across
 the host link (both directions) per second.  `roofline` describes the
 pack/unpack kernel with the most GPU time: algorithmic bytes (payload read +
 payload written) per launch over its average duration, both measured live
-with hipEvents bracketing every launch on its own stream.  `cpu_baseline`
+with hipEvents bound to every launch's dispatch (the kernel's own begin and
+end timestamps).  `cpu_baseline`
 is the oracle on a bounded sample of the same step.
 
 `--workload` selects the other shapes, each with the step its class below
@@ -99,7 +100,7 @@ def parse_args():
                     help="skip the isolated measurements after the timed steps (ceilings, large "
                          "slices, schedule): a kernel trace then holds the steps' launches only")
     ap.add_argument("--no-profile", action="store_true",
-                    help="do not bracket launches with events (for external profilers)")
+                    help="do not time launches with events (for external profilers)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -1072,7 +1073,7 @@ def main():
               "link_peak_per_direction_GBps": PCIE_PEAK_GBPS}
     together = None
     if window and window["hbm_busy_ms"] > 0:
-        # kernels of different streams overlap: the union of their brackets is
+        # kernels of different streams overlap: the union of their intervals is
         # the time the pack/unpack kernels kept HBM busy, and their bytes over
         # that time the rate they reached together
         gbps = window["hbm_bytes"] / (window["hbm_busy_ms"] / 1000) / 1e9

@@ -528,11 +528,14 @@ int kv_ack(kv_acklog *a, int32_t x, int32_t j, int64_t t);
 int kv_ack_restart_point(const kv_acklog *a, int32_t *j, int64_t *t);
 
 /* ---------------------------------------------------------------------------
- * Live kernel timing.  Between kv_profile_begin and kv_profile_end every pack
- * and unpack kernel the library launches is bracketed by hipEvents on its
- * own stream.  kv_profile_end waits for those events, fills up to `max`
- * per-kernel entries and returns the number of distinct kernels.  `bytes`
- * is the algorithmic HBM traffic: payload read plus payload written.
+ * Live kernel timing.  Between kv_profile_begin and kv_profile_end every
+ * kernel the library launches is timed by two hipEvents bound to its
+ * dispatch (hipExtLaunchKernel's start and stop events), which take the
+ * kernel's own begin and end timestamps: no extra packets on the stream,
+ * and no launch latency in the interval.  kv_profile_end waits for those
+ * events, fills up to `max` per-kernel entries and returns the number of
+ * distinct kernels.  `bytes` is the algorithmic HBM traffic: payload read
+ * plus payload written (for the link-copy kernels: bytes over the link).
  */
 typedef struct kv_kernel_stat {
     char name[40];
@@ -547,12 +550,12 @@ int kv_profile_end(kv_kernel_stat *out, int32_t max);
 /* The window kv_profile_end last closed, all streams together.  Kernels of
  * different streams run at the same time, so per-kernel durations do not
  * add up to the GPU time the path took; these are the unions of the
- * bracketed intervals instead: `hbm_busy_ms` is the time during which at
+ * timed intervals instead: `hbm_busy_ms` is the time during which at
  * least one pack or unpack kernel ran and `hbm_bytes` the algorithmic bytes
  * those kernels moved (their rate together is hbm_bytes / hbm_busy_ms);
  * `link_*` the same for the link-copy kernels (bytes crossing the host
- * link).  `span_ms` runs from the first bracket's start to the last one's
- * end.  All zero when nothing was bracketed.  KV_EINVAL for a NULL `out`. */
+ * link).  `span_ms` runs from the first timed kernel's start to the last
+ * one's end.  All zero when nothing was timed.  KV_EINVAL for a NULL `out`. */
 typedef struct kv_profile_window {
     double span_ms;
     double hbm_busy_ms;

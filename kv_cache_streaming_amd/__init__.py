@@ -705,7 +705,7 @@ def kv_profile_end(max_entries: int = 16):
 
 
 def kv_profile_last_window() -> dict:
-    """Union of the bracketed intervals of the window kv_profile_end last
+    """Union of the timed kernel intervals of the window kv_profile_end last
     closed: {span_ms, hbm_busy_ms, hbm_bytes, hbm_launches, link_busy_ms,
     link_bytes, link_launches}."""
     w = kv_profile_window()

@@ -287,10 +287,9 @@ hipEvent_t take_event(ProfileState &ps)
         ps.pool.pop_back();
         return e;
     }
-    // Timing only: no system-scope fence when recorded.  A default event's
-    // record writes back and invalidates the caches, which would add that
-    // cost to every bracketed launch (and slow the work after it); ordering
-    // between streams never uses these events.
+    // Timing only: these events are bound to dispatches and never order
+    // streams, so they are made without the system-scope fence (a recorded
+    // default event writes back and invalidates the caches).
     hipEvent_t e = nullptr;
     if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
         (void)hipGetLastError();
@@ -301,49 +300,37 @@ hipEvent_t take_event(ProfileState &ps)
 
 }  // namespace
 
-bool profiling_enabled()
+LaunchTimer profile_take()
 {
     ProfileState &ps = prof();
     std::lock_guard<std::mutex> g(ps.mu);
-    return ps.on;
-}
-
-void *profile_start(hipStream_t s)
-{
-    ProfileState &ps = prof();
-    std::lock_guard<std::mutex> g(ps.mu);
+    LaunchTimer t;
+    if (!ps.on)
+        return t;
     hipEvent_t a = take_event(ps);
     hipEvent_t b = take_event(ps);
     if (!a || !b) {
         if (a) ps.pool.push_back(a);
         if (b) ps.pool.push_back(b);
-        return nullptr;
+        return t;
     }
-    if (hipEventRecord(a, s) != hipSuccess) {
-        (void)hipGetLastError();
-        ps.pool.push_back(a);
-        ps.pool.push_back(b);
-        return nullptr;
-    }
-    auto *p = new Pending{a, b, std::string(), 0};
-    return p;
+    t.start = a;
+    t.stop = b;
+    return t;
 }
 
-void profile_stop(void *tok, hipStream_t s, const char *name, int64_t bytes)
+void profile_commit(const LaunchTimer &t, const char *name, int64_t bytes, bool launched)
 {
-    auto *p = (Pending *)tok;
+    if (!t.start)
+        return;
     ProfileState &ps = prof();
     std::lock_guard<std::mutex> g(ps.mu);
-    if (hipEventRecord(p->b, s) != hipSuccess) {
-        (void)hipGetLastError();
-        ps.pool.push_back(p->a);
-        ps.pool.push_back(p->b);
+    if (launched) {
+        ps.pending.push_back(Pending{t.start, t.stop, std::string(name), bytes});
     } else {
-        p->name = name;
-        p->bytes = bytes;
-        ps.pending.push_back(*p);
+        ps.pool.push_back(t.start);
+        ps.pool.push_back(t.stop);
     }
-    delete p;
 }
 
 }  // namespace kvs
@@ -525,7 +512,7 @@ int kv_profile_end(kv_kernel_stat *out, int32_t max)
     ps.on = false;
     std::vector<kv_kernel_stat> stats;
     int status = KV_OK;
-    // every bracket's interval, as offsets from the first bracket's start
+    // every timed kernel's interval, as offsets from the first one's start
     std::vector<std::pair<double, double>> hbm_iv, link_iv;
     kv_profile_window win{};
     double first = 0.0, last = 0.0;

@@ -26,6 +26,7 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <tuple>
 
 namespace kvs {
 namespace {
@@ -573,28 +574,47 @@ __global__ __launch_bounds__(kThreads) void copy_paged_tiles(PagedGeometry g, Ro
     }
 }
 
+// Launch kernel `k` on `s`.  With a timer, the timer's two events take the
+// dispatch's own begin and end timestamps, so a timed launch costs no extra
+// packets on the stream and its interval is the kernel's alone.
+template <typename... P, typename... A>
+hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                  const LaunchTimer &t, A... a)
+{
+    std::tuple<P...> vals(a...);
+    void *ptrs[sizeof...(P)];
+    std::apply([&ptrs](auto &...v) {
+        size_t i = 0;
+        ((ptrs[i++] = (void *)&v), ...);
+    }, vals);
+    if (t.start)
+        return hipExtLaunchKernel((const void *)k, grid, block, ptrs, lds, s, t.start, t.stop, 0);
+    return hipLaunchKernel((const void *)k, grid, block, ptrs, lds, s);
+}
+
 template <bool kPack>
 hipError_t launch_paged_tiles(const PagedGeometry &g, const RowTable &rt, int64_t blocks,
-                              hipStream_t s)
+                              hipStream_t s, const LaunchTimer &t)
 {
     const dim3 grid((unsigned)blocks), block(kThreads);
+    hipError_t e;
     switch (g.C) {
-    case 1: copy_paged_tiles<1, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 2: copy_paged_tiles<2, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 4: copy_paged_tiles<4, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 8: copy_paged_tiles<8, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 16: copy_paged_tiles<16, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 32: copy_paged_tiles<32, 4, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 64: copy_paged_tiles<64, 4, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 128: copy_paged_tiles<128, 4, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 1: e = launch(copy_paged_tiles<1, 2, kPack>, grid, block, 0, s, t, g, rt); break;
+    case 2: e = launch(copy_paged_tiles<2, 2, kPack>, grid, block, 0, s, t, g, rt); break;
+    case 4: e = launch(copy_paged_tiles<4, 2, kPack>, grid, block, 0, s, t, g, rt); break;
+    case 8: e = launch(copy_paged_tiles<8, 2, kPack>, grid, block, 0, s, t, g, rt); break;
+    case 16: e = launch(copy_paged_tiles<16, 2, kPack>, grid, block, 0, s, t, g, rt); break;
+    case 32: e = launch(copy_paged_tiles<32, 4, kPack>, grid, block, 0, s, t, g, rt); break;
+    case 64: e = launch(copy_paged_tiles<64, 4, kPack>, grid, block, 0, s, t, g, rt); break;
+    case 128: e = launch(copy_paged_tiles<128, 4, kPack>, grid, block, 0, s, t, g, rt); break;
     default:
         if (g.C <= 16)
-            copy_paged_tiles<0, 2, kPack><<<grid, block, 0, s>>>(g, rt);
+            e = launch(copy_paged_tiles<0, 2, kPack>, grid, block, 0, s, t, g, rt);
         else
-            copy_paged_tiles<0, 4, kPack><<<grid, block, 0, s>>>(g, rt);
+            e = launch(copy_paged_tiles<0, 4, kPack>, grid, block, 0, s, t, g, rt);
         break;
     }
-    return hipGetLastError();
+    return e;
 }
 
 // Vectors per thread of the tile kernel: 512-vector tiles (two per thread)
@@ -604,26 +624,28 @@ hipError_t launch_paged_tiles(const PagedGeometry &g, const RowTable &rt, int64_
 constexpr int tile_per_thread(int32_t C) { return C <= 16 ? 2 : 4; }
 
 template <bool kPack>
-hipError_t launch_tiles_rt(const Geometry &g, const RowTable &rt, int64_t blocks, hipStream_t s)
+hipError_t launch_tiles_rt(const Geometry &g, const RowTable &rt, int64_t blocks, hipStream_t s,
+                           const LaunchTimer &t)
 {
     const dim3 grid((unsigned)blocks), block(kThreads);
+    hipError_t e;
     switch (g.C) {
-    case 1: copy_tiles<1, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 2: copy_tiles<2, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 4: copy_tiles<4, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 8: copy_tiles<8, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 16: copy_tiles<16, 2, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 32: copy_tiles<32, 4, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 64: copy_tiles<64, 4, kPack><<<grid, block, 0, s>>>(g, rt); break;
-    case 128: copy_tiles<128, 4, kPack><<<grid, block, 0, s>>>(g, rt); break;
+    case 1: e = launch(copy_tiles<1, 2, kPack>, grid, block, 0, s, t, g, rt); break;
+    case 2: e = launch(copy_tiles<2, 2, kPack>, grid, block, 0, s, t, g, rt); break;
+    case 4: e = launch(copy_tiles<4, 2, kPack>, grid, block, 0, s, t, g, rt); break;
+    case 8: e = launch(copy_tiles<8, 2, kPack>, grid, block, 0, s, t, g, rt); break;
+    case 16: e = launch(copy_tiles<16, 2, kPack>, grid, block, 0, s, t, g, rt); break;
+    case 32: e = launch(copy_tiles<32, 4, kPack>, grid, block, 0, s, t, g, rt); break;
+    case 64: e = launch(copy_tiles<64, 4, kPack>, grid, block, 0, s, t, g, rt); break;
+    case 128: e = launch(copy_tiles<128, 4, kPack>, grid, block, 0, s, t, g, rt); break;
     default:
         if (tile_per_thread(g.C) == 2)
-            copy_tiles<0, 2, kPack><<<grid, block, 0, s>>>(g, rt);
+            e = launch(copy_tiles<0, 2, kPack>, grid, block, 0, s, t, g, rt);
         else
-            copy_tiles<0, 4, kPack><<<grid, block, 0, s>>>(g, rt);
+            e = launch(copy_tiles<0, 4, kPack>, grid, block, 0, s, t, g, rt);
         break;
     }
-    return hipGetLastError();
+    return e;
 }
 
 int tile_tokens_for(int32_t C)
@@ -727,22 +749,21 @@ int launch_copy(bool pack, const Geometry &g0, const RowTable &rt, int32_t max_c
         gl.nl = std::min<int32_t>(layers_per_launch, g0.nl - done);
         gl.stage = g0.stage + 2 * (int64_t)done * blk;
         const int64_t payload = 2 * (int64_t)gl.nl * blk * 16;
-        void *tok = profiling_enabled() ? profile_start(s) : nullptr;
+        const LaunchTimer t = profile_take();
         hipError_t e;
         if (small) {
             const int64_t threads = (int64_t)gl.nl * gl.B * gl.nh * gl.C;
             const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads)), block(kThreads);
             if (pack)
-                copy_rows_small<true><<<grid, block, 0, s>>>(gl, rt);
+                e = launch(copy_rows_small<true>, grid, block, 0, s, t, gl, rt);
             else
-                copy_rows_small<false><<<grid, block, 0, s>>>(gl, rt);
-            e = hipGetLastError();
+                e = launch(copy_rows_small<false>, grid, block, 0, s, t, gl, rt);
         } else {
             const int64_t blocks = (int64_t)gl.nl * per_layer;
-            e = pack ? launch_tiles_rt<true>(gl, rt, blocks, s) : launch_tiles_rt<false>(gl, rt, blocks, s);
+            e = pack ? launch_tiles_rt<true>(gl, rt, blocks, s, t)
+                     : launch_tiles_rt<false>(gl, rt, blocks, s, t);
         }
-        if (tok)
-            profile_stop(tok, s, name, 2 * payload);
+        profile_commit(t, name, 2 * payload, e == hipSuccess);
         if (e != hipSuccess)
             return hip_fail(e, name);
     }
@@ -766,25 +787,24 @@ int launch_steps(bool pack, const Geometry &g0, const RowTable &rt, int32_t n,
         gl.stage = g0.stage + 2 * (int64_t)done * blk;
         const int64_t payload = 2 * (int64_t)gl.nl * blk * 16 * n;
         const int64_t threads = (int64_t)gl.nl * per_layer;
-        void *tok = profiling_enabled() ? profile_start(s) : nullptr;
+        const LaunchTimer t = profile_take();
+        hipError_t e;
         if ((int64_t)n * g0.C <= kStepMaxVecs) {
             const int64_t units = (int64_t)gl.nl * g0.B * g0.H;
             const dim3 grid((unsigned)((units + kStepWaves - 1) / kStepWaves)), block(kThreads);
             const size_t lds = (size_t)kStepWaves * n * g0.C * sizeof(u32x4);
             if (pack)
-                copy_steps_lds<true><<<grid, block, lds, s>>>(gl, rt, n, slot_vecs, units);
+                e = launch(copy_steps_lds<true>, grid, block, lds, s, t, gl, rt, n, slot_vecs, units);
             else
-                copy_steps_lds<false><<<grid, block, lds, s>>>(gl, rt, n, slot_vecs, units);
+                e = launch(copy_steps_lds<false>, grid, block, lds, s, t, gl, rt, n, slot_vecs, units);
         } else {
             const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads)), block(kThreads);
             if (pack)
-                copy_steps<true><<<grid, block, 0, s>>>(gl, rt, n, slot_vecs);
+                e = launch(copy_steps<true>, grid, block, 0, s, t, gl, rt, n, slot_vecs);
             else
-                copy_steps<false><<<grid, block, 0, s>>>(gl, rt, n, slot_vecs);
+                e = launch(copy_steps<false>, grid, block, 0, s, t, gl, rt, n, slot_vecs);
         }
-        const hipError_t e = hipGetLastError();
-        if (tok)
-            profile_stop(tok, s, name, 2 * payload);
+        profile_commit(t, name, 2 * payload, e == hipSuccess);
         if (e != hipSuccess)
             return hip_fail(e, name);
     }
@@ -818,23 +838,21 @@ int launch_paged_copy(bool pack, const PagedGeometry &g0, const RowTable &rt, in
         gl.nl = std::min<int32_t>(layers_per_launch, g0.nl - done);
         gl.stage = g0.stage + 2 * (int64_t)done * blk;
         const int64_t payload = 2 * (int64_t)gl.nl * blk * 16;
-        void *tok = profiling_enabled() ? profile_start(s) : nullptr;
+        const LaunchTimer t = profile_take();
         hipError_t e;
         if (small) {
             const int64_t threads = (int64_t)gl.nl * gl.B * gl.H * gl.C;
             const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads)), block(kThreads);
             if (pack)
-                copy_paged_small<true><<<grid, block, 0, s>>>(gl, rt);
+                e = launch(copy_paged_small<true>, grid, block, 0, s, t, gl, rt);
             else
-                copy_paged_small<false><<<grid, block, 0, s>>>(gl, rt);
-            e = hipGetLastError();
+                e = launch(copy_paged_small<false>, grid, block, 0, s, t, gl, rt);
         } else {
             const int64_t blocks = (int64_t)gl.nl * per_layer;
-            e = pack ? launch_paged_tiles<true>(gl, rt, blocks, s)
-                     : launch_paged_tiles<false>(gl, rt, blocks, s);
+            e = pack ? launch_paged_tiles<true>(gl, rt, blocks, s, t)
+                     : launch_paged_tiles<false>(gl, rt, blocks, s, t);
         }
-        if (tok)
-            profile_stop(tok, s, name, 2 * payload);
+        profile_commit(t, name, 2 * payload, e == hipSuccess);
         if (e != hipSuccess)
             return hip_fail(e, name);
     }
@@ -858,15 +876,14 @@ int launch_link_copy(void *dst, const void *src, int64_t bytes, bool to_host, hi
             std::min<int64_t>(link_blocks(to_host), (nvec + kThreads - 1) / kThreads);
         const u32x4 *from = (const u32x4 *)((const char *)src + done);
         u32x4 *to = (u32x4 *)((char *)dst + done);
-        void *tok = profiling_enabled() ? profile_start(s) : nullptr;
+        const LaunchTimer t = profile_take();
         const dim3 grid((unsigned)blocks), block(kThreads);
+        hipError_t e;
         if (to_host)
-            link_copy<true><<<grid, block, 0, s>>>(from, to, nvec);
+            e = launch(link_copy<true>, grid, block, 0, s, t, from, to, nvec);
         else
-            link_copy<false><<<grid, block, 0, s>>>(from, to, nvec);
-        const hipError_t e = hipGetLastError();
-        if (tok)
-            profile_stop(tok, s, name, n);
+            e = launch(link_copy<false>, grid, block, 0, s, t, from, to, nvec);
+        profile_commit(t, name, n, e == hipSuccess);
         if (e != hipSuccess)
             return hip_fail(e, name);
     }

@@ -119,9 +119,15 @@ int engine_copy_to_host(EngineCopier *c, void *dst_host, const void *src_dev, in
                         hipStream_t s);
 
 // ---- profiling (api.hip) ----
-bool profiling_enabled();
-// Begin/end a bracketed launch; `tok` is opaque state handed back to profile_end.
-void *profile_start(hipStream_t s);
-void profile_stop(void *tok, hipStream_t s, const char *name, int64_t bytes);
+// Two events that a timed launch binds to its dispatch (hipExtLaunchKernel):
+// they then hold the kernel's own begin and end timestamps.  Both null when
+// profiling is off.
+struct LaunchTimer {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchTimer profile_take();
+// Record the launch timed by `t` (moving `bytes`), or give its events back
+// when the launch failed.  No-op for a null timer.
+void profile_commit(const LaunchTimer &t, const char *name, int64_t bytes, bool launched);
 
 }  // namespace kvs

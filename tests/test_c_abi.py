@@ -46,5 +46,5 @@ def test_paged_partition_schedule_and_acks_from_c(program):
     # microbatch 1 has worker 1's ack missing: the restart is microbatch 1, step 0
     assert program["restart_point"] == "1 0"
     assert program["version"] == "1"
-    # nothing bracketed yet: an all-zero window; a NULL output is KV_EINVAL
+    # nothing timed yet: an all-zero window; a NULL output is KV_EINVAL
     assert program["profile_window"] == "0 0.0 0 -1"

@@ -497,7 +497,7 @@ def test_profiler_counts_launches(kv):
     assert win["hbm_launches"] == 3 and win["link_launches"] == 0
     assert win["hbm_bytes"] == sum(v[2] for v in stats.values())
     total = sum(v[1] for v in stats.values())
-    # one stream: the brackets follow one another, so their union is at most
+    # one stream: the kernels follow one another, so their union is at most
     # their sum and at least the longest of them, and fits in the span
     assert max(v[1] for v in stats.values()) <= win["hbm_busy_ms"] <= total * (1 + 1e-6)
     assert win["hbm_busy_ms"] <= win["span_ms"] * (1 + 1e-6)
@@ -506,7 +506,7 @@ def test_profiler_counts_launches(kv):
 
 def test_profile_window_overlapping_streams(kv):
     """Two streams packing at once, and a ring flush's link copy: the window
-    holds the union of the brackets of each class."""
+    holds the union of the timed intervals of each class."""
     import torch
     dims = (4, 4, 4, 128, 1024)
     L, B, H, D, S = dims
