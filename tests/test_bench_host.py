@@ -68,3 +68,74 @@ def test_committed_summaries_are_well_formed(bench):
         traffic = float(fields["traffic_bytes_per_launch"])
         algo = int(fields["algorithmic_bytes_per_launch"])
         assert 0.99 * algo <= traffic <= 1.5 * algo, f
+
+
+def test_oracle_pieces_partition_the_selection(bench):
+    """The all-cores CPU figure cuts each call into pieces: every selected
+    (row, token) lands in exactly one piece, and nothing else does."""
+    import numpy as np
+    rng = np.random.default_rng(5)
+    for B, threads in ((1, 16), (4, 16), (8, 3), (5, 1)):
+        start = rng.integers(0, 50, B)
+        count = rng.integers(0, 40, B)
+        count[0] = 0                              # an empty row
+        seen = {}
+        for st, ct in bench.oracle_pieces(B, start, count, threads):
+            live = [b for b in range(B) if ct[b] > 0]
+            assert len(live) == 1                 # one row per piece
+            b = live[0]
+            for s in range(st[b], st[b] + ct[b]):
+                assert (b, s) not in seen
+                seen[(b, s)] = True
+        want = {(b, int(s)) for b in range(B) for s in range(start[b], start[b] + count[b])}
+        assert set(seen) == want
+
+
+def test_all_cores_leg_moves_the_whole_call(bench):
+    """Run through the threaded leg, the oracle's pieces leave the destination
+    cache exactly as one whole-call pack + unpack does, and count its bytes."""
+    import numpy as np
+    import oracle
+    dims = (3, 4, 2, 16, 40)
+    L, B, H, D, S = dims
+    n = L * B * H * D * S
+    rng = np.random.default_rng(11)
+    src = [rng.integers(0, 1 << 16, n, dtype=np.uint16) for _ in range(2)]
+    start, count = [3, 0, 10, 1], [20, 0, 30, 39]
+    want = [np.zeros(n, np.uint16), np.zeros(n, np.uint16)]
+    oracle.unpack(dims, want[0], want[1], 1, 2, start, count,
+                  oracle.pack(dims, src[0], src[1], 1, 2, start, count))
+    got = [np.zeros(n, np.uint16), np.zeros(n, np.uint16)]
+    r = bench.cpu_all_cores(oracle, dims, [("pair", src, got, 1, 2, start, count)], 60.0, 1)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+    payload = 2 * 2 * H * D * sum(count) * 2      # K and V, 2 layers, 2 bytes each
+    assert r["cores"] >= 1 and r["value"] > 0
+    assert f"{2 * payload / 1e9:.3f} GB" in r["sample"]
+
+
+def test_all_cores_leg_keeps_order_where_calls_meet(bench, monkeypatch):
+    """Calls that write the same elements stay in order (the later one wins,
+    as run one after another); calls on disjoint elements share a group."""
+    import numpy as np
+    import oracle
+    # a pool of 8 threads whatever this host has: group sizes depend on it
+    monkeypatch.setattr(bench.os, "sched_getaffinity", lambda pid: set(range(8)))
+    dims = (2, 3, 2, 8, 32)
+    L, B, H, D, S = dims
+    n = L * B * H * D * S
+    rng = np.random.default_rng(3)
+    s1 = [rng.integers(0, 1 << 16, n, dtype=np.uint16) for _ in range(2)]
+    s2 = [rng.integers(0, 1 << 16, n, dtype=np.uint16) for _ in range(2)]
+    start, count = [0, 4, 8], [16, 16, 16]
+    pairs = [("first", s1, None, 0, 2, start, count), ("second", s2, None, 0, 2, start, count)]
+    # eight single-token calls at distinct positions: disjoint, so one group
+    steps = [(f"step{j}", s1, None, 0, 2, [20 + j] * B, [1] * B) for j in range(8)]
+    got = [np.zeros(n, np.uint16), np.zeros(n, np.uint16)]
+    want = [np.zeros(n, np.uint16), np.zeros(n, np.uint16)]
+    for name, src, _, l0, nl, st, ct in pairs + steps:
+        oracle.unpack(dims, want[0], want[1], l0, nl, st, ct,
+                      oracle.pack(dims, src[0], src[1], l0, nl, st, ct))
+    run = [(name, src, got, l0, nl, st, ct) for name, src, _, l0, nl, st, ct in pairs + steps]
+    r = bench.cpu_all_cores(oracle, dims, run, 60.0, 1)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+    assert "(1 pass(es), 3 groups)" in r["sample"]
