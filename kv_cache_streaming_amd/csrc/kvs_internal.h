@@ -29,6 +29,7 @@ struct Geometry {
     int32_t h0, nh;         // head range [h0, h0 + nh) moved; the packed format has nh heads
     int32_t tiles_per_row;  // tile kernel: tiles per row (ceil(max count / tile tokens))
     int32_t tile_tokens;    // tile kernel: tokens per tile
+    int32_t b0, nb;         // pack/unpack grids cover rows [b0, b0 + nb) (set by the launcher)
     int64_t T;              // sum of counts
 };
 
@@ -45,6 +46,7 @@ struct PagedGeometry {
     int32_t p_shift;        // log2(P) when P is a power of two, else -1
     int32_t B, l0, nl;
     int32_t tiles_per_row, tile_tokens;
+    int32_t b0, nb;         // grids cover rows [b0, b0 + nb) (set by the launcher)
     int64_t T;              // sum of counts
 };
 

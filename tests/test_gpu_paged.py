@@ -44,6 +44,8 @@ CASES = [  # L, H, D, P, B, stride, ranges
     (3, 2, 24, 5, 3, 90, "tiles"),
     (2, 2, 64, 1, 2, 300, "tiles"),
     (2, 3, 64, 16, 5, 8, "decode"),
+    (2, 3, 64, 16, 6, 10, "span"),          # empty rows before, inside and after the moved ones
+    (2, 2, 24, 5, 5, 6, "span-decode"),     # only the last row moves (few-token kernel)
 ]
 
 
@@ -64,6 +66,15 @@ def test_pack_and_unpack_match_the_oracle(kv, L, H, D, P, B, stride, ranges):
         count = rng.integers(0, cap + 1, size=B).astype(np.int32)
         count[0] = cap - 1
         start = np.array([int(rng.integers(0, cap - c + 1)) for c in count], np.int32)
+    elif ranges == "span":
+        count = np.zeros(B, np.int32)
+        count[1], count[B - 2] = cap - 3, 5
+        start = np.array([int(rng.integers(0, cap - c + 1)) for c in count], np.int32)
+    elif ranges == "span-decode":
+        count = np.zeros(B, np.int32)
+        count[B - 1] = 2
+        start = np.zeros(B, np.int32)
+        start[B - 1] = cap - 2
     else:
         count = rng.integers(1, 3, size=B).astype(np.int32)
         start = rng.integers(0, cap - 2, size=B).astype(np.int32)

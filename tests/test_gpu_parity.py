@@ -114,6 +114,22 @@ def test_empty_and_degenerate(kv):
     assert np.all(host(st) == 0x7A7A)
 
 
+def test_empty_rows_around_the_moved_ones(kv):
+    """The grids cover only the rows from the first to the last that move a
+    token: empty rows before, inside and after that span, over several
+    layers, with the tile kernel and the few-token kernel (D/8 = 3, the
+    generic variant)."""
+    dims = (3, 9, 3, 24, 80)
+    z = [0] * 9
+    check_pack_unpack(kv, dims, 0, 3, [0, 0, 5, 0, 7, 0, 0, 0, 0],
+                      [0, 0, 70, 0, 33, 0, 0, 0, 0], seed=31)
+    check_pack_unpack(kv, dims, 0, 3, [3] + z[1:], [77] + z[1:], seed=32)       # first row only
+    check_pack_unpack(kv, dims, 1, 2, z[:8] + [79], z[:8] + [1], seed=33)      # last row only
+    check_pack_unpack(kv, dims, 0, 3, [0, 10, 0, 0, 0, 0, 0, 20, 0],
+                      [0, 4, 0, 0, 0, 0, 0, 8, 0], seed=34)
+    check_pack_unpack(kv, dims, 2, 1, z[:4] + [60] + z[5:], z[:4] + [20] + z[5:], seed=35)
+
+
 def test_maximum_rows(kv):
     """KV_MAX_ROWS = 256 rows in one call (the row table travels in the kernel
     arguments): ragged and empty rows with the tile kernel, one token per row
