@@ -685,10 +685,11 @@ STEPS = {"gpt2-small-tiny": StreamStep, "gpt2-1.5b": StreamStep, "opt-66b-16l": 
 
 # The transport each step runs with unless --transport names one: the one
 # measured fastest for that step (ties go to the one that leaves the tile
-# kernels more of HBM).  GPT-2-1.5B: the named-engine device->host leg runs
-# the step as fast as the link-copy kernel (107 ms) with the tile kernels at
-# 0.58 of peak instead of 0.49; the OPT-66B ring runs 7% faster and the
-# 100K-context step 2% faster with the link-copy kernel.
+# kernels more of HBM).  GPT-2-1.5B: with the named-engine device->host leg
+# the step takes 107-110 ms against 108-115 ms with the link-copy kernel
+# (alternating runs on one box), with the tile kernels at 0.63-0.65 of peak
+# instead of 0.54-0.56; the OPT-66B ring runs 7% faster and the 100K-context
+# step 2% faster with the link-copy kernel.
 DEFAULT_TRANSPORT = {"gpt2-small-tiny": "auto", "gpt2-1.5b": "engine", "opt-66b-16l": "auto",
                      "bloom-176b-10l": "auto", "gqa-100k": "auto"}
 TRANSPORTS = {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3, "dma_out": 4, "engine": 5}
