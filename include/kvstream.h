@@ -291,18 +291,20 @@ typedef struct kv_swap kv_swap;
  *                      own copy kernel, and it picks the engine).
  *   KV_XFER_DMA_OUT -- device->host as KV_XFER_DMA, host->device as
  *                      KV_XFER_RUNTIME.
- *   KV_XFER_ENGINE  -- device->host on one named DMA engine (one of the
- *                      engines 0-3 that write host memory at full speed,
- *                      chosen per handle through the HSA runtime), submitted
- *                      by a worker thread of the handle once the copy stream
- *                      has reached the copy, with the stream then waiting on
- *                      the copy's completion signal; host->device as
+ *   KV_XFER_ENGINE  -- device->host on a named DMA engine through the HSA
+ *                      runtime: one of engines 0-3 (the ones that write host
+ *                      memory at full speed), for each copy one the runtime
+ *                      reports idle.  The copy is submitted when the call is
+ *                      made, gated on a signal that the copy stream clears
+ *                      once it reaches the copy; the stream then waits on the
+ *                      copy's completion signal.  host->device as
  *                      KV_XFER_RUNTIME.  Needs stream memory waits
  *                      (KV_EINVAL at create time otherwise).  Destroying the
- *                      handle waits until its copies are done.  A profiler
- *                      that runs one dispatch at a time (hardware counter
- *                      collection) cannot order these copies: collect
- *                      counters with another transport.
+ *                      handle waits until its copies are done.  These copies
+ *                      cannot be captured into a graph, and a profiler that
+ *                      runs one dispatch at a time (hardware counter
+ *                      collection) cannot order them: collect counters with
+ *                      another transport.
  * Measured on MI355X: DMA copies in both directions at once run at full
  * duplex when one direction moves large (bank-sized) chunks, but fall to
  * about one direction's rate when both move small dependent chunks (one
