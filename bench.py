@@ -813,6 +813,36 @@ def large_slices(step, kv):
     return out
 
 
+def layer_slices(step, kv, cache, start, count, warm=5, reps=20):
+    """Isolated one-layer pack and unpack on the workload's own slice shape
+    (a BLOOM-176B layer of every row, one 100K-context row): layers 0 and 1
+    alternate so every call reads data the last one did not (each layer's
+    slice is larger than the 256 MB Infinity Cache or close to it).  Seconds
+    are the library's kernel durations timed from their dispatches; each
+    unpack writes back what that layer's pack produced, so the cache ends as
+    it began.  HBM bytes = read + write of the payload."""
+    torch, lay = step.torch, step.lay
+    k, v = cache
+    B = lay.B
+    pb = kv.kv_pack_bytes(lay, 1, count)
+    stg = [torch.empty(pb // 2, dtype=torch.int16, device="cuda") for _ in range(2)]
+    s = torch.cuda.Stream()
+    out = {"payload_bytes": pb}
+    for name, fn in (("pack", kv.kv_pack_tokens), ("unpack", kv.kv_unpack_tokens)):
+        secs = []
+        for i in range(warm + reps):
+            l = i % 2
+            kv.kv_profile_begin()
+            fn(lay, k, v, l, 1, start, count, stg[l], pb, s)
+            torch.cuda.synchronize()
+            stats = kv.kv_profile_end()
+            if i >= warm:
+                secs.append(sum(x[1] for x in stats.values()) / 1000)
+        rate_entry(out, name, secs, 2 * pb, HBM_PEAK_GBPS, "_hbm_GBps")
+    del stg
+    return out
+
+
 def paged_slices(step, kv):
     """Isolated rates of the paged pool kernels on the workload's prompt: every
     layer's 1000 prompt tokens of 8 rows packed from (and unpacked into) a pool
@@ -1230,7 +1260,12 @@ def main():
             if step.w.B * step.w.Smax >= 4096:
                 detail["paged_slices"] = paged_slices(step, kv)
         if isinstance(step, SwapStep):
+            detail["layer_slices"] = layer_slices(step, kv, step.slots[0], step.rows_start,
+                                                  step.rows)
             detail["microbatch_schedule"] = step.schedule(kv)
+        if isinstance(step, LongStep):
+            detail["layer_slices"] = layer_slices(step, kv, step.A, step.row_start,
+                                                  step.row_count)
         if isinstance(step, RingStep):
             detail["repartition_2x2"] = step.repartition(kv)
     cpu = None
