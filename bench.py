@@ -48,6 +48,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -68,6 +70,8 @@ PCIE_PEAK_GBPS = 63.0          # PCIe 5.0 x16, per direction
 
 RING_GATHER = 1   # kv_ring_gather of the rings the steps use (set from --ring-gather)
 WHOLE_CALLS = True   # swaps of complete images as one call each (set from --swap-calls)
+OUT_STREAMS = 2      # device-to-host copy streams of the long-context step (--out-streams)
+ROW_TRANSPORT = None  # transport of the long-context step's row swap (--row-transport)
 
 
 def counters_file(workload, kernel_name):
@@ -79,8 +83,9 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="gpt2-1.5b", choices=sorted(STEPS),
-                    help="gpt2-1.5b is the headline; the others measure the remaining workloads")
+    ap.add_argument("--workload", default="gqa-100k", choices=sorted(STEPS),
+                    help="gqa-100k (the largest workload that fits one GPU) is the headline; "
+                         "the others measure the remaining workloads")
     ap.add_argument("--swap-bank-mib", type=int, default=256)
     ap.add_argument("--transport", choices=("auto", "kernel", "runtime", "dma", "dma_out", "engine"),
                     default=None,
@@ -92,6 +97,12 @@ def parse_args():
     ap.add_argument("--swap-calls", choices=("whole", "layer"), default="whole",
                     help="gpt2 shapes: a complete host image (prompt load, microbatch swap) moves "
                          "in one call the engine chunks by bank (whole) or in one call per layer")
+    ap.add_argument("--row-transport", choices=("auto", "kernel", "runtime", "dma", "dma_out",
+                                                "engine"), default=None,
+                    help="gqa-100k: transport of the row swap (default: --transport)")
+    ap.add_argument("--out-streams", type=int, choices=(1, 2), default=2,
+                    help="gqa-100k: the row swap-out and the prompt streaming share one "
+                         "device-to-host copy stream (1) or have one each (2)")
     ap.add_argument("--compute-streams", type=int, choices=(1, 2), default=2,
                     help="gpt2 shapes: packs and unpacks of the two link directions on one "
                          "compute stream (1) or one each (2)")
@@ -164,9 +175,19 @@ class StreamStep:
         self.positions = [[self.prompt + j] * B for j in range(w.decode_steps)]
 
     def link_bytes(self):
+        return self.link_bytes_out() + self.link_bytes_in()
+
+    def link_bytes_out(self):
+        """prompt streaming, ring flushes, microbatch swap-out"""
         L = self.w.L
-        return (2 * L * self.layer_prompt + 2 * self.w.decode_steps * self.slot
-                + 2 * L * self.layer_full)
+        return L * self.layer_prompt + self.w.decode_steps * self.slot + L * self.layer_full
+
+    def link_bytes_in(self):
+        """prompt load, ring restore, microbatch swap-in"""
+        return self.link_bytes_out()
+
+    def ceiling_caches(self):
+        return self.caches["B"], self.caches["C"]
 
     def run(self):
         torch, w = self.torch, self.w
@@ -383,7 +404,18 @@ class RingStep:
         self.ring.set_gather(RING_GATHER)
 
     def link_bytes(self):
-        return 2 * self.w.decode_steps * self.slot
+        return self.link_bytes_out() + self.link_bytes_in()
+
+    def link_bytes_out(self):
+        """ring flushes"""
+        return self.w.decode_steps * self.slot
+
+    def link_bytes_in(self):
+        """ring restore"""
+        return self.w.decode_steps * self.slot
+
+    def ceiling_caches(self):
+        return self.A, self.D
 
     def run(self):
         st = self.s["t"]
@@ -483,7 +515,18 @@ class SwapStep:
         self.r = 0
 
     def link_bytes(self):
-        return 2 * self.image
+        return self.link_bytes_out() + self.link_bytes_in()
+
+    def link_bytes_out(self):
+        """swap-out of microbatch x-1"""
+        return self.image
+
+    def link_bytes_in(self):
+        """swap-in of microbatch x+1"""
+        return self.image
+
+    def ceiling_caches(self):
+        return self.slots[0], self.slots[1]
 
     def run(self):
         N, r = self.N, self.r
@@ -621,8 +664,9 @@ class LongStep:
         self.row_image = L * self.row_layer
         # a bank holds at least one row of one layer (the engine splits at rows)
         sb = max(swap_bank_bytes, -(-self.row_layer // (1 << 20)) << 20)
+        rt = transport if ROW_TRANSPORT is None else ROW_TRANSPORT
         self.eng_o = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb,
-                               self.s["d2h_row"], transport)
+                               self.s["d2h_row" if OUT_STREAMS == 2 else "d2h"], rt)
         # the one-row slot: the row's packed image is the same bytes in a cache
         # of one row (the other rows move no tokens)
         self.lay1 = kv.kv_layout_init(L, 1, w.H, w.D, w.Smax, w.dtype)
@@ -630,7 +674,7 @@ class LongStep:
         self.slot1 = (torch.empty(n1, dtype=torch.int16, device="cuda"),
                       torch.empty(n1, dtype=torch.int16, device="cuda"))
         self.eng_i = kv.KvSwap(self.lay1, _bank(torch, sb), _bank(torch, sb), sb, self.s["h2d"],
-                               transport)
+                               rt)
         # the first step swaps in whatever the second image holds: its bytes
         # only have to be there, not to be a real row (no kernels at set-up,
         # so a counter run sees the steps' launches only)
@@ -645,8 +689,18 @@ class LongStep:
         self.k = 0
 
     def link_bytes(self):
-        return (self.w.L * self.prompt_layer + 2 * self.row_image
-                + 2 * self.w.decode_steps * self.slot)
+        return self.link_bytes_out() + self.link_bytes_in()
+
+    def link_bytes_out(self):
+        """prompt streaming, row swap-out, ring flushes"""
+        return self.w.L * self.prompt_layer + self.row_image + self.w.decode_steps * self.slot
+
+    def link_bytes_in(self):
+        """row swap-in, ring restore"""
+        return self.row_image + self.w.decode_steps * self.slot
+
+    def ceiling_caches(self):
+        return self.A, self.A
 
     def run(self):
         torch, w = self.torch, self.w
@@ -694,34 +748,49 @@ DEFAULT_TRANSPORT = {"gpt2-small-tiny": "auto", "gpt2-1.5b": "engine", "opt-66b-
                      "bloom-176b-10l": "auto", "gqa-100k": "auto"}
 TRANSPORTS = {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3, "dma_out": 4, "engine": 5}
 
-def link_ceiling(torch, nbytes=1 << 30, reps=3):
-    """GB/s of one large contiguous pinned copy each way, and both at once."""
-    d = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
-    d2 = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
-    h = torch.empty(nbytes // 2, dtype=torch.int16, pin_memory=True)
-    h2 = torch.empty(nbytes // 2, dtype=torch.int16, pin_memory=True)
-    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
-    out = {}
-    for name, fn in (("d2h", lambda: h.copy_(d, non_blocking=True)),
-                     ("h2d", lambda: d.copy_(h, non_blocking=True))):
-        fn()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            fn()
-        torch.cuda.synchronize()
-        out[name] = reps * nbytes / (time.perf_counter() - t0) / 1e9
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        with torch.cuda.stream(s1):
-            h.copy_(d, non_blocking=True)
-        with torch.cuda.stream(s2):
-            d2.copy_(h2, non_blocking=True)
-    torch.cuda.synchronize()
-    out["duplex_total"] = 2 * reps * nbytes / (time.perf_counter() - t0) / 1e9
-    del d, d2, h, h2
-    return out
+def link_ceiling(step, kv, transport, target_bytes=4 << 30, reps=3):
+    """GB/s the host link reaches through this library with `transport`, each
+    way and both ways at once: a swap-out and a swap-in of whole layers (every
+    row, all Smax positions; about 4 GB) through 256 MiB banks on streams of
+    their own, timed from the first enqueue to the synchronisation after the
+    last.  The swap-in lands in the step's second cache, or in the last layers
+    when the step has one cache (contents after the timed steps are not
+    used)."""
+    torch, lay = step.torch, step.lay
+    L, B, S = lay.L, lay.B, lay.Smax
+    full = [S] * B
+    per_layer = kv.kv_pack_bytes(lay, 1, full)
+    nl = max(1, min(L, target_bytes // per_layer))
+    nbytes = nl * per_layer
+    src, dst = step.ceiling_caches()
+    l_in = L - nl if src is dst else 0
+    # 256 MiB banks, or one row of one layer when that is larger
+    bank = max(256 << 20, -(-kv.kv_pack_bytes(lay, 1, [S] + [0] * (B - 1)) // (1 << 20)) << 20)
+    s = {n: torch.cuda.Stream() for n in ("po", "pi", "co", "ci")}
+    eo = kv.KvSwap(lay, _bank(torch, bank), _bank(torch, bank), bank, s["co"], transport)
+    ei = kv.KvSwap(lay, _bank(torch, bank), _bank(torch, bank), bank, s["ci"], transport)
+    ho, hi = HostBuffer(kv, nbytes), HostBuffer(kv, nbytes)
+    zero = [0] * B
+
+    def out():
+        eo.swap_out(src[0], src[1], 0, nl, zero, full, ho.data_ptr(), nbytes, s["po"])
+
+    def inn():
+        ei.swap_in(dst[0], dst[1], l_in, nl, zero, full, hi.data_ptr(), nbytes, s["pi"])
+
+    def both():
+        out()
+        inn()
+
+    res = {"transport": {v: k for k, v in TRANSPORTS.items()}[transport], "bytes_per_leg": nbytes}
+    for name, fn, legs in (("d2h", out, 1), ("h2d", inn, 1), ("duplex_total", both, 2)):
+        secs = rep_seconds(torch, fn, None, warm=1, reps=reps)
+        res[name] = round(legs * nbytes / float(np.median(secs)) / 1e9, 2)
+    eo.close()
+    ei.close()
+    ho.close()
+    hi.close()
+    return res
 
 
 def hbm_copy_ceiling(torch, nbytes=1 << 30, reps=4):
@@ -1172,8 +1241,11 @@ def main():
     import synth
     w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
-    global RING_GATHER, WHOLE_CALLS
+    global RING_GATHER, WHOLE_CALLS, OUT_STREAMS, ROW_TRANSPORT
     WHOLE_CALLS = args.swap_calls == "whole"
+    OUT_STREAMS = args.out_streams
+    if args.row_transport is not None:
+        ROW_TRANSPORT = TRANSPORTS[args.row_transport]
     RING_GATHER = {"flush": kv.KV_RING_GATHER_AT_FLUSH, "each": kv.KV_RING_GATHER_EACH_STEP}[
         args.ring_gather]
     if args.transport is None:
@@ -1251,8 +1323,23 @@ def main():
                     "GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                     "link_busy_share_of_step": round(window["link_busy_ms"] / (elapsed * 1000), 4)}
         detail["hbm_kernels_together"] = together
+    # each link direction on its own: bytes per step over the step time, as a
+    # share of the PCIe 5.0 x16 peak (and, with the detail, of the ceiling the
+    # same transport reaches alone)
+    out_b, in_b = step.link_bytes_out(), step.link_bytes_in()
+    directions = {}
+    for name, nb in (("d2h", out_b), ("h2d", in_b)):
+        gbps = nb / (ms / 1000) / 1e9
+        directions[name] = {"bytes_per_step": nb, "GBps": round(gbps, 2),
+                            "frac_of_pcie_peak": round(gbps / PCIE_PEAK_GBPS, 4)}
+    detail["link_directions"] = directions
     if not args.no_profile and not args.no_detail:
-        detail["link_ceiling_GBps"] = {k: round(v, 2) for k, v in link_ceiling(torch).items()}
+        ceil = link_ceiling(step, kv, TRANSPORTS[args.transport])
+        detail["link_ceiling_GBps"] = ceil
+        for name in ("d2h", "h2d"):
+            directions[name]["frac_of_ceiling"] = round(directions[name]["GBps"] / ceil[name], 4)
+        if ROW_TRANSPORT is not None and ROW_TRANSPORT != TRANSPORTS[args.transport]:
+            detail["link_ceiling_row_transport_GBps"] = link_ceiling(step, kv, ROW_TRANSPORT)
         if isinstance(step, StreamStep):
             detail["decode_step_us"] = decode_step_us(step, kv)
             detail["hbm_copy_ceiling_GBps"] = round(hbm_copy_ceiling(torch), 1)
@@ -1285,6 +1372,8 @@ def main():
                        "swap_bank_mib": args.swap_bank_mib,
                        "transport": args.transport, "ring_gather": args.ring_gather,
                        "compute_streams": args.compute_streams, "swap_calls": args.swap_calls,
+                       "out_streams": args.out_streams,
+                       "row_transport": args.row_transport or args.transport,
                        "hw_queues": int(os.environ["GPU_MAX_HW_QUEUES"])},
             "roofline": roofline, "cpu_baseline": cpu, "detail": detail}
     # the metric names two figures: the in-step pack/unpack rate (of the
@@ -1292,6 +1381,10 @@ def main():
     # the HBM peak) and the host-link rate (value)
     line["metric_parts"] = {
         "swap_host_link_GBps": line["value"],
+        "host_link_d2h_GBps": directions["d2h"]["GBps"],
+        "host_link_d2h_frac_of_pcie": directions["d2h"]["frac_of_pcie_peak"],
+        "host_link_h2d_GBps": directions["h2d"]["GBps"],
+        "host_link_h2d_frac_of_pcie": directions["h2d"]["frac_of_pcie_peak"],
         "pack_unpack_GBps": roofline["achieved"] if roofline else None,
         "pack_unpack_hbm_frac": roofline["frac"] if roofline else None,
         "pack_unpack_kernel": roofline["kernel"] if roofline else None,

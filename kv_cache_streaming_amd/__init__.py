@@ -19,7 +19,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvstream.so")
+# KVSTREAM_LIB names another build of the same library (the sanitizer build
+# of the host-side tests); the in-tree build otherwise
+LIB_PATH = os.environ.get("KVSTREAM_LIB") or os.path.join(_HERE, "libkvstream.so")
 
 KV_OK, KV_EINVAL, KV_ERANGE, KV_ESIZE, KV_EHIP, KV_EBUSY = 0, -1, -2, -3, -4, -5
 KV_F16, KV_BF16 = 0, 1
@@ -421,11 +423,16 @@ class KvSwap:
         self._h = h
 
     def close(self):
+        """Destroy the handle; KvError when its DMA copies could not be waited for."""
         if getattr(self, "_h", None):
-            self._destroy(self._h)
-            self._h = None
+            h, self._h = self._h, None
+            _check(self._destroy(h), "kv_swap_destroy")
 
-    __del__ = close
+    def __del__(self):
+        try:
+            self.close()
+        except KvError:
+            pass
 
     def swap_out(self, k, v, layer_begin, layer_count, start, count, host, host_bytes=None,
                  compute=None, done=None):
@@ -493,11 +500,16 @@ class KvRing:
         self._h = h
 
     def close(self):
+        """Destroy the handle; KvError when its DMA copies could not be waited for."""
         if getattr(self, "_h", None):
-            self._destroy(self._h)
-            self._h = None
+            h, self._h = self._h, None
+            _check(self._destroy(h), "kv_ring_destroy")
 
-    __del__ = close
+    def __del__(self):
+        try:
+            self.close()
+        except KvError:
+            pass
 
     def push(self, k, v, pos, compute=None):
         p = _Rows(pos, self.lay.B, "pos")

@@ -4,9 +4,11 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <strings.h>
 #include <utility>
 #include <vector>
 
@@ -76,7 +78,31 @@ int check_device_buffer(const void *p, int64_t bytes, const char *name)
     if (t0 != hipMemoryTypeDevice || t1 != hipMemoryTypeDevice)
         return set_error(KV_EINVAL, "%s [%p, +%lld) is not device memory", name, p,
                          (long long)bytes);
+    // the whole range must lie in the one allocation that holds its first byte
+    // (two adjacent allocations would pass the check of both ends)
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) == hipSuccess && base) {
+        const uintptr_t b = (uintptr_t)base, x = (uintptr_t)p;
+        if (x < b || (uint64_t)(x - b) + (uint64_t)bytes > (uint64_t)size)
+            return set_error(KV_EINVAL,
+                             "%s [%p, +%lld) runs past the end of its allocation [%p, +%zu)",
+                             name, p, (long long)bytes, base, size);
+    } else {
+        (void)hipGetLastError();   // memory the runtime cannot size: the end checks stand
+    }
     return KV_OK;
+}
+
+bool serialized_dispatch()
+{
+    // HIP's own serialisation switch, and the environment rocprofv3 sets for
+    // hardware counter collection (which runs one dispatch at a time)
+    auto on = [](const char *name) {
+        const char *v = std::getenv(name);
+        return v && *v && std::strcmp(v, "0") != 0 && strcasecmp(v, "false") != 0;
+    };
+    return on("AMD_SERIALIZE_KERNEL") || on("ROCPROF_COUNTER_COLLECTION");
 }
 
 int check_pinned_host(const void *p, int64_t bytes, const char *name)

@@ -15,6 +15,7 @@
 // and a "filled" event (after it, the bank holds the data the other stream
 // needs).
 #include "kvs_internal.h"
+#include "chunks.h"
 
 #include <algorithm>
 #include <cstring>
@@ -27,91 +28,15 @@ using namespace kvs;
 
 namespace {
 
-struct Chunk {
-    int32_t l0, nl, b0, b1;
-    int64_t staged;
-    int32_t pieces;
-    int64_t host_off[2], bank_off[2], bytes[2];
-};
-
-// Chunking of one swap: whole layers (as many as fit a bank) when a layer
-// fits, otherwise row groups of one layer.  Returns KV_OK or KV_ESIZE.
+// Chunking of one swap into a vector (see for_each_chunk).
 int plan_chunks(const kv_layout &lay, int32_t l0, int32_t nl, const RowTable &rt,
                 int64_t bank_bytes, std::vector<Chunk> *out)
 {
     out->clear();
-    const int64_t T = rt.off[lay.B];
-    const int64_t per_tok = (int64_t)lay.H * lay.D * lay.elem_bytes;   // one K (or V) token of a row
-    const int64_t layer_bytes = 2 * per_tok * T;
-    if (nl == 0 || T == 0)
+    return for_each_chunk(lay, l0, nl, rt, bank_bytes, [out](const Chunk &c) {
+        out->push_back(c);
         return KV_OK;
-    if (layer_bytes <= bank_bytes) {
-        const int32_t per = (int32_t)std::min<int64_t>(nl, bank_bytes / layer_bytes);
-        for (int32_t l = 0; l < nl; l += per) {
-            Chunk c;
-            c.l0 = l0 + l;
-            c.nl = std::min(per, nl - l);
-            c.b0 = 0;
-            c.b1 = lay.B;
-            c.staged = c.nl * layer_bytes;
-            c.pieces = 1;
-            c.host_off[0] = l * layer_bytes;
-            c.bank_off[0] = 0;
-            c.bytes[0] = c.staged;
-            c.host_off[1] = c.bank_off[1] = c.bytes[1] = 0;
-            out->push_back(c);
-        }
-        return KV_OK;
-    }
-    for (int32_t b = 0; b < lay.B; ++b) {
-        const int64_t rb = 2 * per_tok * (rt.off[b + 1] - rt.off[b]);
-        if (rb > bank_bytes)
-            return set_error(KV_ESIZE, "row %d of one layer needs %lld bytes; banks hold %lld", b,
-                             (long long)rb, (long long)bank_bytes);
-    }
-    for (int32_t l = 0; l < nl; ++l) {
-        int32_t b0 = 0;
-        while (b0 < lay.B) {
-            int32_t b1 = b0;
-            while (b1 < lay.B &&
-                   2 * per_tok * (rt.off[b1 + 1] - rt.off[b0]) <= bank_bytes)
-                ++b1;
-            const int64_t tok = rt.off[b1] - rt.off[b0];
-            if (tok > 0) {
-                Chunk c;
-                c.l0 = l0 + l;
-                c.nl = 1;
-                c.b0 = b0;
-                c.b1 = b1;
-                c.staged = 2 * per_tok * tok;
-                c.pieces = 2;
-                c.host_off[0] = l * layer_bytes + per_tok * rt.off[b0];
-                c.host_off[1] = l * layer_bytes + per_tok * T + per_tok * rt.off[b0];
-                c.bank_off[0] = 0;
-                c.bank_off[1] = per_tok * tok;
-                c.bytes[0] = c.bytes[1] = per_tok * tok;
-                out->push_back(c);
-            }
-            b0 = b1;
-        }
-    }
-    return KV_OK;
-}
-
-// Row table of one chunk: rows outside [b0, b1) move nothing.
-void chunk_rows(const kv_layout &lay, const RowTable &rt, const Chunk &c, RowTable *sub,
-                int32_t *max_count)
-{
-    int32_t off = 0, mx = 0;
-    for (int32_t b = 0; b < lay.B; ++b) {
-        const int32_t n = (b >= c.b0 && b < c.b1) ? rt.off[b + 1] - rt.off[b] : 0;
-        sub->start[b] = n ? rt.start[b] : 0;
-        sub->off[b] = off;
-        off += n;
-        mx = std::max(mx, n);
-    }
-    sub->off[lay.B] = off;
-    *max_count = mx;
+    });
 }
 
 int check_banks_apart(void *const bank[2], int64_t bank_bytes, const kv_layout &lay,
@@ -176,6 +101,11 @@ int check_transport(int32_t transport)
 {
     if (transport < KV_XFER_AUTO || transport > KV_XFER_ENGINE)
         return set_error(KV_EINVAL, "transport %d is not a kv_transport", transport);
+    if (transport == KV_XFER_ENGINE && serialized_dispatch())
+        return set_error(KV_EINVAL,
+                         "KV_XFER_ENGINE needs concurrent dispatch: with AMD_SERIALIZE_KERNEL or "
+                         "counter collection (ROCPROF_COUNTER_COLLECTION) its stream waits on a "
+                         "DMA copy never finish; use another transport");
     return KV_OK;
 }
 
@@ -209,7 +139,11 @@ struct kv_ring {
     int64_t slot_bytes;
     int64_t steps, flushed;
     std::vector<int32_t> pos;    // steps * B positions, in step order
-    hipEvent_t ev[4];            // free0, free1, filled0, filled1
+    hipEvent_t ev[5];            // free0, free1, filled0, filled1, sync
+    // compute streams of the packs (gather per step) into the bank of the
+    // unflushed steps: the copy stream orders itself after each of them
+    // before it reads (flush) or overwrites (restore) that bank
+    std::vector<hipStream_t> pack_streams;
     bool wait_needed[2];         // a push must wait on free_ev before writing the bank
     bool free_valid[2];          // free_ev has been recorded at least once
     // flush copies not yet known complete: (event after the copy, steps held once it lands)
@@ -221,6 +155,7 @@ struct kv_ring {
     std::vector<std::pair<const void *, const void *>> pend;
     hipEvent_t free_ev(int b) const { return ev[b]; }
     hipEvent_t filled_ev(int b) const { return ev[2 + b]; }
+    hipEvent_t sync_ev() const { return ev[4]; }
 };
 
 namespace {
@@ -328,11 +263,11 @@ int kv_swap_destroy(kv_swap *e)
 {
     if (!e)
         return KV_OK;
-    engine_copier_destroy(e->copier);
+    const int st = engine_copier_destroy(e->copier);
     for (hipEvent_t ev : e->ev)
         (void)hipEventDestroy(ev);
     delete e;
-    return KV_OK;
+    return st;
 }
 
 int kv_swap_out(kv_swap *e, const void *k, const void *v, int32_t layer_begin,
@@ -519,7 +454,7 @@ int kv_ring_create(kv_ring **out, const kv_layout *lay, int32_t R, void *bank0, 
     r->wait_needed[0] = r->wait_needed[1] = false;
     r->free_valid[0] = r->free_valid[1] = false;
     r->copier = nullptr;
-    if ((st = create_events(r->ev, 4))) {
+    if ((st = create_events(r->ev, 5))) {
         delete r;
         return st;
     }
@@ -537,7 +472,7 @@ int kv_ring_destroy(kv_ring *r)
 {
     if (!r)
         return KV_OK;
-    engine_copier_destroy(r->copier);
+    const int st = engine_copier_destroy(r->copier);
     for (hipEvent_t ev : r->ev)
         (void)hipEventDestroy(ev);
     for (auto &p : r->landing)
@@ -545,7 +480,7 @@ int kv_ring_destroy(kv_ring *r)
     for (hipEvent_t ev : r->spare)
         (void)hipEventDestroy(ev);
     delete r;
-    return KV_OK;
+    return st;
 }
 
 namespace {
@@ -616,6 +551,21 @@ int ring_gather(kv_ring *r, hipStream_t compute)
     return st;
 }
 
+// Make the copy stream wait for every pack of an unflushed step, except
+// those on `covered` when `skip` (the stream whose own event the copy waits on
+// anyway).  One event serves them all: a stream wait takes the event's state
+// at the time of the wait.
+int ring_order_packs(kv_ring *r, bool skip, hipStream_t covered)
+{
+    int st;
+    for (hipStream_t s : r->pack_streams)
+        if (!(skip && s == covered) &&
+            ((st = record(r->sync_ev(), s, "ring pack order")) ||
+             (st = wait(r->copy, r->sync_ev(), "ring pack order wait"))))
+            return st;
+    return KV_OK;
+}
+
 // Copy steps [first, first+n) -- all in one bank -- to the host image.
 int ring_flush_range(kv_ring *r, int64_t first, int64_t n, hipStream_t compute)
 {
@@ -623,8 +573,10 @@ int ring_flush_range(kv_ring *r, int64_t first, int64_t n, hipStream_t compute)
     const int64_t off = (first % r->R) * r->slot_bytes;
     int st;
     if ((st = record(r->filled_ev(bk), compute, "ring filled")) ||
-        (st = wait(r->copy, r->filled_ev(bk), "ring flush wait")))
+        (st = wait(r->copy, r->filled_ev(bk), "ring flush wait")) ||
+        (st = ring_order_packs(r, true, compute)))
         return st;
+    r->pack_streams.clear();
     if ((st = transfer(r->transport, r->copier, (char *)r->bank[bk] + off,
                        (char *)r->host + first * r->slot_bytes,
                        (char *)r->host_dev + first * r->slot_bytes, n * r->slot_bytes, true,
@@ -689,6 +641,9 @@ int kv_ring_push(kv_ring *r, const void *k, const void *v, const int32_t *pos,
         void *slot = (char *)r->bank[bk] + (j % r->R) * r->slot_bytes;
         if ((st = enqueue_copy(true, lay, k, v, 0, lay.L, rt, mx, slot, compute)))
             return st;
+        if (std::find(r->pack_streams.begin(), r->pack_streams.end(), compute) ==
+            r->pack_streams.end())
+            r->pack_streams.push_back(compute);
     }
     r->pos.insert(r->pos.end(), pos, pos + lay.B);
     r->steps = j + 1;
@@ -739,6 +694,10 @@ int ring_restore_n(kv_ring *r, void *k, void *v, int64_t n_steps, hipStream_t co
         (st = check_device_buffer(v, lay.v_bytes, "value cache")))
         return st;
     if ((st = check_banks_apart(r->bank, r->bank_bytes, lay, k, v)))
+        return st;
+    // steps pushed after the last flush may still be packing into a bank
+    // the loads below overwrite
+    if ((st = ring_order_packs(r, false, nullptr)))
         return st;
     for (int64_t j0 = 0, g = 0; j0 < n_steps; j0 += r->R, ++g) {
         const int64_t n = std::min<int64_t>(r->R, n_steps - j0);
@@ -793,6 +752,7 @@ int kv_ring_restore_steps(kv_ring *r, void *k, void *v, int64_t n, hipStream_t c
     if (n < r->steps) {
         r->steps = r->flushed = n;
         r->pend.clear();
+        r->pack_streams.clear();
         r->pos.resize((size_t)n * r->lay.B);
         r->durable = std::min(r->durable, n);
         std::deque<std::pair<hipEvent_t, int64_t>> keep;

@@ -59,6 +59,10 @@ int check_layout(const kv_layout *lay);
 int check_device_buffer(const void *p, int64_t bytes, const char *name);
 int check_pinned_host(const void *p, int64_t bytes, const char *name);
 bool overlaps(const void *a, int64_t an, const void *b, int64_t bn);
+// True when the environment asks for kernel dispatches one at a time
+// (AMD_SERIALIZE_KERNEL, or rocprofv3's counter collection): a copy that a
+// stream waits on through a memory value then never starts.
+bool serialized_dispatch();
 // Validates per-row ranges and fills `rt`; returns KV_OK or an error.  `count`
 // NULL means one token per row.
 int build_rows(const kv_layout &lay, const int32_t *start, const int32_t *count, RowTable *rt,
@@ -112,8 +116,11 @@ struct EngineCopier;
 // A copier on one of the DMA engines that write host memory at full speed,
 // for the current device; KV_EINVAL when the device or runtime cannot.
 int engine_copier_create(EngineCopier **out);
-// Waits until every copy is submitted and every stream is past it.
-void engine_copier_destroy(EngineCopier *c);
+// Waits until every copy is submitted and every stream is past it.  Returns
+// KV_EHIP (with kv_last_error set) when a copy was still running after ten
+// seconds: its signals are then left allocated rather than freed under the
+// engine.
+int engine_copier_destroy(EngineCopier *c);
 // Enqueue on `s` a copy of `bytes` from device memory to pinned host memory
 // that starts once everything enqueued on `s` so far has run, and that later
 // work on `s` waits for.

@@ -36,7 +36,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# KV_ORACLE_LIB names another build of oracle.c (the sanitizer build of the
+# host-side tests); the in-tree build otherwise
+_LIB = os.environ.get("KV_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32

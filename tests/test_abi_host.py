@@ -204,3 +204,32 @@ def test_swap_plan_rejects_a_row_larger_than_a_bank(kv):
     with pytest.raises(kv.KvError) as e:
         kv.kv_swap_plan(lay, 0, 2, [0, 0], [8, 1], 2 * 2 * 16 * 2 * 8 - 1)
     assert e.value.status == kv.KV_ESIZE
+
+
+@pytest.mark.parametrize("var,val,refused", [
+    ("AMD_SERIALIZE_KERNEL", "3", True), ("ROCPROF_COUNTER_COLLECTION", "1", True),
+    ("ROCPROF_COUNTER_COLLECTION", "True", True), ("AMD_SERIALIZE_KERNEL", "0", False)])
+def test_engine_transport_refused_under_serialised_dispatch(kv, monkeypatch, var, val, refused):
+    """KV_XFER_ENGINE makes a stream wait on a DMA copy's completion value;
+    when dispatches run one at a time (HIP's AMD_SERIALIZE_KERNEL, or the
+    environment rocprofv3 sets for counter collection) that wait would never
+    end, so both handles refuse the transport at create time, before any
+    other check."""
+    monkeypatch.delenv("AMD_SERIALIZE_KERNEL", raising=False)
+    monkeypatch.delenv("ROCPROF_COUNTER_COLLECTION", raising=False)
+    monkeypatch.setenv(var, val)
+    lay = kv.kv_layout_init(2, 2, 2, 64, 16)
+    h = ctypes.c_void_p()
+    st = kv._lib.kv_swap_create(ctypes.byref(h), ctypes.byref(lay), 4096, 8192, 4096, None,
+                                kv.KV_XFER_ENGINE)
+    assert st == kv.KV_EINVAL and not h.value
+    assert ("KV_XFER_ENGINE" in kv.kv_last_error()) == refused
+    slot = kv.kv_pack_bytes(lay, 2, None, 1)
+    st = kv._lib.kv_ring_create(ctypes.byref(h), ctypes.byref(lay), 2, 4096, 4096 + 2 * slot,
+                                2 * slot, 65536, 4 * slot, None, kv.KV_XFER_ENGINE)
+    assert st == kv.KV_EINVAL and not h.value
+    assert ("KV_XFER_ENGINE" in kv.kv_last_error()) == refused
+    # the other transports are not affected by the setting
+    st = kv._lib.kv_swap_create(ctypes.byref(h), ctypes.byref(lay), 4096, 8192, 4096, None,
+                                kv.KV_XFER_AUTO)
+    assert st == kv.KV_EINVAL and "KV_XFER_ENGINE" not in kv.kv_last_error()

@@ -29,7 +29,7 @@ def test_headline_line():
         assert key in d, key
     assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1
     assert d["higher_is_better"] is True and d["vs_baseline"] is None
-    assert d["config"]["workload"] == "gpt2-1.5b"
+    assert d["config"]["workload"] == "gqa-100k"
     # value: the host-link bytes of a step over its time
     link = d["detail"]["link_bytes_per_step"]
     assert abs(d["value"] - link / (d["ms_per_step"] / 1000) / 1e9) <= 0.01 * d["value"]

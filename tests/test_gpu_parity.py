@@ -250,7 +250,7 @@ def test_error_paths(kv):
     assert ring.steps == 3
 
 
-TRANSPORTS = [0, 1, 2, 3, 5]   # KV_XFER_AUTO, _KERNEL, _RUNTIME, _DMA, _ENGINE
+TRANSPORTS = [0, 1, 2, 3, 4, 5]   # KV_XFER_AUTO, _KERNEL, _RUNTIME, _DMA, _DMA_OUT, _ENGINE
 
 
 def run_ring(kv, dims, R, positions, seed, bits=True, mutate=False, delay_cycles=0, transport=0,

@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import dev, host, note, pinned, pinned_host_view
+from gpu_util import dev, empty, host, note, pinned, pinned_host_view
 
 pytestmark = pytest.mark.gpu
 
@@ -115,3 +115,47 @@ def test_replicate_fail_restore_resume(kv):
         assert rings[j].durable_steps == t0 + 1
         rings[j].close()
     eng.close()
+
+
+@pytest.mark.parametrize("same_stream", [True, False])
+def test_restore_steps_waits_for_unflushed_pack(kv, same_stream):
+    """A partial restore issued right after a push whose pack has not run yet
+    (held back by a bounded spin on its stream), with no host synchronisation
+    in between: the restore loads the replica into the bank that pack writes,
+    so the load must wait for it, or the restored step 0 would carry the
+    unflushed step's bytes.  Each-step gather; the pushes' stream is the
+    restore's own, or another one."""
+    import torch
+    dims = (3, 2, 2, 64, 40)
+    L, B, H, D, S = dims
+    R = 4
+    note(f"restore_steps after an unflushed pack dims={dims} R={R} same_stream={same_stream}")
+    lay = kv.kv_layout_init(*dims, 0)
+    K, V = synth.cache_pair(dims, 4321)
+    dk, dv = dev(K), dev(V)
+    slot = kv.kv_pack_bytes(lay, L, None, 1)
+    T = 2 * R + 1
+    rhost = pinned(T * slot // 2)
+    copy = torch.cuda.Stream()
+    push_s = torch.cuda.Stream()
+    restore_s = push_s if same_stream else torch.cuda.Stream()
+    ring = kv.KvRing(lay, R, empty(R * slot // 2), empty(R * slot // 2), rhost, copy_stream=copy)
+    positions = [[3 * t + b for b in range(B)] for t in range(T)]
+    rk, rv = empty(K.size, fill=0x1DEA), empty(V.size, fill=0x1DEA)
+    torch.cuda.synchronize()                     # inputs in place; none from here on
+    for t in range(2 * R):                       # two banks, both flushed
+        ring.push(dk, dv, positions[t], push_s)
+    with torch.cuda.stream(push_s):
+        torch.cuda._sleep(200_000_000)           # holds back the next pack
+    ring.push(dk, dv, positions[2 * R], push_s)  # step 2R: slot 0 of bank 0, not flushed
+    ring.restore_steps(rk, rv, 2 * R, restore_s)
+    assert ring.steps == 2 * R
+    torch.cuda.synchronize()
+    slots = [oracle.pack(dims, K, V, 0, L, positions[t], [1] * B) for t in range(2 * R)]
+    img = oracle.ring_host(slots)
+    assert np.array_equal(pinned_host_view(rhost)[:img.size], img), "replica differs"
+    ek = np.full(K.size, 0x1DEA, np.uint16)
+    ev = ek.copy()
+    oracle.ring_restore(dims, ek, ev, positions[:2 * R], img)
+    assert np.array_equal(host(rk), ek) and np.array_equal(host(rv), ev), "restore differs"
+    ring.close()
