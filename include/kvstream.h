@@ -351,6 +351,27 @@ int kv_swap_in(kv_swap *e, void *k, void *v,
                const int32_t *start, const int32_t *count,
                const void *host, int64_t host_bytes, hipStream_t compute, hipEvent_t done);
 
+/* Swap-out that allocates nothing, for callers that cannot allocate memory:
+ * code under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same host bytes as kv_swap_out over the same region, without a
+ * handle or banks: each chunk of the region (whole layers, or row groups of
+ * one layer, that fit KV_NOALLOC_SCRATCH_BYTES) is packed on `s` into a
+ * static device buffer of the library and then copied to `host` (pinned) by
+ * the link-copy kernel on `s`, chunk after chunk in stream order.  The host
+ * image is valid once `s` has passed the call.  The library holds that
+ * buffer (KV_NOALLOC_SCRATCH_BYTES) on every GPU it runs on until the process
+ * ends; the call itself calls no hipMalloc, hipFree or other allocating
+ * routine.  All calls on one GPU share the buffer and nothing in it needs to
+ * start at any value: calls on one stream follow one another, but calls that
+ * overlap in time on one GPU (other streams, other threads) race on it and
+ * must be ordered by the caller.  KV_ESIZE when one layer of one row needs
+ * more than KV_NOALLOC_SCRATCH_BYTES; other errors as kv_swap_out. */
+#define KV_NOALLOC_SCRATCH_BYTES (128ll << 20)
+int kv_swap_out_noalloc(const kv_layout *lay, const void *k, const void *v,
+                        int32_t layer_begin, int32_t layer_count,
+                        const int32_t *start, const int32_t *count,
+                        void *host, int64_t host_bytes, hipStream_t s);
+
 /* Layer-by-layer prompt streaming ([DV, Fig 7b; Fast prompt KV transfer]):
  * pack one prompt layer (as kv_pack_prompt_layer) into the next bank on
  * `compute` and copy it to `host` on the copy stream, so that streaming layer

@@ -122,6 +122,7 @@ _SIGNATURES = {
     "kv_swap_out": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
     "kv_swap_in": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
     "kv_stream_prompt_layer": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _P]),
+    "kv_swap_out_noalloc": (ctypes.c_int, [_LAY, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P]),
     "kv_swap_plan": (_I64, [_LAY, _I32, _I32, _P, _P, _I64, _P, _I64]),
     "kv_ring_create": (ctypes.c_int, [ctypes.POINTER(_P), _LAY, _I32, _P, _P, _I64, _P, _I64, _P,
                                       _I32]),
@@ -457,6 +458,17 @@ class KvSwap:
         _check(_lib.kv_stream_prompt_layer(self._h, _addr(k), _addr(v), layer, tok_begin,
                                            tok_count, rl.ptr, _addr(host), nb, _stream(compute),
                                            _event(done)), "kv_stream_prompt_layer")
+
+
+def kv_swap_out_noalloc(lay, k, v, layer_begin, layer_count, start, count, host,
+                        host_bytes=None, stream=None) -> None:
+    """Swap-out through the library's static scratch buffer on one stream
+    (allocates nothing; see kv_swap_out_noalloc in kvstream.h)."""
+    st, ct = _Rows(start, lay.B, "start"), _Rows(count, lay.B, "count")
+    nb = _nbytes(host) if host_bytes is None else host_bytes
+    _check(_lib.kv_swap_out_noalloc(ctypes.byref(lay), _addr(k), _addr(v), layer_begin,
+                                    layer_count, st.ptr, ct.ptr, _addr(host), nb, _stream(stream)),
+           "kv_swap_out_noalloc")
 
 
 def kv_swap_create(lay, bank0, bank1, bank_bytes=None, copy_stream=None,
