@@ -111,6 +111,10 @@ def parse_args():
     ap.add_argument("--no-detail", action="store_true",
                     help="skip the isolated measurements after the timed steps (ceilings, large "
                          "slices, schedule): a kernel trace then holds the steps' launches only")
+    ap.add_argument("--slices-only", action="store_true",
+                    help="run only the isolated large-slice calls of the workload (the ones the "
+                         "70%%-of-peak bar applies to) and print their rates: a profiler run then "
+                         "holds those launches alone")
     ap.add_argument("--no-profile", action="store_true",
                     help="do not time launches with events (for external profilers)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -912,6 +916,19 @@ def layer_slices(step, kv, cache, start, count, warm=5, reps=20):
     return out
 
 
+def slices_only(step, kv):
+    """The isolated large-slice calls of a workload (each moves 256 MiB of
+    payload or more): 48 GPT-2-1.5B layers in one call, a BLOOM-176B layer of
+    every row, one layer of the longest 100K-context row."""
+    if isinstance(step, StreamStep):
+        return {"gpt2_48_layers": large_slices(step, kv)}
+    if isinstance(step, SwapStep):
+        return {"bloom_layer": layer_slices(step, kv, step.slots[0], step.rows_start, step.rows)}
+    if isinstance(step, LongStep):
+        return {"long_row_layer": layer_slices(step, kv, step.A, step.row_start, step.row_count)}
+    return {}
+
+
 def paged_slices(step, kv):
     """Isolated rates of the paged pool kernels on the workload's prompt: every
     layer's 1000 prompt tokens of 8 rows packed from (and unpacked into) a pool
@@ -1262,6 +1279,10 @@ def main():
         torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.slices_only:
+        print(json.dumps({"workload": w.name, "large_slices": slices_only(step, kv)}), flush=True)
+        return
 
     if isinstance(step, StreamStep) and args.compute_streams == 1:
         step.run = step.run_one_stream

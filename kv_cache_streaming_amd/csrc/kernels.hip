@@ -13,15 +13,16 @@
 //    per (layer, row, head, key vector c); it moves K vector c and V vector c
 //    of each of the row's tokens.  A wave covers 64/C heads, so every store
 //    instruction writes contiguous runs of C*16 bytes of the packed buffer.
-//  * copy_tiles -- many tokens per row (prompt layers, chunks, swaps): one
-//    256-thread workgroup per (layer, row, head, token tile).  V is a
-//    straight contiguous copy.  K's token range is D/8 rows ("chunks") of
-//    tile*16 contiguous bytes each, which the packed format wants token-major;
-//    the tile is loaded chunk-major (each wave reads 1 KiB contiguous),
-//    transposed at 16-byte granularity through LDS, and stored token-major
-//    (contiguous).  Unpack is the mirror image.  The LDS index is XOR-swizzled
-//    so that both the chunk-major writes and the token-major reads spread a
-//    wave's 16-byte accesses over all banks.
+//  * copy_split -- many tokens per row (prompt layers, chunks, swaps):
+//    256-thread workgroups, each either a K tile or a V run of one (layer,
+//    row, head).  A V workgroup is a straight contiguous copy.  K's token
+//    range is D/8 rows ("chunks") of 16-byte vectors, which the packed format
+//    wants token-major; a K tile is loaded chunk-major (each wave reads
+//    contiguous runs of one chunk row), transposed at 16-byte granularity
+//    through LDS, and stored token-major (contiguous).  Unpack is the mirror
+//    image.  The LDS index is XOR-swizzled so that both the chunk-major
+//    writes and the token-major reads spread a wave's 16-byte accesses over
+//    all banks.
 #include "kvs_internal.h"
 
 #include <algorithm>
@@ -314,17 +315,28 @@ __global__ __launch_bounds__(kThreads) void copy_steps_lds(Geometry g, RowTable 
     }
 }
 
-// One tile = kThreads * PER vectors of K (and as many of V); TT = tile / C
-// tokens.  Element e = tid + p*kThreads of the tile is read as (chunk e/TT,
-// token e%TT) on the cache side (chunk-major) and as (token e/C, chunk e%C)
-// on the packed side (token-major).
-template <int CT, int PER, bool kPack>
-__global__ __launch_bounds__(kThreads) void copy_tiles(Geometry g, RowTable rt)
+// The tile kernel (many tokens per row: prompt layers, chunks, swaps).  Split
+// roles: a row's first g.k_tiles workgroups move K only -- a tile of TTK =
+// 256 * KPER / C tokens of every chunk row, loaded chunk-major (each wave
+// reads contiguous runs of one chunk row), transposed through LDS and
+// stored token-major -- and the others move V only, a straight contiguous
+// copy of 256 * VPER vectors with every load issued before the first store.
+// Against the former tile kernel, whose workgroups moved a K tile and the
+// matching V run together (one vector per thread each for heads of up to 16
+// vectors), measured alone on cold data, median of 20: a BLOOM-176B layer
+// 0.69-0.70 -> 0.73-0.74 of HBM peak packed and 0.69-0.75 -> 0.71-0.72
+// unpacked, a 99,000-token 100K-context row layer 0.71 -> 0.74-0.76 both
+// ways, 48 GPT-2-1.5B layers in one call 0.75 -> 0.78 and 0.73-0.77 ->
+// 0.76-0.77.  Larger tiles (2 or 4 vectors per thread for K, V or both)
+// were slower on 8- and 16-vector heads.
+template <int CT, int KPER, int VPER, bool kPack>
+__global__ __launch_bounds__(kThreads) void copy_split(Geometry g, RowTable rt)
 {
-    constexpr int TV = kThreads * PER;
-    __shared__ u32x4 lds[TV];
+    constexpr int TVK = kThreads * KPER;
+    constexpr int TVV = kThreads * VPER;
+    __shared__ u32x4 lds[TVK];
     const int32_t C = CT ? CT : g.C;
-    const int32_t TT = CT ? TV / CT : g.tile_tokens;
+    const int32_t TTK = CT ? TVK / CT : g.tile_tokens;
 
     int32_t bid = blockIdx.x;
     const int32_t tile = bid % g.tiles_per_row;
@@ -336,69 +348,98 @@ __global__ __launch_bounds__(kThreads) void copy_tiles(Geometry g, RowTable rt)
 
     const int32_t off = rt.off[b];
     const int32_t cnt = rt.off[b + 1] - off;
-    const int32_t t0 = tile * TT;
+    const int64_t unit = ((int64_t)(g.l0 + li) * g.B + b) * g.H + g.h0 + h;
+    const int64_t blk = (int64_t)g.nh * g.T * C;          // one (layer, K|V) block
+    u32x4 *ks_unit = (u32x4 *)(g.stage + 2 * (int64_t)li * blk +
+                               ((int64_t)g.nh * off + (int64_t)h * cnt) * C);
+    const int tid = threadIdx.x;
+
+    if (tile >= g.k_tiles) {
+        const int32_t v0 = (tile - g.k_tiles) * TVV;
+        const int32_t nv = cnt * C;
+        if (v0 >= nv)
+            return;
+        const int32_t n = min(TVV, nv - v0);
+        u32x4 *vc = (u32x4 *)(g.v + (unit * g.Smax + rt.start[b]) * C) + v0;
+        u32x4 *vs = ks_unit + blk + v0;
+        u32x4 r[VPER];
+        if (kPack) {
+            const __amdgpu_buffer_rsrc_t rs = stage_rsrc(vs, (int64_t)n * 16);
+#pragma unroll
+            for (int p = 0; p < VPER; ++p) {
+                const int e = tid + p * kThreads;
+                if (e < n)
+                    r[p] = vc[e];
+            }
+#pragma unroll
+            for (int p = 0; p < VPER; ++p) {
+                const int e = tid + p * kThreads;
+                if (e < n)
+                    stage_store(r[p], rs, e);
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < VPER; ++p) {
+                const int e = tid + p * kThreads;
+                if (e < n)
+                    r[p] = vs[e];
+            }
+#pragma unroll
+            for (int p = 0; p < VPER; ++p) {
+                const int e = tid + p * kThreads;
+                if (e < n)
+                    vc[e] = r[p];
+            }
+        }
+        return;
+    }
+
+    const int32_t t0 = tile * TTK;
     if (t0 >= cnt)
         return;
-    const int32_t nt = min(TT, cnt - t0);
+    const int32_t nt = min(TTK, cnt - t0);
     const int32_t nvec = nt * C;
-    const int32_t s0 = rt.start[b] + t0;
-
-    const int64_t unit = ((int64_t)(g.l0 + li) * g.B + b) * g.H + g.h0 + h;
-    u32x4 *kc = (u32x4 *)(g.k + unit * C * g.Smax + s0);     // chunk c, token i: kc[c*Smax + i]
-    u32x4 *vc = (u32x4 *)(g.v + (unit * g.Smax + s0) * C);   // nvec contiguous vectors
-    const int64_t blk = (int64_t)g.nh * g.T * C;
-    u32x4 *ks = (u32x4 *)(g.stage + 2 * (int64_t)li * blk +
-                          ((int64_t)g.nh * off + (int64_t)h * cnt + t0) * C);
-    u32x4 *vs = ks + blk;                                    // both nvec contiguous vectors
-    const int tid = threadIdx.x;
-    u32x4 kr[PER], vr[PER];
-
+    u32x4 *kc = (u32x4 *)(g.k + unit * C * g.Smax + rt.start[b] + t0);  // chunk c, token i: kc[c*Smax + i]
+    u32x4 *ks = ks_unit + (int64_t)t0 * C;                              // nvec contiguous vectors
+    u32x4 kr[KPER];
     if (kPack) {
-        const __amdgpu_buffer_rsrc_t krs = stage_rsrc(ks, nvec * 16), vrs = stage_rsrc(vs, nvec * 16);
+        const __amdgpu_buffer_rsrc_t krs = stage_rsrc(ks, (int64_t)nvec * 16);
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int e = tid + p * kThreads, c = e / TT, i = e % TT;
+        for (int p = 0; p < KPER; ++p) {
+            const int e = tid + p * kThreads, c = e / TTK, i = e % TTK;
             if (c < C && i < nt)
                 kr[p] = kc[(int64_t)c * g.Smax + i];
-            if (e < nvec)
-                vr[p] = vc[e];
         }
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int e = tid + p * kThreads, c = e / TT, i = e % TT;
+        for (int p = 0; p < KPER; ++p) {
+            const int e = tid + p * kThreads, c = e / TTK, i = e % TTK;
             if (c < C && i < nt)
                 lds[lds_slot<CT>(i, c, C)] = kr[p];
-            if (e < nvec)
-                stage_store(vr[p], vrs, e);
         }
         __syncthreads();
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
+        for (int p = 0; p < KPER; ++p) {
             const int e = tid + p * kThreads;
             if (e < nvec)
                 stage_store(lds[lds_slot<CT>(e / C, e % C, C)], krs, e);
         }
     } else {
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
+        for (int p = 0; p < KPER; ++p) {
             const int e = tid + p * kThreads;
-            if (e < nvec) {
+            if (e < nvec)
                 kr[p] = ks[e];
-                vr[p] = vs[e];
-            }
         }
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
+        for (int p = 0; p < KPER; ++p) {
             const int e = tid + p * kThreads;
-            if (e < nvec) {
+            if (e < nvec)
                 lds[lds_slot<CT>(e / C, e % C, C)] = kr[p];
-                vc[e] = vr[p];
-            }
         }
         __syncthreads();
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int e = tid + p * kThreads, c = e / TT, i = e % TT;
+        for (int p = 0; p < KPER; ++p) {
+            const int e = tid + p * kThreads, c = e / TTK, i = e % TTK;
             if (c < C && i < nt)
                 kc[(int64_t)c * g.Smax + i] = lds[lds_slot<CT>(i, c, C)];
         }
@@ -464,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void copy_paged_small(PagedGeometry g, Ro
     }
 }
 
-// Many tokens per row on a pool: the tile scheme of copy_tiles (K loaded
+// Many tokens per row on a pool: the joint K+V tile scheme (K loaded
 // chunk-major, transposed through LDS, stored token-major), with the tile's
 // block ids staged in LDS first.  Within a block a key chunk row is P*16
 // contiguous bytes, so chunk-major loads stay contiguous per block.
@@ -646,37 +687,53 @@ hipError_t launch_paged_tiles(const PagedGeometry &g, const RowTable &rt, int64_
     return e;
 }
 
-// Vectors per thread of the tile kernel: 256-vector tiles (one per thread)
-// for heads of up to 16 vectors -- many small workgroups, so that the last
-// of them leave the CUs evenly loaded: measured against two per thread,
-// 3-17% faster inside the steps and 1-4% faster alone on 8- and 16-vector
-// heads -- and 1024-vector tiles for wider heads, so that a tile still
-// spans at least 8 tokens.
-constexpr int tile_per_thread(int32_t C) { return C <= 16 ? 1 : 4; }
+// Vectors per thread of the split-role kernel for K and for V: one each for
+// heads of up to 32 vectors; four K vectors per thread for wider heads, so
+// that a K tile still spans 8 or more tokens.  Measured alone on 256-, 512-
+// and 1024-dim heads (4000 tokens, cold data): one vector per thread reached
+// 0.76/0.75 of peak (pack/unpack) at 256 dims but 0.65/0.67 at 512 and
+// 0.44/0.42 at 1024 (2-token K tiles); four K vectors 0.74/0.71, 0.72/0.71
+// and 0.72/0.71; four for both 0.67-0.69; the former joint K+V tiles of
+// 1024 vectors 0.70/0.68, 0.70/0.68-0.69, 0.69-0.70/0.68.
+struct SplitMode {
+    int kper, vper;
+};
+
+SplitMode split_mode(int32_t C)
+{
+    return C <= 32 ? SplitMode{1, 1} : SplitMode{4, 1};
+}
+
+template <int CT, bool kPack>
+hipError_t launch_split_c(const SplitMode &m, const Geometry &g, const RowTable &rt, dim3 grid,
+                          hipStream_t s, const LaunchTimer &t)
+{
+    const dim3 block(kThreads);
+    if constexpr (CT == 0 || CT <= 32)
+        if (m.kper == 1 && m.vper == 1)
+            return launch(copy_split<CT, 1, 1, kPack>, grid, block, 0, s, t, g, rt);
+    if constexpr (CT == 0 || CT > 32)
+        if (m.kper == 4 && m.vper == 1)
+            return launch(copy_split<CT, 4, 1, kPack>, grid, block, 0, s, t, g, rt);
+    return hipErrorInvalidValue;
+}
 
 template <bool kPack>
-hipError_t launch_tiles_rt(const Geometry &g, const RowTable &rt, int64_t blocks, hipStream_t s,
-                           const LaunchTimer &t)
+hipError_t launch_split(const SplitMode &m, const Geometry &g, const RowTable &rt, int64_t blocks,
+                        hipStream_t s, const LaunchTimer &t)
 {
-    const dim3 grid((unsigned)blocks), block(kThreads);
-    hipError_t e;
+    const dim3 grid((unsigned)blocks);
     switch (g.C) {
-    case 1: e = launch(copy_tiles<1, 1, kPack>, grid, block, 0, s, t, g, rt); break;
-    case 2: e = launch(copy_tiles<2, 1, kPack>, grid, block, 0, s, t, g, rt); break;
-    case 4: e = launch(copy_tiles<4, 1, kPack>, grid, block, 0, s, t, g, rt); break;
-    case 8: e = launch(copy_tiles<8, 1, kPack>, grid, block, 0, s, t, g, rt); break;
-    case 16: e = launch(copy_tiles<16, 1, kPack>, grid, block, 0, s, t, g, rt); break;
-    case 32: e = launch(copy_tiles<32, 4, kPack>, grid, block, 0, s, t, g, rt); break;
-    case 64: e = launch(copy_tiles<64, 4, kPack>, grid, block, 0, s, t, g, rt); break;
-    case 128: e = launch(copy_tiles<128, 4, kPack>, grid, block, 0, s, t, g, rt); break;
-    default:
-        if (tile_per_thread(g.C) == 1)
-            e = launch(copy_tiles<0, 1, kPack>, grid, block, 0, s, t, g, rt);
-        else
-            e = launch(copy_tiles<0, 4, kPack>, grid, block, 0, s, t, g, rt);
-        break;
+    case 1: return launch_split_c<1, kPack>(m, g, rt, grid, s, t);
+    case 2: return launch_split_c<2, kPack>(m, g, rt, grid, s, t);
+    case 4: return launch_split_c<4, kPack>(m, g, rt, grid, s, t);
+    case 8: return launch_split_c<8, kPack>(m, g, rt, grid, s, t);
+    case 16: return launch_split_c<16, kPack>(m, g, rt, grid, s, t);
+    case 32: return launch_split_c<32, kPack>(m, g, rt, grid, s, t);
+    case 64: return launch_split_c<64, kPack>(m, g, rt, grid, s, t);
+    case 128: return launch_split_c<128, kPack>(m, g, rt, grid, s, t);
+    default: return launch_split_c<0, kPack>(m, g, rt, grid, s, t);
     }
-    return e;
 }
 
 // Tokens per tile of a kernel whose threads move `per` vectors each.
@@ -780,8 +837,11 @@ int launch_copy(bool pack, const Geometry &g0, const RowTable &rt, int32_t max_c
     if (small) {
         per_layer = ((int64_t)g.nb * g.nh * g.C + kThreads - 1) / kThreads;
     } else {
-        g.tile_tokens = tile_tokens_for(g.C, tile_per_thread(g.C));
-        g.tiles_per_row = (max_count + g.tile_tokens - 1) / g.tile_tokens;
+        const SplitMode m = split_mode(g.C);
+        g.tile_tokens = tile_tokens_for(g.C, m.kper);
+        g.k_tiles = (max_count + g.tile_tokens - 1) / g.tile_tokens;
+        const int32_t tvv = kThreads * m.vper;
+        g.tiles_per_row = g.k_tiles + (int32_t)(((int64_t)max_count * g.C + tvv - 1) / tvv);
         per_layer = (int64_t)g.nb * g.nh * g.tiles_per_row;
     }
     // A launch covers whole layers.  Keep every grid within 2^31-1 blocks and,
@@ -810,8 +870,9 @@ int launch_copy(bool pack, const Geometry &g0, const RowTable &rt, int32_t max_c
                 e = launch(copy_rows_small<false>, grid, block, 0, s, t, gl, rt);
         } else {
             const int64_t blocks = (int64_t)gl.nl * per_layer;
-            e = pack ? launch_tiles_rt<true>(gl, rt, blocks, s, t)
-                     : launch_tiles_rt<false>(gl, rt, blocks, s, t);
+            const SplitMode m = split_mode(g.C);
+            e = pack ? launch_split<true>(m, gl, rt, blocks, s, t)
+                     : launch_split<false>(m, gl, rt, blocks, s, t);
         }
         profile_commit(t, name, 2 * payload, e == hipSuccess);
         if (e != hipSuccess)

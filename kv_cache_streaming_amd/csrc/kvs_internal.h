@@ -29,6 +29,7 @@ struct Geometry {
     int32_t h0, nh;         // head range [h0, h0 + nh) moved; the packed format has nh heads
     int32_t tiles_per_row;  // tile kernel: tiles per row (ceil(max count / tile tokens))
     int32_t tile_tokens;    // tile kernel: tokens per tile
+    int32_t k_tiles;        // split tile kernel: the first k_tiles tiles of a row move K, the rest V
     int32_t b0, nb;         // pack/unpack grids cover rows [b0, b0 + nb) (set by the launcher)
     int64_t T;              // sum of counts
 };

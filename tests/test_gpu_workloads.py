@@ -56,6 +56,15 @@ def layer_host(t, w, l):
     return t.view(w.L, -1)[l].cpu().numpy().view(np.uint16).copy()
 
 
+def row_digest(t, w, l, b):
+    """Two integer sums over row b of layer l of a flat device cache tensor
+    (plain and position-weighted), as a fingerprint of its contents."""
+    import torch
+    x = t.view(w.L, w.B, -1)[l, b].view(torch.int32).to(torch.int64)
+    wgt = torch.arange(x.numel(), device=x.device, dtype=torch.int64) % 65521 + 1
+    return int(x.sum().item()), int((x * wgt).sum().item())
+
+
 def one_layer(w):
     return (1, w.B, w.H, w.D, w.Smax)
 
@@ -448,10 +457,42 @@ def test_gqa_100k_long_context(kv):
         K1, V1 = host_layer(l)
         want = oracle.pack(one_layer(w), K1, V1, 0, 1, [0] * B, count)
         assert np.array_equal(sv[l * per:(l + 1) * per], want), f"row swap-out layer {l}"
+    # every layer of the image: the row's own region of each layer is a cache
+    # of one row, so the oracle packs it from that region alone
+    row_dims = (1, 1, w.H, w.D, w.Smax)
+    for l in range(w.L):
+        Kr = dk.view(w.L, B, -1)[l, bstar].cpu().numpy().view(np.uint16)
+        Vr = dv.view(w.L, B, -1)[l, bstar].cpu().numpy().view(np.uint16)
+        want = oracle.pack(row_dims, Kr, Vr, 0, 1, [0], [count[bstar]])
+        assert np.array_equal(sv[l * per:(l + 1) * per], want), f"row swap-out layer {l}"
+    # the row as it was (device copy) and digests of every other row of every
+    # layer, to compare after the swap-in
+    saved_k = dk.view(w.L, B, -1)[:, bstar, :].clone()
+    saved_v = dv.view(w.L, B, -1)[:, bstar, :].clone()
+    others = [b for b in range(B) if b != bstar]
+    digest_before = [row_digest(t, w, l, b) for t in (dk, dv) for l in range(w.L) for b in others]
     dk.view(w.L, B, -1)[:, bstar, :].fill_(0x7E7E)
     dv.view(w.L, B, -1)[:, bstar, :].fill_(0x7E7E)
     ei.swap_in(dk, dv, 0, w.L, [0] * B, count, shost, total)
     torch.cuda.synchronize()
+    # the swapped row is back in every layer: its tokens [0, len) from the
+    # image, the positions past len still the sentinel; no other row changed
+    n = count[bstar]
+    for t, saved in ((dk, saved_k), (dv, saved_v)):
+        got = t.view(w.L, B, -1)[:, bstar, :]
+        if t is dk:   # K row region: [H, D/8, Smax, 8], positions on the third axis
+            g4 = got.view(w.L, w.H * w.D // 8, w.Smax, 8)
+            s4 = saved.view(w.L, w.H * w.D // 8, w.Smax, 8)
+            assert torch.equal(g4[:, :, :n], s4[:, :, :n]), "row swap-in K, tokens"
+            assert bool((g4[:, :, n:] == 0x7E7E).all()), "row swap-in K wrote past len"
+        else:         # V row region: [H, Smax, D]
+            g3 = got.view(w.L, w.H, w.Smax, w.D)
+            s3 = saved.view(w.L, w.H, w.Smax, w.D)
+            assert torch.equal(g3[:, :, :n], s3[:, :, :n]), "row swap-in V, tokens"
+            assert bool((g3[:, :, n:] == 0x7E7E).all()), "row swap-in V wrote past len"
+    del saved_k, saved_v
+    digest_after = [row_digest(t, w, l, b) for t in (dk, dv) for l in range(w.L) for b in others]
+    assert digest_after == digest_before, "row swap-in touched another row"
     for l in (0, 31, 59):
         K1, V1 = host_layer(l)
         ek = K1.copy().reshape(B, -1)
