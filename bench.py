@@ -70,8 +70,6 @@ PCIE_PEAK_GBPS = 63.0          # PCIe 5.0 x16, per direction
 
 RING_GATHER = 1   # kv_ring_gather of the rings the steps use (set from --ring-gather)
 WHOLE_CALLS = True   # swaps of complete images as one call each (set from --swap-calls)
-OUT_STREAMS = 2      # device-to-host copy streams of the long-context step (--out-streams)
-ROW_TRANSPORT = None  # transport of the long-context step's row swap (--row-transport)
 
 
 def counters_file(workload, kernel_name):
@@ -100,9 +98,16 @@ def parse_args():
     ap.add_argument("--row-transport", choices=("auto", "kernel", "runtime", "dma", "dma_out",
                                                 "engine"), default=None,
                     help="gqa-100k: transport of the row swap (default: --transport)")
-    ap.add_argument("--out-streams", type=int, choices=(1, 2), default=2,
-                    help="gqa-100k: the row swap-out and the prompt streaming share one "
-                         "device-to-host copy stream (1) or have one each (2)")
+    ap.add_argument("--prompt-engines", default=None,
+                    help="gqa-100k with --transport engine: comma-separated DMA engines (0-3, or "
+                         "-1 for an idle one at each copy) of the prompt-streaming handles; "
+                         "chunks alternate over the handles, each with its own copy stream "
+                         "(bloom-176b-10l: the same for its swap-out handles, by layer)")
+    ap.add_argument("--row-engines", default=None,
+                    help="gqa-100k with --row-transport engine: DMA engines of the row swap-out "
+                         "handles (the layers split into contiguous ranges over them)")
+    ap.add_argument("--row-link-blocks", type=int, default=None,
+                    help="gqa-100k: link-copy workgroups of the row swap-out (KV_OPT_LINK_BLOCKS)")
     ap.add_argument("--compute-streams", type=int, choices=(1, 2), default=2,
                     help="gpt2 shapes: packs and unpacks of the two link directions on one "
                          "compute stream (1) or one each (2)")
@@ -374,9 +379,12 @@ def _duplex_layers(eng_o, eng_i, src, dst, L, start, count, img_out, img_in, per
                    s_in, packed):
     """Layer-pipelined swap-out of `src` || swap-in into `dst`, where `dst` may be
     the region `src` is leaving: the unpack of layer l waits for the pack of
-    layer l (event `packed[l]`), nothing else couples the two directions."""
+    layer l (event `packed[l]`), nothing else couples the two directions.
+    `eng_o` may be a list of swap-out handles: layers alternate over them."""
+    outs = eng_o if isinstance(eng_o, list) else [eng_o]
     for l in range(L):
-        eng_o.swap_out(src[0], src[1], l, 1, start, count, img_out + l * per_layer, per_layer, s_out)
+        outs[l % len(outs)].swap_out(src[0], src[1], l, 1, start, count, img_out + l * per_layer,
+                                     per_layer, s_out)
         packed[l].record(s_out)
         s_in.wait_event(packed[l])
         eng_i.swap_in(dst[0], dst[1], l, 1, start, count, img_in + l * per_layer, per_layer, s_in)
@@ -479,7 +487,10 @@ class SwapStep:
     layer's unpack waiting only for that layer's pack (both link directions at
     once)."""
 
-    def __init__(self, w, swap_bank_bytes, transport=0):
+    def __init__(self, w, swap_bank_bytes, transport=0, out_engines=None):
+        """out_engines: with the engine transport, the DMA engines of the
+        swap-out handles (layers alternate over them, each handle with its own
+        copy stream); None: one handle, an idle engine at each copy."""
         import torch
 
         import kv_cache_streaming_amd as kv
@@ -500,6 +511,14 @@ class SwapStep:
         sb = swap_bank_bytes
         self.eng_o = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb, self.s["d2h"],
                                transport)
+        self.eng_out = [self.eng_o]
+        if out_engines and transport == TRANSPORTS["engine"]:
+            self.eng_o.set_option(kv.KV_OPT_DMA_ENGINE, out_engines[0])
+            for e in out_engines[1:]:
+                h = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb,
+                              torch.cuda.Stream(), transport)
+                h.set_option(kv.KV_OPT_DMA_ENGINE, e)
+                self.eng_out.append(h)
         self.eng_i = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb, self.s["h2d"],
                                transport)
         self.packed = [torch.cuda.Event() for _ in range(L)]
@@ -537,7 +556,7 @@ class SwapStep:
         self.r += 1
         x = r % N
         other = self.slots[(r + 1) % 2]          # holds x-1, receives x+1
-        _duplex_layers(self.eng_o, self.eng_i, other, other, self.w.L, self.rows_start, self.rows,
+        _duplex_layers(self.eng_out, self.eng_i, other, other, self.w.L, self.rows_start, self.rows,
                        self.img[(x - 1) % N], self.img[(x + 1) % N], self.per_layer,
                        self.s["out"], self.s["in"], self.packed)
         self.torch.cuda.synchronize()
@@ -633,13 +652,29 @@ class LongStep:
     row streamed out in 4096-token chunks per layer, and 64 decode steps
     through a 16-slot staging ring restored into the cache."""
 
-    def __init__(self, w, swap_bank_bytes, transport=0):
+    def __init__(self, w, swap_bank_bytes, transport=0, row_transport=None, prompt_engines=None,
+                 row_link_blocks=None, row_engines=None):
+        """row_transport: the row swap's kv_transport (None: the workload's
+        default, else `transport`); prompt_engines: DMA engines of the
+        prompt-streaming handles with the engine transport (None: the
+        workload's default); row_link_blocks: link-copy workgroups of the
+        row swap-out (None: the workload's default); row_engines: with the
+        engine transport for the row, the DMA engines of its swap-out handles
+        (the layers split into as many contiguous ranges, one call each)."""
         import torch
 
         import kv_cache_streaming_amd as kv
         import synth
         self.kv, self.w, self.torch = kv, w, torch
         L, B = w.L, w.B
+        if row_transport is None:
+            row_transport = TRANSPORTS.get(DEFAULT_ROW_TRANSPORT.get(w.name), transport)
+        if prompt_engines is None:
+            prompt_engines = [int(x) for x in DEFAULT_PROMPT_ENGINES.get(w.name, "-1").split(",")]
+        if row_link_blocks is None:
+            row_link_blocks = DEFAULT_ROW_LINK_BLOCKS.get(w.name, 0)
+        if row_engines is None:
+            row_engines = [int(x) for x in DEFAULT_ROW_ENGINES.get(w.name, "-1").split(",")]
         self.lay = kv.kv_layout_init(*w.dims, w.dtype)
         self.lens = [int(x) for x in synth.row_lengths(w)]
         self.positions = [list(map(int, p)) for p in synth.decode_positions(w)]
@@ -654,8 +689,16 @@ class LongStep:
             self.chunks.append((c0, kv.kv_pack_bytes(self.lay, 1, cnt)))
         self.prompt_layer = sum(c[1] for c in self.chunks)
         cb = max(c[1] for c in self.chunks)
-        self.eng_p = kv.KvSwap(self.lay, _bank(torch, cb), _bank(torch, cb), cb, self.s["d2h"],
-                               transport)
+        # prompt-streaming handles: chunks alternate over them, each with its
+        # own copy stream, so that a handle's next copy is already queued on
+        # its DMA engine while the other's runs
+        self.eng_p = []
+        for i, e in enumerate(prompt_engines if transport == TRANSPORTS["engine"] else [-1]):
+            cs = self.s["d2h"] if i == 0 else torch.cuda.Stream()
+            h = kv.KvSwap(self.lay, _bank(torch, cb), _bank(torch, cb), cb, cs, transport)
+            if transport == TRANSPORTS["engine"]:
+                h.set_option(kv.KV_OPT_DMA_ENGINE, e)
+            self.eng_p.append(h)
         # layer l's chunks land in host region l % 2, one layer each: the host
         # buffer a prompt worker forwards from (the whole prompt, 60 GB at these
         # lengths, need not stay page-locked on this side)
@@ -668,9 +711,16 @@ class LongStep:
         self.row_image = L * self.row_layer
         # a bank holds at least one row of one layer (the engine splits at rows)
         sb = max(swap_bank_bytes, -(-self.row_layer // (1 << 20)) << 20)
-        rt = transport if ROW_TRANSPORT is None else ROW_TRANSPORT
-        self.eng_o = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb,
-                               self.s["d2h_row" if OUT_STREAMS == 2 else "d2h"], rt)
+        rt = row_transport
+        self.eng_o = []
+        for i, e in enumerate(row_engines if rt == TRANSPORTS["engine"] else [-1]):
+            cs = self.s["d2h_row"] if i == 0 else torch.cuda.Stream()
+            h = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb, cs, rt)
+            if rt == TRANSPORTS["engine"]:
+                h.set_option(kv.KV_OPT_DMA_ENGINE, e)
+            if row_link_blocks:
+                h.set_option(kv.KV_OPT_LINK_BLOCKS, row_link_blocks)
+            self.eng_o.append(h)
         # the one-row slot: the row's packed image is the same bytes in a cache
         # of one row (the other rows move no tokens)
         self.lay1 = kv.kv_layout_init(L, 1, w.H, w.D, w.Smax, w.dtype)
@@ -710,16 +760,23 @@ class LongStep:
         torch, w = self.torch, self.w
         out, inn = self.k % 2, (self.k + 1) % 2
         self.k += 1
-        self.eng_o.swap_out(self.A[0], self.A[1], 0, w.L, self.row_start, self.row_count,
-                            self.row_host[out], self.row_image, self.s["out"])
+        n = len(self.eng_o)
+        for i, h in enumerate(self.eng_o):
+            l0, l1 = w.L * i // n, w.L * (i + 1) // n
+            h.swap_out(self.A[0], self.A[1], l0, l1 - l0, self.row_start, self.row_count,
+                       self.row_host[out].data_ptr() + l0 * self.row_layer,
+                       (l1 - l0) * self.row_layer, self.s["out"])
         self.eng_i.swap_in(self.slot1[0], self.slot1[1], 0, w.L, [0], [max(self.row_count)],
                            self.row_host[inn], self.row_image, self.s["in"])
+        k, n = 0, len(self.eng_p)
         for l in range(w.L):
             off = self.prompt_host[l % 2].data_ptr()
             for c0, nb in self.chunks:
-                self.eng_p.stream_prompt_layer(self.A[0], self.A[1], l, c0, w.chunk_tokens,
-                                               self.lens, off, nb, self.s["p"])
+                self.eng_p[k % n].stream_prompt_layer(self.A[0], self.A[1], l, c0,
+                                                      w.chunk_tokens, self.lens, off, nb,
+                                                      self.s["p"])
                 off += nb
+                k += 1
         st = self.s["t"]
         self.ring.reset()
         for pos in self.positions:
@@ -745,12 +802,23 @@ STEPS = {"gpt2-small-tiny": StreamStep, "gpt2-1.5b": StreamStep, "opt-66b-16l": 
 # measured fastest for that step (ties go to the one that leaves the tile
 # kernels more of HBM).  GPT-2-1.5B: with the named-engine device->host leg
 # the step takes 107-110 ms against 108-115 ms with the link-copy kernel
-# (alternating runs on one box), with the tile kernels at 0.63-0.65 of peak
-# instead of 0.54-0.56; the OPT-66B ring runs 7% faster and the 100K-context
-# step 2% faster with the link-copy kernel.
+# (alternating runs on one box), with the tile kernels at 0.63-0.66 of peak
+# instead of 0.54-0.56; the OPT-66B ring runs 7% faster and the BLOOM step
+# 2-3% faster with the link-copy kernel.  The 100K-context step streams its
+# prompt on DMA engine 0 through two handles (the next chunk's copy is
+# queued on the engine while the other runs) and swaps its row with the
+# link-copy kernel from 12 workgroups: 1491 ms (66.0 GB/s) with the prompt
+# packs at 0.55 of HBM peak, against 1477 ms (66.7 GB/s) and 0.32 with the
+# link-copy kernel for every outgoing copy (two runs each, one box).
 DEFAULT_TRANSPORT = {"gpt2-small-tiny": "auto", "gpt2-1.5b": "engine", "opt-66b-16l": "auto",
-                     "bloom-176b-10l": "auto", "gqa-100k": "auto"}
+                     "bloom-176b-10l": "auto", "gqa-100k": "engine"}
 TRANSPORTS = {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3, "dma_out": 4, "engine": 5}
+# the long-context step's row swap transport (absent: the step's transport),
+# its prompt handles' DMA engines and its row swap-out's link-copy workgroups
+DEFAULT_ROW_TRANSPORT = {"gqa-100k": "auto"}
+DEFAULT_PROMPT_ENGINES = {"gqa-100k": "0,0"}
+DEFAULT_ROW_LINK_BLOCKS = {"gqa-100k": 12}
+DEFAULT_ROW_ENGINES = {}
 
 def link_ceiling(step, kv, transport, target_bytes=4 << 30, reps=3):
     """GB/s the host link reaches through this library with `transport`, each
@@ -1258,16 +1326,31 @@ def main():
     import synth
     w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
-    global RING_GATHER, WHOLE_CALLS, OUT_STREAMS, ROW_TRANSPORT
+    global RING_GATHER, WHOLE_CALLS
     WHOLE_CALLS = args.swap_calls == "whole"
-    OUT_STREAMS = args.out_streams
-    if args.row_transport is not None:
-        ROW_TRANSPORT = TRANSPORTS[args.row_transport]
     RING_GATHER = {"flush": kv.KV_RING_GATHER_AT_FLUSH, "each": kv.KV_RING_GATHER_EACH_STEP}[
         args.ring_gather]
     if args.transport is None:
         args.transport = DEFAULT_TRANSPORT[w.name]
-    step = STEPS[w.name](w, args.swap_bank_mib << 20, TRANSPORTS[args.transport])
+    if STEPS[w.name] is LongStep:
+        if args.row_transport is None:
+            args.row_transport = DEFAULT_ROW_TRANSPORT.get(w.name, args.transport)
+        if args.prompt_engines is None:
+            args.prompt_engines = DEFAULT_PROMPT_ENGINES.get(w.name, "-1")
+        if args.row_link_blocks is None:
+            args.row_link_blocks = DEFAULT_ROW_LINK_BLOCKS.get(w.name, 0)
+        if args.row_engines is None:
+            args.row_engines = DEFAULT_ROW_ENGINES.get(w.name, "-1")
+        step = LongStep(w, args.swap_bank_mib << 20, TRANSPORTS[args.transport],
+                        TRANSPORTS[args.row_transport],
+                        [int(x) for x in args.prompt_engines.split(",")], args.row_link_blocks,
+                        [int(x) for x in args.row_engines.split(",")])
+    elif STEPS[w.name] is SwapStep:
+        step = SwapStep(w, args.swap_bank_mib << 20, TRANSPORTS[args.transport],
+                        [int(x) for x in args.prompt_engines.split(",")]
+                        if args.prompt_engines else None)
+    else:
+        step = STEPS[w.name](w, args.swap_bank_mib << 20, TRANSPORTS[args.transport])
     torch.cuda.synchronize()
 
     if args.calibrate_copy_mib:
@@ -1359,8 +1442,9 @@ def main():
         detail["link_ceiling_GBps"] = ceil
         for name in ("d2h", "h2d"):
             directions[name]["frac_of_ceiling"] = round(directions[name]["GBps"] / ceil[name], 4)
-        if ROW_TRANSPORT is not None and ROW_TRANSPORT != TRANSPORTS[args.transport]:
-            detail["link_ceiling_row_transport_GBps"] = link_ceiling(step, kv, ROW_TRANSPORT)
+        if args.row_transport not in (None, args.transport):
+            detail["link_ceiling_row_transport_GBps"] = link_ceiling(
+                step, kv, TRANSPORTS[args.row_transport])
         if isinstance(step, StreamStep):
             detail["decode_step_us"] = decode_step_us(step, kv)
             detail["hbm_copy_ceiling_GBps"] = round(hbm_copy_ceiling(torch), 1)
@@ -1393,8 +1477,11 @@ def main():
                        "swap_bank_mib": args.swap_bank_mib,
                        "transport": args.transport, "ring_gather": args.ring_gather,
                        "compute_streams": args.compute_streams, "swap_calls": args.swap_calls,
-                       "out_streams": args.out_streams,
-                       "row_transport": args.row_transport or args.transport,
+                       **({"row_transport": args.row_transport,
+                           "prompt_engines": args.prompt_engines,
+                           "row_engines": args.row_engines,
+                           "row_link_blocks": args.row_link_blocks}
+                          if isinstance(step, LongStep) else {}),
                        "hw_queues": int(os.environ["GPU_MAX_HW_QUEUES"])},
             "roofline": roofline, "cpu_baseline": cpu, "detail": detail}
     # the metric names two figures: the in-step pack/unpack rate (of the

@@ -303,8 +303,8 @@ typedef struct kv_swap kv_swap;
  *                      handle waits until its copies are done.  These copies
  *                      cannot be captured into a graph, and a profiler that
  *                      runs one dispatch at a time (hardware counter
- *                      collection) cannot order them: collect counters with
- *                      another transport.
+ *                      collection) cannot order them: create then refuses
+ *                      the transport (collect counters with another one).
  * Measured on MI355X: DMA copies in both directions at once run at full
  * duplex when one direction moves large (bank-sized) chunks, but fall to
  * about one direction's rate when both move small dependent chunks (one
@@ -323,10 +323,41 @@ typedef enum kv_transport {
 } kv_transport;
 
 /* bank0/bank1: caller-owned device banks of bank_bytes each; `copy`: the
- * stream that carries the transfers; `transport`: a kv_transport. */
+ * stream that carries the transfers; `transport`: a kv_transport.
+ * Returns KV_EINVAL for KV_XFER_ENGINE when kernel dispatches are
+ * serialised (AMD_SERIALIZE_KERNEL set, or ROCPROF_COUNTER_COLLECTION as
+ * rocprofv3 sets it for hardware counters): the stream's wait on a DMA
+ * copy would then never end. */
 int kv_swap_create(kv_swap **out, const kv_layout *lay, void *bank0, void *bank1,
                    int64_t bank_bytes, hipStream_t copy, int32_t transport);
+/* Waits until the handle's DMA copies are done; KV_EHIP if one was still
+ * running after ten seconds (its signals are then left allocated). */
 int kv_swap_destroy(kv_swap *e);
+
+/* Per-handle settings of the link leg, for swap engines and rings; they
+ * apply to copies enqueued after the call.
+ *   KV_OPT_DMA_ENGINE  -- KV_XFER_ENGINE handles only: -1 (the default)
+ *                         takes, at each copy, one of the four fast engines
+ *                         the runtime reports idle; 0..3 always uses that
+ *                         engine.  On MI355X the engines differ in what
+ *                         they leave to co-running kernels: with the
+ *                         100K-context step's prompt streaming on engine 0
+ *                         its pack kernels kept 0.64 of HBM peak, on
+ *                         engines 2 or 3 0.50-0.53 (on engine 1 the step
+ *                         ran 25% slower).
+ *   KV_OPT_LINK_BLOCKS -- workgroups of the link-copy kernel's
+ *                         device->host copies (KV_XFER_AUTO, KV_XFER_KERNEL);
+ *                         0 (the default) means 8, at most 1024.  More
+ *                         workgroups move the copy faster when it shares
+ *                         the link with DMA copies; fewer leave co-running
+ *                         kernels more of HBM.
+ * KV_EINVAL for an unknown option, a value out of range, or an engine
+ * setting on a handle of another transport. */
+typedef enum kv_option {
+    KV_OPT_DMA_ENGINE = 1,
+    KV_OPT_LINK_BLOCKS = 2
+} kv_option;
+int kv_swap_set_option(kv_swap *e, int32_t option, int64_t value);
 
 /* Swap-out: pack the selected region (kernels on `compute`, so they see the
  * cache as of the call) and copy it to `host` (pinned) on the copy stream.
@@ -414,7 +445,10 @@ typedef struct kv_ring kv_ring;
 int kv_ring_create(kv_ring **out, const kv_layout *lay, int32_t R,
                    void *bank0, void *bank1, int64_t bank_bytes,
                    void *host, int64_t host_bytes, hipStream_t copy, int32_t transport);
+/* As kv_swap_destroy. */
 int kv_ring_destroy(kv_ring *r);
+/* As kv_swap_set_option. */
+int kv_ring_set_option(kv_ring *r, int32_t option, int64_t value);
 
 /* One decode step: pos is int32[B], every pos_b in [0, Smax).  The step is
  * packed from (k, v) on `compute` at this call, or, in gather-at-flush mode,

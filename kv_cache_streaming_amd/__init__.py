@@ -27,6 +27,7 @@ KV_OK, KV_EINVAL, KV_ERANGE, KV_ESIZE, KV_EHIP, KV_EBUSY = 0, -1, -2, -3, -4, -5
 KV_F16, KV_BF16 = 0, 1
 KV_XFER_AUTO, KV_XFER_KERNEL, KV_XFER_RUNTIME, KV_XFER_DMA, KV_XFER_DMA_OUT, KV_XFER_ENGINE = 0, 1, 2, 3, 4, 5
 KV_RING_GATHER_EACH_STEP, KV_RING_GATHER_AT_FLUSH = 0, 1
+KV_OPT_DMA_ENGINE, KV_OPT_LINK_BLOCKS = 1, 2
 KV_MAX_ROWS = 256
 STATUS_NAMES = {0: "KV_OK", -1: "KV_EINVAL", -2: "KV_ERANGE", -3: "KV_ESIZE",
                 -4: "KV_EHIP", -5: "KV_EBUSY"}
@@ -119,6 +120,8 @@ _SIGNATURES = {
     "kv_stream_in": (ctypes.c_int, [_LAY, _PART, _P, _P, _PART, _P, _P, _P, _I64, _P]),
     "kv_swap_create": (ctypes.c_int, [ctypes.POINTER(_P), _LAY, _P, _P, _I64, _P, _I32]),
     "kv_swap_destroy": (ctypes.c_int, [_P]),
+    "kv_swap_set_option": (ctypes.c_int, [_P, _I32, _I64]),
+    "kv_ring_set_option": (ctypes.c_int, [_P, _I32, _I64]),
     "kv_swap_out": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
     "kv_swap_in": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
     "kv_stream_prompt_layer": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _P]),
@@ -435,6 +438,9 @@ class KvSwap:
         except KvError:
             pass
 
+    def set_option(self, option: int, value: int) -> None:
+        _check(_lib.kv_swap_set_option(self._h, option, value), "kv_swap_set_option")
+
     def swap_out(self, k, v, layer_begin, layer_count, start, count, host, host_bytes=None,
                  compute=None, done=None):
         st, ct = _Rows(start, self.lay.B, "start"), _Rows(count, self.lay.B, "count")
@@ -478,6 +484,14 @@ def kv_swap_create(lay, bank0, bank1, bank_bytes=None, copy_stream=None,
 
 def kv_swap_destroy(e: KvSwap) -> None:
     e.close()
+
+
+def kv_swap_set_option(e: KvSwap, option: int, value: int) -> None:
+    e.set_option(option, value)
+
+
+def kv_ring_set_option(r: "KvRing", option: int, value: int) -> None:
+    r.set_option(option, value)
 
 
 def kv_swap_out(e: KvSwap, *args, **kw) -> None:
@@ -541,6 +555,9 @@ class KvRing:
 
     def set_gather(self, mode: int) -> None:
         _check(_lib.kv_ring_set_gather(self._h, mode), "kv_ring_set_gather")
+
+    def set_option(self, option: int, value: int) -> None:
+        _check(_lib.kv_ring_set_option(self._h, option, value), "kv_ring_set_option")
 
     @property
     def steps(self) -> int:

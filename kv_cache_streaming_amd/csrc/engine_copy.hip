@@ -25,7 +25,6 @@
 
 #include <atomic>
 #include <chrono>
-#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -135,6 +134,7 @@ struct Slot {
 struct EngineCopier {
     HsaAgents agents;
     uint32_t engine = 0;
+    bool pinned = false;           // always `engine`, never another idle one
     std::vector<Slot *> slots;
 };
 
@@ -164,15 +164,6 @@ int engine_copier_create(EngineCopier **out)
     if (hsa_amd_memory_copy_engine_status(a.cpu, a.gpu, &mask) != HSA_STATUS_SUCCESS)
         mask = 0;
     const uint32_t first = g_next_engine.fetch_add(1);
-    // KV_ENGINE_ORDER (tuning): engine of the i-th copier, e.g. "0,2,1,3"
-    if (const char *order = std::getenv("KV_ENGINE_ORDER")) {
-        uint32_t n = 0;
-        for (const char *q = order; *q; ++q)
-            if (*q >= '0' && *q <= '3' && n++ == first % 8) {
-                c->engine = kFastEngines[*q - '0'];
-                break;
-            }
-    }
     for (uint32_t i = 0; i < 4 && !c->engine; ++i) {
         const uint32_t e = kFastEngines[(first + i) % 4];
         if (mask & e)
@@ -182,6 +173,15 @@ int engine_copier_create(EngineCopier **out)
         c->engine = kFastEngines[first % 4];
     *out = c;
     return KV_OK;
+}
+
+void engine_copier_pin(EngineCopier *c, int32_t engine)
+{
+    if (!c)
+        return;
+    c->pinned = engine >= 0 && engine < 4;
+    if (c->pinned)
+        c->engine = kFastEngines[engine];
 }
 
 int engine_copier_destroy(EngineCopier *c)
@@ -307,56 +307,16 @@ int engine_copy_to_host(EngineCopier *c, void *dst_host, const void *src_dev, in
     if (hsa_amd_memory_copy_engine_status(c->agents.cpu, c->agents.gpu, &idle) !=
         HSA_STATUS_SUCCESS)
         idle = 0;
-    static const bool fixed = [] {
-        const char *v = std::getenv("KV_ENGINE_FIXED");
-        return v && std::atoi(v) > 0;
-    }();
-    if (!fixed && !(idle & c->engine))
+    if (!c->pinned && !(idle & c->engine))
         for (uint32_t e : kFastEngines)
             if (idle & e) {
                 c->engine = e;
                 break;
             }
-    // experimental: halves of a large copy on a pair of engines (0+2 or 1+3)
-    static const int split = [] {
-        const char *v = std::getenv("KV_ENGINE_SPLIT");
-        return v ? std::atoi(v) : 0;
-    }();
-    if (split && bytes >= (4 << 20)) {
-        uint32_t a = c->engine, b = 0;
-        for (uint32_t p = 0; p < 2 && !b; ++p) {
-            const uint32_t e0 = kFastEngines[p], e1 = kFastEngines[p + 2];
-            if ((idle & e0) && (idle & e1)) {
-                a = e0;
-                b = e1;
-            }
-        }
-        if (!b)
-            b = (a == kFastEngines[0] || a == kFastEngines[1]) ? a << 2 : a >> 2;
-        const int64_t half = (bytes / 2) & ~(int64_t)4095;
-        hsa_signal_store_relaxed(slot->done, 2);
-        if (hsa_amd_memory_async_copy_on_engine(dst_host, c->agents.cpu, src_dev, c->agents.gpu,
-                                                (size_t)half, 1, &slot->gate, slot->done,
-                                                (hsa_amd_sdma_engine_id_t)a, false) !=
-            HSA_STATUS_SUCCESS)
-            return set_error(KV_EHIP, "DMA engine %#x refused a copy of %lld bytes", a,
-                             (long long)half);
-        if (hsa_amd_memory_async_copy_on_engine((char *)dst_host + half, c->agents.cpu,
-                                                (const char *)src_dev + half, c->agents.gpu,
-                                                (size_t)(bytes - half), 1, &slot->gate,
-                                                slot->done, (hsa_amd_sdma_engine_id_t)b,
-                                                false) != HSA_STATUS_SUCCESS) {
-            hsa_signal_subtract_screlease(slot->done, 1);
-            hsa_signal_store_screlease(slot->gate, 0);
-            slot->retired = true;
-            return set_error(KV_EHIP, "DMA engine %#x refused a copy of %lld bytes", b,
-                             (long long)(bytes - half));
-        }
-        c->engine = a;
-    } else if (hsa_amd_memory_async_copy_on_engine(dst_host, c->agents.cpu, src_dev,
-                                                   c->agents.gpu, (size_t)bytes, 1, &slot->gate,
-                                                   slot->done, (hsa_amd_sdma_engine_id_t)c->engine,
-                                                   false) != HSA_STATUS_SUCCESS)
+    if (hsa_amd_memory_async_copy_on_engine(dst_host, c->agents.cpu, src_dev, c->agents.gpu,
+                                            (size_t)bytes, 1, &slot->gate, slot->done,
+                                            (hsa_amd_sdma_engine_id_t)c->engine, false) !=
+        HSA_STATUS_SUCCESS)
         return set_error(KV_EHIP, "DMA engine %#x refused a copy of %lld bytes", c->engine,
                          (long long)bytes);
     // from here the engine holds the copy: every failure path must release it

@@ -76,8 +76,8 @@ int create_events(hipEvent_t *ev, int n)
 // One contiguous transfer between a bank and pinned host memory on `s`, with
 // the engine's transport.  `host_dev` is the device-visible address of the
 // host side (used by the link-copy kernel).
-int transfer(int32_t transport, EngineCopier *copier, void *bank, void *host, void *host_dev,
-             int64_t bytes, bool to_host, hipStream_t s)
+int transfer(int32_t transport, EngineCopier *copier, int32_t link_blocks, void *bank, void *host,
+             void *host_dev, int64_t bytes, bool to_host, hipStream_t s)
 {
     if (bytes <= 0)
         return KV_OK;
@@ -85,7 +85,7 @@ int transfer(int32_t transport, EngineCopier *copier, void *bank, void *host, vo
         return engine_copy_to_host(copier, host, bank, bytes, s);
     const bool kernel = transport == KV_XFER_KERNEL || (transport == KV_XFER_AUTO && to_host);
     if (kernel)
-        return to_host ? launch_link_copy(host_dev, bank, bytes, true, s)
+        return to_host ? launch_link_copy(host_dev, bank, bytes, true, s, link_blocks)
                        : launch_link_copy(bank, host_dev, bytes, false, s);
     hipError_t r;
     if (transport == KV_XFER_DMA || (transport == KV_XFER_DMA_OUT && to_host))
@@ -118,6 +118,7 @@ struct kv_swap {
     hipStream_t copy;
     int32_t transport;
     EngineCopier *copier;        // KV_XFER_ENGINE: the device->host DMA engine
+    int32_t link_blocks;         // link-copy kernel workgroups, device->host (0: default)
     hipEvent_t ev[4];            // free0, free1, filled0, filled1
     bool free_valid[2];
     int next;
@@ -136,6 +137,7 @@ struct kv_ring {
     hipStream_t copy;
     int32_t transport;
     EngineCopier *copier;        // KV_XFER_ENGINE: the device->host DMA engine
+    int32_t link_blocks;         // link-copy kernel workgroups, device->host (0: default)
     int64_t slot_bytes;
     int64_t steps, flushed;
     std::vector<int32_t> pos;    // steps * B positions, in step order
@@ -198,7 +200,7 @@ int swap_out_rows(kv_swap *e, const void *k, const void *v, int32_t l0, int32_t 
             (st = wait(e->copy, e->filled_ev(bk), "swap-out copy wait")))
             return st;
         for (int p = 0; p < c.pieces; ++p)
-            if ((st = transfer(e->transport, e->copier, (char *)e->bank[bk] + c.bank_off[p],
+            if ((st = transfer(e->transport, e->copier, e->link_blocks, (char *)e->bank[bk] + c.bank_off[p],
                                (char *)host + c.host_off[p], (char *)host_dev + c.host_off[p],
                                c.bytes[p], true, e->copy)))
                 return st;
@@ -245,6 +247,7 @@ int kv_swap_create(kv_swap **out, const kv_layout *lay, void *bank0, void *bank1
     e->free_valid[0] = e->free_valid[1] = false;
     e->next = 0;
     e->copier = nullptr;
+    e->link_blocks = 0;
     if ((st = create_events(e->ev, 4))) {
         delete e;
         return st;
@@ -343,7 +346,7 @@ int kv_swap_in(kv_swap *e, void *k, void *v, int32_t layer_begin, int32_t layer_
         if (e->free_valid[bk] && (st = wait(e->copy, e->free_ev(bk), "swap-in bank wait")))
             return st;
         for (int p = 0; p < c.pieces; ++p)
-            if ((st = transfer(e->transport, e->copier, (char *)e->bank[bk] + c.bank_off[p],
+            if ((st = transfer(e->transport, e->copier, e->link_blocks, (char *)e->bank[bk] + c.bank_off[p],
                                (char *)host + c.host_off[p], (char *)host_dev + c.host_off[p],
                                c.bytes[p], false, e->copy)))
                 return st;
@@ -454,6 +457,7 @@ int kv_ring_create(kv_ring **out, const kv_layout *lay, int32_t R, void *bank0, 
     r->wait_needed[0] = r->wait_needed[1] = false;
     r->free_valid[0] = r->free_valid[1] = false;
     r->copier = nullptr;
+    r->link_blocks = 0;
     if ((st = create_events(r->ev, 5))) {
         delete r;
         return st;
@@ -577,7 +581,7 @@ int ring_flush_range(kv_ring *r, int64_t first, int64_t n, hipStream_t compute)
         (st = ring_order_packs(r, true, compute)))
         return st;
     r->pack_streams.clear();
-    if ((st = transfer(r->transport, r->copier, (char *)r->bank[bk] + off,
+    if ((st = transfer(r->transport, r->copier, r->link_blocks, (char *)r->bank[bk] + off,
                        (char *)r->host + first * r->slot_bytes,
                        (char *)r->host_dev + first * r->slot_bytes, n * r->slot_bytes, true,
                        r->copy)))
@@ -704,7 +708,7 @@ int ring_restore_n(kv_ring *r, void *k, void *v, int64_t n_steps, hipStream_t co
         const int bk = (int)(g & 1);
         if (r->free_valid[bk] && (st = wait(r->copy, r->free_ev(bk), "ring restore bank wait")))
             return st;
-        if ((st = transfer(r->transport, r->copier, r->bank[bk], (char *)r->host + j0 * r->slot_bytes,
+        if ((st = transfer(r->transport, r->copier, r->link_blocks, r->bank[bk], (char *)r->host + j0 * r->slot_bytes,
                            (char *)r->host_dev + j0 * r->slot_bytes, n * r->slot_bytes, false,
                            r->copy)))
             return st;
@@ -809,4 +813,45 @@ int kv_ring_reset(kv_ring *r)
     return KV_OK;
 }
 
+namespace {
+
+int set_option(int32_t transport, EngineCopier *copier, int32_t *link_blocks, int32_t option,
+               int64_t value)
+{
+    switch (option) {
+    case KV_OPT_DMA_ENGINE:
+        if (transport != KV_XFER_ENGINE)
+            return set_error(KV_EINVAL, "KV_OPT_DMA_ENGINE applies to KV_XFER_ENGINE handles");
+        if (value < -1 || value > 3)
+            return set_error(KV_EINVAL, "DMA engine %lld is not -1 or 0..3", (long long)value);
+        engine_copier_pin(copier, (int32_t)value);
+        return KV_OK;
+    case KV_OPT_LINK_BLOCKS:
+        if (value < 0 || value > kLinkBlocksMax)
+            return set_error(KV_EINVAL, "link-copy workgroups %lld outside [0, %d]",
+                             (long long)value, kLinkBlocksMax);
+        *link_blocks = (int32_t)value;
+        return KV_OK;
+    default:
+        return set_error(KV_EINVAL, "option %d is not a kv_option", option);
+    }
+}
+
+}  // namespace
+
+int kv_swap_set_option(kv_swap *e, int32_t option, int64_t value)
+{
+    if (!e)
+        return set_error(KV_EINVAL, "swap handle is NULL");
+    return set_option(e->transport, e->copier, &e->link_blocks, option, value);
+}
+
+int kv_ring_set_option(kv_ring *r, int32_t option, int64_t value)
+{
+    if (!r)
+        return set_error(KV_EINVAL, "ring handle is NULL");
+    return set_option(r->transport, r->copier, &r->link_blocks, option, value);
+}
+
 }  // extern "C"
+

@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void copy_split(Geometry g, RowTable rt)
     constexpr int TVV = kThreads * VPER;
     __shared__ u32x4 lds[TVK];
     const int32_t C = CT ? CT : g.C;
-    const int32_t TTK = CT ? TVK / CT : g.tile_tokens;
+    const int32_t TTK = CT ? TVK / (CT ? CT : 1) : g.tile_tokens;
 
     int32_t bid = blockIdx.x;
     const int32_t tile = bid % g.tiles_per_row;
@@ -444,6 +444,23 @@ __global__ __launch_bounds__(kThreads) void copy_split(Geometry g, RowTable rt)
                 kc[(int64_t)c * g.Smax + i] = lds[lds_slot<CT>(i, c, C)];
         }
     }
+}
+
+// Vectors per thread of the split-role kernel for K and for V: one each for
+// heads of up to 32 vectors; four K vectors per thread for wider heads, so
+// that a K tile still spans 8 or more tokens.  Measured alone on 256-, 512-
+// and 1024-dim heads (4000 tokens, cold data): one vector per thread reached
+// 0.76/0.75 of peak (pack/unpack) at 256 dims but 0.65/0.67 at 512 and
+// 0.44/0.42 at 1024 (2-token K tiles); four K vectors 0.74/0.71, 0.72/0.71
+// and 0.72/0.71; four for both 0.67-0.69; the former joint K+V tiles of
+// 1024 vectors 0.70/0.68, 0.70/0.68-0.69, 0.69-0.70/0.68.
+struct SplitMode {
+    int kper, vper;
+};
+
+SplitMode split_mode(int32_t C)
+{
+    return C <= 32 ? SplitMode{1, 1} : SplitMode{4, 1};
 }
 
 // ---- paged pool --------------------------------------------------------------
@@ -656,6 +673,155 @@ hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, uint32_t lds, hipStrea
     return hipLaunchKernel((const void *)k, grid, block, ptrs, lds, s);
 }
 
+// Unpack of many tokens per row into a pool, split roles as copy_split: K
+// workgroups stage the block ids of their tile in LDS and scatter the tile
+// through LDS; V workgroups move 256 * VPER vectors of the row's token range
+// (token-major, contiguous in the packed buffer), each to the slot its
+// token's block gives.  Tokens of skipped blocks are not written.
+template <int CT, int KPER, int VPER>
+__global__ __launch_bounds__(kThreads) void unpack_paged_split(PagedGeometry g, RowTable rt)
+{
+    constexpr int TVK = kThreads * KPER;
+    constexpr int TVV = kThreads * VPER;
+    __shared__ u32x4 lds[TVK];
+    __shared__ int32_t ids[TVK + 1];      // blocks touched by a K tile (at most its tokens + 1)
+    const int32_t C = CT ? CT : g.C;
+    const int32_t TTK = CT ? TVK / (CT ? CT : 1) : g.tile_tokens;
+
+    int32_t bid = blockIdx.x;
+    const int32_t tile = bid % g.tiles_per_row;
+    bid /= g.tiles_per_row;
+    const int32_t h = bid % g.H;
+    bid /= g.H;
+    const int32_t b = g.b0 + bid % g.nb;
+    const int32_t li = bid / g.nb;
+
+    const int32_t off = rt.off[b];
+    const int32_t cnt = rt.off[b + 1] - off;
+    const int64_t layer = g.l0 + li;
+    const int64_t CP = (int64_t)C * g.P;          // vectors of one (block, head) unit
+    const int64_t blk = (int64_t)g.H * g.T * C;
+    const u32x4 *ks_unit = (const u32x4 *)(g.stage + 2 * (int64_t)li * blk +
+                                           ((int64_t)g.H * off + (int64_t)h * cnt) * C);
+    const int32_t *trow = g.table + (int64_t)b * g.table_stride;
+    const int tid = threadIdx.x;
+
+    if (tile >= g.k_tiles) {
+        const int32_t v0 = (tile - g.k_tiles) * TVV;
+        const int32_t nv = cnt * C;
+        if (v0 >= nv)
+            return;
+        const int32_t n = min(TVV, nv - v0);
+        const u32x4 *vs = ks_unit + blk + v0;
+        u32x4 *vpool = (u32x4 *)g.v;
+        u32x4 r[VPER];
+#pragma unroll
+        for (int p = 0; p < VPER; ++p) {
+            const int e = tid + p * kThreads;
+            if (e < n)
+                r[p] = vs[e];
+        }
+#pragma unroll
+        for (int p = 0; p < VPER; ++p) {
+            const int e = tid + p * kThreads;
+            if (e < n) {
+                const int32_t tok = (v0 + e) / C, c = v0 + e - tok * C;
+                uint32_t q, slot;
+                paged_split(g, (uint32_t)(rt.start[b] + tok), q, slot);
+                const int32_t id = trow[q];
+                if (id >= 0 && id < g.NB)
+                    vpool[((layer * g.NB + id) * g.H + h) * CP + (int64_t)slot * C + c] = r[p];
+            }
+        }
+        return;
+    }
+
+    const int32_t t0 = tile * TTK;
+    if (t0 >= cnt)
+        return;
+    const int32_t nt = min(TTK, cnt - t0);
+    const int32_t nvec = nt * C;
+    const uint32_t s0 = (uint32_t)(rt.start[b] + t0);
+    uint32_t q0, o0, q1, o1;
+    paged_split(g, s0, q0, o0);
+    paged_split(g, s0 + (uint32_t)nt - 1u, q1, o1);
+    const int32_t nblk = (int32_t)(q1 - q0) + 1;
+    for (int j = tid; j < nblk; j += kThreads) {
+        const int32_t id = trow[q0 + j];
+        ids[j] = (id >= 0 && id < g.NB) ? id : -1;
+    }
+    const u32x4 *ks = ks_unit + (int64_t)t0 * C;
+    u32x4 kr[KPER];
+#pragma unroll
+    for (int p = 0; p < KPER; ++p) {
+        const int e = tid + p * kThreads;
+        if (e < nvec)
+            kr[p] = ks[e];
+    }
+#pragma unroll
+    for (int p = 0; p < KPER; ++p) {
+        const int e = tid + p * kThreads;
+        if (e < nvec)
+            lds[lds_slot<CT>(e / C, e % C, C)] = kr[p];
+    }
+    __syncthreads();     // the tile in LDS and the block ids
+    u32x4 *kw = (u32x4 *)g.k;
+#pragma unroll
+    for (int p = 0; p < KPER; ++p) {
+        const int e = tid + p * kThreads, c = e / TTK, i = e % TTK;
+        if (c < C && i < nt) {
+            uint32_t q, slot;
+            paged_split(g, o0 + (uint32_t)i, q, slot);
+            const int32_t id = ids[q];
+            if (id >= 0)
+                kw[((layer * g.NB + id) * g.H + h) * CP + (int64_t)c * g.P + slot] =
+                    lds[lds_slot<CT>(i, c, C)];
+        }
+    }
+}
+
+template <int CT>
+hipError_t launch_unpack_paged_split_c(const SplitMode &m, const PagedGeometry &g,
+                                       const RowTable &rt, dim3 grid, hipStream_t s,
+                                       const LaunchTimer &t)
+{
+    const dim3 block(kThreads);
+    if constexpr (CT == 0 || CT <= 32)
+        if (m.kper == 1 && m.vper == 1)
+            return launch(unpack_paged_split<CT, 1, 1>, grid, block, 0, s, t, g, rt);
+    if constexpr (CT == 0 || CT > 32)
+        if (m.kper == 4 && m.vper == 1)
+            return launch(unpack_paged_split<CT, 4, 1>, grid, block, 0, s, t, g, rt);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_unpack_paged_split(const SplitMode &m, const PagedGeometry &g,
+                                     const RowTable &rt, int64_t blocks, hipStream_t s,
+                                     const LaunchTimer &t)
+{
+    const dim3 grid((unsigned)blocks);
+    switch (g.C) {
+    case 1: return launch_unpack_paged_split_c<1>(m, g, rt, grid, s, t);
+    case 2: return launch_unpack_paged_split_c<2>(m, g, rt, grid, s, t);
+    case 4: return launch_unpack_paged_split_c<4>(m, g, rt, grid, s, t);
+    case 8: return launch_unpack_paged_split_c<8>(m, g, rt, grid, s, t);
+    case 16: return launch_unpack_paged_split_c<16>(m, g, rt, grid, s, t);
+    case 32: return launch_unpack_paged_split_c<32>(m, g, rt, grid, s, t);
+    case 64: return launch_unpack_paged_split_c<64>(m, g, rt, grid, s, t);
+    case 128: return launch_unpack_paged_split_c<128>(m, g, rt, grid, s, t);
+    default: return launch_unpack_paged_split_c<0>(m, g, rt, grid, s, t);
+    }
+}
+
+// Which tile kernel a paged pack or unpack uses.  Measured alone on a
+// GPT-2-1.5B pool (48 layers x 8 rows x 1000 tokens, 2.46 GB), two runs:
+// split roles unpack 16-token pages at 0.68 of HBM peak and 256-token pages
+// at 0.69 (joint tiles 0.67 and 0.67), but pack them at 0.66 and 0.66-0.67
+// (joint 0.68 and 0.67).  (A split V workgroup of a pack looks up each
+// vector's block in the table before it can load from the pool; one of an
+// unpack loads the packed buffer first.)  So: joint tiles pack, split roles
+// unpack.
+
 // Vectors per thread of the paged tile kernel: 256-vector tiles for heads of
 // up to 16 vectors (measured 4-5% faster packs and 1.5-3% faster unpacks
 // than 512-vector tiles on a GPT-2-1.5B pool), 1024-vector tiles for wider
@@ -685,23 +851,6 @@ hipError_t launch_paged_tiles(const PagedGeometry &g, const RowTable &rt, int64_
         break;
     }
     return e;
-}
-
-// Vectors per thread of the split-role kernel for K and for V: one each for
-// heads of up to 32 vectors; four K vectors per thread for wider heads, so
-// that a K tile still spans 8 or more tokens.  Measured alone on 256-, 512-
-// and 1024-dim heads (4000 tokens, cold data): one vector per thread reached
-// 0.76/0.75 of peak (pack/unpack) at 256 dims but 0.65/0.67 at 512 and
-// 0.44/0.42 at 1024 (2-token K tiles); four K vectors 0.74/0.71, 0.72/0.71
-// and 0.72/0.71; four for both 0.67-0.69; the former joint K+V tiles of
-// 1024 vectors 0.70/0.68, 0.70/0.68-0.69, 0.69-0.70/0.68.
-struct SplitMode {
-    int kper, vper;
-};
-
-SplitMode split_mode(int32_t C)
-{
-    return C <= 32 ? SplitMode{1, 1} : SplitMode{4, 1};
 }
 
 template <int CT, bool kPack>
@@ -793,17 +942,13 @@ __global__ __launch_bounds__(kThreads) void link_copy(const u32x4 *__restrict__ 
     }
 }
 
-// Workgroups of one link copy (KV_LINK_BLOCKS overrides, for tuning).
-int link_blocks(bool to_host)
+// Workgroups of one link copy: `blocks` when positive, else the default
+// (8 for device->host, 128 for host->device).
+int link_blocks(bool to_host, int32_t blocks)
 {
-    static const int env = [] {
-        const char *e = std::getenv("KV_LINK_BLOCKS");
-        const int v = e ? std::atoi(e) : 0;
-        return v > 0 && v <= 65535 ? v : 0;
-    }();
-    if (env)
-        return env;
-    return to_host ? 8 : 128;
+    if (blocks > 0)
+        return blocks;
+    return to_host ? kLinkBlocksToHost : 128;
 }
 
 // The span [b0, b0 + nb) from the first to the last row that moves a token:
@@ -934,9 +1079,16 @@ int launch_paged_copy(bool pack, const PagedGeometry &g0, const RowTable &rt, in
     int64_t per_layer;
     if (small) {
         per_layer = ((int64_t)g.nb * g.H * g.C + kThreads - 1) / kThreads;
-    } else {
+    } else if (pack) {
         g.tile_tokens = tile_tokens_for(g.C, paged_per_thread(g.C));
         g.tiles_per_row = (max_count + g.tile_tokens - 1) / g.tile_tokens;
+        per_layer = (int64_t)g.nb * g.H * g.tiles_per_row;
+    } else {
+        const SplitMode m = split_mode(g.C);
+        g.tile_tokens = tile_tokens_for(g.C, m.kper);
+        g.k_tiles = (max_count + g.tile_tokens - 1) / g.tile_tokens;
+        const int32_t tvv = kThreads * m.vper;
+        g.tiles_per_row = g.k_tiles + (int32_t)(((int64_t)max_count * g.C + tvv - 1) / tvv);
         per_layer = (int64_t)g.nb * g.H * g.tiles_per_row;
     }
     const int64_t max_blocks = small ? 0x7fffffffLL / kThreads : 0x7fffffffLL;
@@ -963,7 +1115,7 @@ int launch_paged_copy(bool pack, const PagedGeometry &g0, const RowTable &rt, in
         } else {
             const int64_t blocks = (int64_t)gl.nl * per_layer;
             e = pack ? launch_paged_tiles<true>(gl, rt, blocks, s, t)
-                     : launch_paged_tiles<false>(gl, rt, blocks, s, t);
+                     : launch_unpack_paged_split(split_mode(g.C), gl, rt, blocks, s, t);
         }
         profile_commit(t, name, 2 * payload, e == hipSuccess);
         if (e != hipSuccess)
@@ -972,7 +1124,8 @@ int launch_paged_copy(bool pack, const PagedGeometry &g0, const RowTable &rt, in
     return KV_OK;
 }
 
-int launch_link_copy(void *dst, const void *src, int64_t bytes, bool to_host, hipStream_t s)
+int launch_link_copy(void *dst, const void *src, int64_t bytes, bool to_host, hipStream_t s,
+                     int32_t blocks_wanted)
 {
     if (bytes <= 0)
         return KV_OK;
@@ -986,7 +1139,7 @@ int launch_link_copy(void *dst, const void *src, int64_t bytes, bool to_host, hi
         const int64_t n = std::min(kPiece, bytes - done);
         const int32_t nvec = (int32_t)(n / 16);
         const int64_t blocks =
-            std::min<int64_t>(link_blocks(to_host), (nvec + kThreads - 1) / kThreads);
+            std::min<int64_t>(link_blocks(to_host, blocks_wanted), (nvec + kThreads - 1) / kThreads);
         const u32x4 *from = (const u32x4 *)((const char *)src + done);
         u32x4 *to = (u32x4 *)((char *)dst + done);
         const LaunchTimer t = profile_take();

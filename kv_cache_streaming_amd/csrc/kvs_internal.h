@@ -47,6 +47,7 @@ struct PagedGeometry {
     int32_t p_shift;        // log2(P) when P is a power of two, else -1
     int32_t B, l0, nl;
     int32_t tiles_per_row, tile_tokens;
+    int32_t k_tiles;        // split tile kernel: the first k_tiles tiles of a row move K, the rest V
     int32_t b0, nb;         // grids cover rows [b0, b0 + nb) (set by the launcher)
     int64_t T;              // sum of counts
 };
@@ -104,9 +105,13 @@ int launch_paged_copy(bool pack, const PagedGeometry &g, const RowTable &rt, int
                       hipStream_t s);
 
 // Copies `bytes` (a multiple of 16) between a device buffer and pinned host
-// memory with the link-copy kernel.  `dst`/`src` are device-visible
-// addresses (see host_device_address).
-int launch_link_copy(void *dst, const void *src, int64_t bytes, bool to_host, hipStream_t s);
+// memory with the link-copy kernel, from `blocks` workgroups (0: the
+// default for the direction, kLinkBlocksToHost for device->host).
+// `dst`/`src` are device-visible addresses (see host_device_address).
+constexpr int32_t kLinkBlocksToHost = 8;
+constexpr int32_t kLinkBlocksMax = 1024;
+int launch_link_copy(void *dst, const void *src, int64_t bytes, bool to_host, hipStream_t s,
+                     int32_t blocks = 0);
 
 // Device-visible address of pinned host memory [host, host+bytes); returns
 // KV_OK or KV_EINVAL.
@@ -122,6 +127,9 @@ int engine_copier_create(EngineCopier **out);
 // seconds: its signals are then left allocated rather than freed under the
 // engine.
 int engine_copier_destroy(EngineCopier *c);
+// Pin the copier to one of the four fast engines (0-3), or let it take, at
+// each copy, one the runtime reports idle (-1, the default).
+void engine_copier_pin(EngineCopier *c, int32_t engine);
 // Enqueue on `s` a copy of `bytes` from device memory to pinned host memory
 // that starts once everything enqueued on `s` so far has run, and that later
 // work on `s` waits for.

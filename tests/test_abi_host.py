@@ -233,3 +233,8 @@ def test_engine_transport_refused_under_serialised_dispatch(kv, monkeypatch, var
     st = kv._lib.kv_swap_create(ctypes.byref(h), ctypes.byref(lay), 4096, 8192, 4096, None,
                                 kv.KV_XFER_AUTO)
     assert st == kv.KV_EINVAL and "KV_XFER_ENGINE" not in kv.kv_last_error()
+
+
+def test_set_option_null_handles(kv):
+    for fn in (kv._lib.kv_swap_set_option, kv._lib.kv_ring_set_option):
+        assert fn(None, kv.KV_OPT_LINK_BLOCKS, 4) == kv.KV_EINVAL

@@ -254,7 +254,7 @@ TRANSPORTS = [0, 1, 2, 3, 4, 5]   # KV_XFER_AUTO, _KERNEL, _RUNTIME, _DMA, _DMA_
 
 
 def run_ring(kv, dims, R, positions, seed, bits=True, mutate=False, delay_cycles=0, transport=0,
-             gather=0, caches=1):
+             gather=0, caches=1, options=()):
     """Push every step, flush, restore into a zero cache; compare with the oracle.
     `caches` > 1: step j reads cache pair (j // 3) % caches (runs of three steps
     per cache)."""
@@ -277,6 +277,8 @@ def run_ring(kv, dims, R, positions, seed, bits=True, mutate=False, delay_cycles
                      copy_stream=copy, transport=transport)
     if gather:
         ring.set_gather(kv.KV_RING_GATHER_AT_FLUSH)
+    for opt, val in options:
+        ring.set_option(opt, val)
     slots = []
     rng = np.random.default_rng(seed)
     if delay_cycles:
@@ -316,6 +318,13 @@ def test_ring_decode_flow(kv, transport, gather):
     dims = (3, 4, 2, 64, 50)
     pos = [[10 + j, 20 + j, 3 + j, 40 + (j % 9)] for j in range(19)]   # 2 full banks + a partial
     run_ring(kv, dims, 8, pos, seed=21, transport=transport, gather=gather)
+
+
+@pytest.mark.parametrize("transport,opt,val", [(5, 1, 0), (5, 1, 3), (0, 2, 2)])
+def test_ring_link_options(kv, transport, opt, val):
+    dims = (3, 4, 2, 64, 50)
+    pos = [[10 + j, 20 + j, 3 + j, 40 + (j % 9)] for j in range(19)]
+    run_ring(kv, dims, 8, pos, seed=22, transport=transport, options=[(opt, val)])
 
 
 @pytest.mark.parametrize("D,R,steps", [(128, 16, 37), (8, 5, 12), (24, 7, 15), (1024, 4, 9)])
@@ -397,11 +406,12 @@ def test_ring_gather_at_flush_waits_for_a_late_flush(kv):
     run_ring(kv, dims, 2, pos, seed=27, delay_cycles=200_000_000, gather=1)
 
 
-def run_swap(kv, dims, l0, nl, start, count, bank_bytes, seed, delay_cycles=0, transport=0):
+def run_swap(kv, dims, l0, nl, start, count, bank_bytes, seed, delay_cycles=0, transport=0,
+             options=()):
     import torch
     L, B, H, D, S = dims
     note(f"swap dims={dims} layers=[{l0},+{nl}) bank={bank_bytes} delay={delay_cycles} "
-         f"transport={transport}")
+         f"transport={transport} options={options}")
     K, V = synth.cache_pair(dims, seed, bits=True)
     lay = kv.kv_layout_init(L, B, H, D, S, 0)
     dk, dv = dev(K), dev(V)
@@ -410,6 +420,8 @@ def run_swap(kv, dims, l0, nl, start, count, bank_bytes, seed, delay_cycles=0, t
     copy = torch.cuda.Stream()
     compute = torch.cuda.current_stream()
     eng = kv.KvSwap(lay, b0, b1, bank_bytes, copy, transport)
+    for opt, val in options:
+        eng.set_option(opt, val)
     hostbuf = pinned(want.size + CANARY)
     if delay_cycles:
         with torch.cuda.stream(copy):
@@ -435,6 +447,41 @@ def run_swap(kv, dims, l0, nl, start, count, bank_bytes, seed, delay_cycles=0, t
     eng.swap_in(dk2, dv2, l0, nl, start, count, hostbuf, want.nbytes, compute, done2)
     done2.synchronize()
     assert np.array_equal(host(dk2), ek) and np.array_equal(host(dv2), ev), "swap-in differs"
+    eng.close()
+
+
+@pytest.mark.parametrize("transport,opt,val", [
+    (0, 2, 1), (0, 2, 3), (0, 2, 200), (1, 2, 12), (5, 1, 0), (5, 1, 2), (5, 1, 3), (5, 1, -1),
+    (5, 2, 5)])
+def test_swap_link_options(kv, transport, opt, val):
+    """Per-handle link settings (KV_OPT_LINK_BLOCKS: 1, 3, 200 or 12
+    link-copy workgroups; KV_OPT_DMA_ENGINE: engine 0, 2, 3 or an idle one)
+    move the same bytes: row-group chunks, late copies."""
+    dims = (3, 5, 2, 128, 260)
+    count = [260, 0, 100, 255, 3]
+    start = [0, 0, 160, 5, 257]
+    per_row = [2 * 2 * 128 * 2 * c for c in count]
+    run_swap(kv, dims, 0, 3, start, count, max(per_row) + 4096, seed=34,
+             delay_cycles=50_000_000, transport=transport, options=[(opt, val)])
+
+
+def test_link_options_rejected(kv):
+    import torch
+    dims = (2, 2, 2, 64, 16)
+    lay = kv.kv_layout_init(*dims, 0)
+    note("link option errors")
+    eng = kv.KvSwap(lay, empty(4096), empty(4096), 8192, torch.cuda.Stream(), kv.KV_XFER_AUTO)
+    for opt, val in ((kv.KV_OPT_DMA_ENGINE, 0), (kv.KV_OPT_LINK_BLOCKS, -1),
+                     (kv.KV_OPT_LINK_BLOCKS, 1025), (99, 1)):
+        with pytest.raises(kv.KvError) as ei:
+            eng.set_option(opt, val)
+        assert ei.value.status == kv.KV_EINVAL
+    eng.close()
+    eng = kv.KvSwap(lay, empty(4096), empty(4096), 8192, torch.cuda.Stream(), kv.KV_XFER_ENGINE)
+    for val in (-2, 4):
+        with pytest.raises(kv.KvError) as ei:
+            eng.set_option(kv.KV_OPT_DMA_ENGINE, val)
+        assert ei.value.status == kv.KV_EINVAL
     eng.close()
 
 
