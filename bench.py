@@ -106,6 +106,10 @@ def parse_args():
     ap.add_argument("--row-engines", default=None,
                     help="gqa-100k with --row-transport engine: DMA engines of the row swap-out "
                          "handles (the layers split into contiguous ranges over them)")
+    ap.add_argument("--row-bank-mib", type=int, default=None,
+                    help="gqa-100k: banks of the row swap (0: the whole row image)")
+    ap.add_argument("--row-first", type=int, choices=(0, 1), default=None,
+                    help="gqa-100k: the prompt's copies wait for the row swap-out's (1)")
     ap.add_argument("--row-link-blocks", type=int, default=None,
                     help="gqa-100k: link-copy workgroups of the row swap-out (KV_OPT_LINK_BLOCKS)")
     ap.add_argument("--compute-streams", type=int, choices=(1, 2), default=2,
@@ -653,14 +657,19 @@ class LongStep:
     through a 16-slot staging ring restored into the cache."""
 
     def __init__(self, w, swap_bank_bytes, transport=0, row_transport=None, prompt_engines=None,
-                 row_link_blocks=None, row_engines=None):
+                 row_link_blocks=None, row_engines=None, row_first=None, row_bank_bytes=None):
         """row_transport: the row swap's kv_transport (None: the workload's
         default, else `transport`); prompt_engines: DMA engines of the
         prompt-streaming handles with the engine transport (None: the
         workload's default); row_link_blocks: link-copy workgroups of the
         row swap-out (None: the workload's default); row_engines: with the
         engine transport for the row, the DMA engines of its swap-out handles
-        (the layers split into as many contiguous ranges, one call each)."""
+        (the layers split into as many contiguous ranges, one call each);
+        row_first: the prompt's copies start once the row swap-out's copies
+        are done (the two outgoing legs take the link one after the other);
+        row_bank_bytes: the row swap's banks (None: the workload's default;
+        0: the whole row image, packed in one pass before its copy and
+        unpacked in one pass after it)."""
         import torch
 
         import kv_cache_streaming_amd as kv
@@ -675,6 +684,10 @@ class LongStep:
             row_link_blocks = DEFAULT_ROW_LINK_BLOCKS.get(w.name, 0)
         if row_engines is None:
             row_engines = [int(x) for x in DEFAULT_ROW_ENGINES.get(w.name, "-1").split(",")]
+        self.row_first = DEFAULT_ROW_FIRST.get(w.name, False) if row_first is None else row_first
+        if row_bank_bytes is None:
+            row_bank_bytes = DEFAULT_ROW_BANK_MIB.get(w.name, swap_bank_bytes >> 20) << 20
+        self.row_done = torch.cuda.Event()
         self.lay = kv.kv_layout_init(*w.dims, w.dtype)
         self.lens = [int(x) for x in synth.row_lengths(w)]
         self.positions = [list(map(int, p)) for p in synth.decode_positions(w)]
@@ -692,9 +705,10 @@ class LongStep:
         # prompt-streaming handles: chunks alternate over them, each with its
         # own copy stream, so that a handle's next copy is already queued on
         # its DMA engine while the other's runs
-        self.eng_p = []
+        self.eng_p, self.p_copy = [], []
         for i, e in enumerate(prompt_engines if transport == TRANSPORTS["engine"] else [-1]):
             cs = self.s["d2h"] if i == 0 else torch.cuda.Stream()
+            self.p_copy.append(cs)
             h = kv.KvSwap(self.lay, _bank(torch, cb), _bank(torch, cb), cb, cs, transport)
             if transport == TRANSPORTS["engine"]:
                 h.set_option(kv.KV_OPT_DMA_ENGINE, e)
@@ -709,13 +723,15 @@ class LongStep:
         self.row_count = [self.lens[b] if b == bstar else 0 for b in range(B)]
         self.row_layer = kv.kv_pack_bytes(self.lay, 1, self.row_count)
         self.row_image = L * self.row_layer
+        # the row swap's banks, 0 meaning the whole image (one chunk each way);
         # a bank holds at least one row of one layer (the engine splits at rows)
-        sb = max(swap_bank_bytes, -(-self.row_layer // (1 << 20)) << 20)
+        ob = row_bank_bytes or (-(-self.row_image // (1 << 20)) << 20)
+        ob = max(ob, -(-self.row_layer // (1 << 20)) << 20)
         rt = row_transport
         self.eng_o = []
         for i, e in enumerate(row_engines if rt == TRANSPORTS["engine"] else [-1]):
             cs = self.s["d2h_row"] if i == 0 else torch.cuda.Stream()
-            h = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb, cs, rt)
+            h = kv.KvSwap(self.lay, _bank(torch, ob), _bank(torch, ob), ob, cs, rt)
             if rt == TRANSPORTS["engine"]:
                 h.set_option(kv.KV_OPT_DMA_ENGINE, e)
             if row_link_blocks:
@@ -727,7 +743,7 @@ class LongStep:
         n1 = L * w.H * w.D * w.Smax
         self.slot1 = (torch.empty(n1, dtype=torch.int16, device="cuda"),
                       torch.empty(n1, dtype=torch.int16, device="cuda"))
-        self.eng_i = kv.KvSwap(self.lay1, _bank(torch, sb), _bank(torch, sb), sb, self.s["h2d"],
+        self.eng_i = kv.KvSwap(self.lay1, _bank(torch, ob), _bank(torch, ob), ob, self.s["h2d"],
                                rt)
         # the first step swaps in whatever the second image holds: its bytes
         # only have to be there, not to be a real row (no kernels at set-up,
@@ -765,7 +781,11 @@ class LongStep:
             l0, l1 = w.L * i // n, w.L * (i + 1) // n
             h.swap_out(self.A[0], self.A[1], l0, l1 - l0, self.row_start, self.row_count,
                        self.row_host[out].data_ptr() + l0 * self.row_layer,
-                       (l1 - l0) * self.row_layer, self.s["out"])
+                       (l1 - l0) * self.row_layer, self.s["out"],
+                       self.row_done if (self.row_first and i == n - 1) else None)
+        if self.row_first:
+            for cs in self.p_copy:
+                cs.wait_event(self.row_done)
         self.eng_i.swap_in(self.slot1[0], self.slot1[1], 0, w.L, [0], [max(self.row_count)],
                            self.row_host[inn], self.row_image, self.s["in"])
         k, n = 0, len(self.eng_p)
@@ -807,9 +827,11 @@ STEPS = {"gpt2-small-tiny": StreamStep, "gpt2-1.5b": StreamStep, "opt-66b-16l": 
 # 2-3% faster with the link-copy kernel.  The 100K-context step streams its
 # prompt on DMA engine 0 through two handles (the next chunk's copy is
 # queued on the engine while the other runs) and swaps its row with the
-# link-copy kernel from 12 workgroups: 1491 ms (66.0 GB/s) with the prompt
-# packs at 0.55 of HBM peak, against 1477 ms (66.7 GB/s) and 0.32 with the
-# link-copy kernel for every outgoing copy (two runs each, one box).
+# link-copy kernel from 16 workgroups, through banks that hold the whole row
+# image (packed in one pass before the copy), the prompt's copies after the
+# row's: 1469-1471 ms (66.9-67.0 GB/s) with its pack kernels at 0.63 of HBM
+# peak, against 1477 ms (66.7 GB/s) and 0.32 with the link-copy kernel for
+# every outgoing copy (two runs each, one box).
 DEFAULT_TRANSPORT = {"gpt2-small-tiny": "auto", "gpt2-1.5b": "engine", "opt-66b-16l": "auto",
                      "bloom-176b-10l": "auto", "gqa-100k": "engine"}
 TRANSPORTS = {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3, "dma_out": 4, "engine": 5}
@@ -817,8 +839,10 @@ TRANSPORTS = {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3, "dma_out": 4, "eng
 # its prompt handles' DMA engines and its row swap-out's link-copy workgroups
 DEFAULT_ROW_TRANSPORT = {"gqa-100k": "auto"}
 DEFAULT_PROMPT_ENGINES = {"gqa-100k": "0,0"}
-DEFAULT_ROW_LINK_BLOCKS = {"gqa-100k": 12}
+DEFAULT_ROW_LINK_BLOCKS = {"gqa-100k": 16}
 DEFAULT_ROW_ENGINES = {}
+DEFAULT_ROW_FIRST = {"gqa-100k": True}
+DEFAULT_ROW_BANK_MIB = {"gqa-100k": 0}
 
 def link_ceiling(step, kv, transport, target_bytes=4 << 30, reps=3):
     """GB/s the host link reaches through this library with `transport`, each
@@ -1341,10 +1365,15 @@ def main():
             args.row_link_blocks = DEFAULT_ROW_LINK_BLOCKS.get(w.name, 0)
         if args.row_engines is None:
             args.row_engines = DEFAULT_ROW_ENGINES.get(w.name, "-1")
+        if args.row_first is None:
+            args.row_first = int(DEFAULT_ROW_FIRST.get(w.name, False))
+        if args.row_bank_mib is None:
+            args.row_bank_mib = DEFAULT_ROW_BANK_MIB.get(w.name, args.swap_bank_mib)
         step = LongStep(w, args.swap_bank_mib << 20, TRANSPORTS[args.transport],
                         TRANSPORTS[args.row_transport],
                         [int(x) for x in args.prompt_engines.split(",")], args.row_link_blocks,
-                        [int(x) for x in args.row_engines.split(",")])
+                        [int(x) for x in args.row_engines.split(",")], bool(args.row_first),
+                        args.row_bank_mib << 20)
     elif STEPS[w.name] is SwapStep:
         step = SwapStep(w, args.swap_bank_mib << 20, TRANSPORTS[args.transport],
                         [int(x) for x in args.prompt_engines.split(",")]
@@ -1480,6 +1509,8 @@ def main():
                        **({"row_transport": args.row_transport,
                            "prompt_engines": args.prompt_engines,
                            "row_engines": args.row_engines,
+                           "row_first": args.row_first,
+                           "row_bank_mib": args.row_bank_mib,
                            "row_link_blocks": args.row_link_blocks}
                           if isinstance(step, LongStep) else {}),
                        "hw_queues": int(os.environ["GPU_MAX_HW_QUEUES"])},
