@@ -84,7 +84,9 @@ def parse_args():
     ap.add_argument("--workload", default="gqa-100k", choices=sorted(STEPS),
                     help="gqa-100k (the largest workload that fits one GPU) is the headline; "
                          "the others measure the remaining workloads")
-    ap.add_argument("--swap-bank-mib", type=int, default=256)
+    ap.add_argument("--swap-bank-mib", type=int, default=None,
+                    help="banks of the swap engines in MiB (default: the workload's entry in "
+                         "DEFAULT_SWAP_BANK_MIB, else 256; 0 for the BLOOM step: one layer)")
     ap.add_argument("--transport", choices=("auto", "kernel", "runtime", "dma", "dma_out", "engine"),
                     default=None,
                     help="bank<->host transfers (see kv_transport in include/kvstream.h); "
@@ -102,7 +104,8 @@ def parse_args():
                     help="gqa-100k with --transport engine: comma-separated DMA engines (0-3, or "
                          "-1 for an idle one at each copy) of the prompt-streaming handles; "
                          "chunks alternate over the handles, each with its own copy stream "
-                         "(bloom-176b-10l: the same for its swap-out handles, by layer)")
+                         "(bloom-176b-10l: the same for its swap-out handles, by layer; "
+                         "gpt2 shapes: the engines of the prompt, ring and swap-out handles)")
     ap.add_argument("--row-engines", default=None,
                     help="gqa-100k with --row-transport engine: DMA engines of the row swap-out "
                          "handles (the layers split into contiguous ranges over them)")
@@ -135,7 +138,10 @@ class StreamStep:
     """Prompt streaming, decode ring and microbatch swap of a uniform-prompt
     workload (the GPT-2 shapes): the five phases listed at the top."""
 
-    def __init__(self, w, swap_bank_bytes, transport=0):
+    def __init__(self, w, swap_bank_bytes, transport=0, out_engines=None):
+        """out_engines: with the engine transport, the DMA engines of the
+        device->host handles (prompt streaming, staging ring, swap-out), or
+        None for the workload's default (an idle one at each copy)."""
         import torch
 
         import kv_cache_streaming_amd as kv
@@ -180,6 +186,11 @@ class StreamStep:
         self.ring_host = pinned(w.decode_steps * self.slot)
         self.ring = kv.KvRing(self.lay, R, bank(R * self.slot), bank(R * self.slot),
                               self.ring_host, copy_stream=self.s["d2h"], transport=x)
+        if out_engines is None:
+            out_engines = DEFAULT_OUT_ENGINES.get(w.name)
+        if out_engines and x == TRANSPORTS["engine"]:
+            for h, e in zip((self.eng_p, self.ring, self.eng_o), out_engines):
+                h.set_option(kv.KV_OPT_DMA_ENGINE, e)
         self.ring.set_gather(RING_GATHER)
         # double-buffered host images: one written this step, one read
         self.host_p = [pinned(L * self.layer_prompt) for _ in range(2)]
@@ -512,7 +523,8 @@ class SwapStep:
         self.host = HostBuffer(kv, self.N * self.image)
         self.img = [self.host.data_ptr() + x * self.image for x in range(self.N)]
         self.s = {name: torch.cuda.Stream() for name in ("out", "in", "d2h", "h2d", "swap")}
-        sb = swap_bank_bytes
+        # 0: banks of one layer of a microbatch
+        sb = swap_bank_bytes or (-(-self.per_layer // (1 << 20)) << 20)
         self.eng_o = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb, self.s["d2h"],
                                transport)
         self.eng_out = [self.eng_o]
@@ -838,6 +850,14 @@ TRANSPORTS = {"auto": 0, "kernel": 1, "runtime": 2, "dma": 3, "dma_out": 4, "eng
 # the long-context step's row swap transport (absent: the step's transport),
 # its prompt handles' DMA engines and its row swap-out's link-copy workgroups
 DEFAULT_ROW_TRANSPORT = {"gqa-100k": "auto"}
+# swap banks: the BLOOM step's hold one layer of a microbatch (0), so each
+# layer is packed in one pass and copied as one piece: 281-282 ms per round
+# (97.5-98.0 GB/s) with its unpacks at 0.61 of HBM peak in the step, against
+# 297 ms (92.6 GB/s) and 0.44 with 256 MiB banks (6 row groups per layer)
+DEFAULT_SWAP_BANK_MIB = {"bloom-176b-10l": 0}
+# DMA engines of the GPT-2 step's device->host handles (prompt, ring,
+# swap-out) with the engine transport; absent: an idle engine at each copy
+DEFAULT_OUT_ENGINES = {}
 DEFAULT_PROMPT_ENGINES = {"gqa-100k": "0,0"}
 DEFAULT_ROW_LINK_BLOCKS = {"gqa-100k": 16}
 DEFAULT_ROW_ENGINES = {}
@@ -1356,6 +1376,8 @@ def main():
         args.ring_gather]
     if args.transport is None:
         args.transport = DEFAULT_TRANSPORT[w.name]
+    if args.swap_bank_mib is None:
+        args.swap_bank_mib = DEFAULT_SWAP_BANK_MIB.get(w.name, 256)
     if STEPS[w.name] is LongStep:
         if args.row_transport is None:
             args.row_transport = DEFAULT_ROW_TRANSPORT.get(w.name, args.transport)
@@ -1374,6 +1396,10 @@ def main():
                         [int(x) for x in args.prompt_engines.split(",")], args.row_link_blocks,
                         [int(x) for x in args.row_engines.split(",")], bool(args.row_first),
                         args.row_bank_mib << 20)
+    elif STEPS[w.name] is StreamStep:
+        step = StreamStep(w, args.swap_bank_mib << 20, TRANSPORTS[args.transport],
+                          [int(x) for x in args.prompt_engines.split(",")]
+                          if args.prompt_engines else None)
     elif STEPS[w.name] is SwapStep:
         step = SwapStep(w, args.swap_bank_mib << 20, TRANSPORTS[args.transport],
                         [int(x) for x in args.prompt_engines.split(",")]

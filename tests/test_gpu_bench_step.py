@@ -149,7 +149,8 @@ def test_bloom_swap_round(bench):
     import synth
     w = synth.WORKLOADS["bloom-176b-10l"]
     note(f"bench step {w.name} dims={w.dims}")
-    step = bench.SwapStep(w, 256 << 20, bench.TRANSPORTS[bench.DEFAULT_TRANSPORT[w.name]])
+    step = bench.SwapStep(w, bench.DEFAULT_SWAP_BANK_MIB.get(w.name, 256) << 20,
+                          bench.TRANSPORTS[bench.DEFAULT_TRANSPORT[w.name]])
     dims, L, B = w.dims, w.L, w.B
     for r in range(2):
         x = r % step.N
