@@ -139,3 +139,33 @@ def test_all_cores_leg_keeps_order_where_calls_meet(bench, monkeypatch):
     r = bench.cpu_all_cores(oracle, dims, run, 60.0, 1)
     assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
     assert "(1 pass(es), 3 groups)" in r["sample"]
+
+
+def test_committed_counters_match_the_headline_kernels(bench):
+    """The committed counter summary of the headline workload's dominant
+    kernel was taken on the current kernel source, so the bench line carries
+    HBM traffic (not null)."""
+    path = bench.counters_file("gqa-100k", "pack_tiles")
+    fields = dict(line.split(":", 1) for line in open(path) if ":" in line and
+                  not line.startswith("#"))
+    alg = int(fields["algorithmic_bytes_per_launch"])
+    assert bench.read_counters("gqa-100k", "pack_tiles", alg) is not None
+
+
+def test_long_context_defaults(bench):
+    """The 100K-context step's link configuration: prompt on DMA engine 0
+    through two handles, row swap on the link-copy kernel (16 workgroups)
+    through whole-image banks, the prompt's copies after the row's."""
+    w = "gqa-100k"
+    assert bench.DEFAULT_TRANSPORT[w] == "engine"
+    assert bench.DEFAULT_ROW_TRANSPORT[w] == "auto"
+    assert bench.DEFAULT_PROMPT_ENGINES[w] == "0,0"
+    assert bench.DEFAULT_ROW_LINK_BLOCKS[w] == 16
+    assert bench.DEFAULT_ROW_BANK_MIB[w] == 0 and bench.DEFAULT_ROW_FIRST[w] is True
+    args = sys.argv
+    try:
+        sys.argv = ["bench.py"]
+        a = bench.parse_args()
+    finally:
+        sys.argv = args
+    assert a.workload == w and a.gpus == 1
