@@ -605,3 +605,53 @@ def test_profile_window_overlapping_streams(kv):
     assert 0 < win["link_busy_ms"] <= win["span_ms"] * (1 + 1e-6)
     assert win["hbm_busy_ms"] <= win["span_ms"] * (1 + 1e-6)
     ring.close()
+
+
+def test_staging_past_its_allocation_is_refused(kv):
+    """A staging range that starts inside one device allocation and runs past
+    its end is refused before anything is enqueued, whether the bytes past
+    the end belong to another allocation or to none."""
+    import ctypes
+    import torch
+    dims = (2, 2, 2, 64, 64)
+    L, B, H, D, S = dims
+    note("staging past the end of its allocation")
+    lay = kv.kv_layout_init(L, B, H, D, S, 0)
+    K, V = synth.cache_pair(dims, 5)
+    dk, dv = dev(K), dev(V)
+    lib = kv._lib
+    lib.hipMalloc.restype = ctypes.c_int
+    lib.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    lib.hipFree.restype = ctypes.c_int
+    lib.hipFree.argtypes = [ctypes.c_void_p]
+    size = 4 << 20
+    bufs = []
+    for _ in range(2):
+        p = ctypes.c_void_p()
+        assert lib.hipMalloc(ctypes.byref(p), size) == 0 and p.value
+        bufs.append(p.value)
+    try:
+        # only where the runtime sizes allocations: without that the range
+        # check falls back to the two ends, and this case must not run
+        lib.hipMemGetAddressRange.restype = ctypes.c_int
+        lib.hipMemGetAddressRange.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                              ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p]
+        base, got = ctypes.c_void_p(), ctypes.c_size_t()
+        if (lib.hipMemGetAddressRange(ctypes.byref(base), ctypes.byref(got), bufs[0]) != 0
+                or base.value != bufs[0] or got.value < size):
+            pytest.skip("the runtime does not report allocation ranges")
+        need = kv.kv_pack_bytes(lay, L, None, S)
+        assert need <= size
+        start = bufs[0] + size - need // 2        # half the packed block fits, half does not
+        with pytest.raises(kv.KvError) as e:
+            kv.kv_pack_tokens(lay, dk, dv, 0, L, [0] * B, [S] * B, start, need)
+        assert e.value.status == kv.KV_EINVAL
+        msg = kv.kv_last_error()
+        assert "past the end of its allocation" in msg or "not device memory" in msg, msg
+        # the same call on the allocation's own range goes through
+        kv.kv_pack_tokens(lay, dk, dv, 0, L, [0] * B, [S] * B, bufs[0], need)
+        torch.cuda.synchronize()
+    finally:
+        torch.cuda.synchronize()
+        for p in bufs:
+            lib.hipFree(p)
