@@ -187,7 +187,7 @@ class StreamStep:
         self.ring = kv.KvRing(self.lay, R, bank(R * self.slot), bank(R * self.slot),
                               self.ring_host, copy_stream=self.s["d2h"], transport=x)
         if out_engines is None:
-            out_engines = DEFAULT_OUT_ENGINES.get(w.name)
+            out_engines = default_out_engines(w.name)
         if out_engines and x == TRANSPORTS["engine"]:
             for h, e in zip((self.eng_p, self.ring, self.eng_o), out_engines):
                 h.set_option(kv.KV_OPT_DMA_ENGINE, e)
@@ -412,7 +412,9 @@ class RingStep:
     staging ring, flushed to pinned host memory every 16 steps, then the ring's
     host image restored into cache D (recovery on a fresh worker)."""
 
-    def __init__(self, w, swap_bank_bytes, transport=0):
+    def __init__(self, w, swap_bank_bytes, transport=0, out_engines=None):
+        """out_engines: with the engine transport, [engine] pins the ring's
+        flush copies to that DMA engine (None: an idle one at each copy)."""
         import torch
 
         import kv_cache_streaming_amd as kv
@@ -429,6 +431,10 @@ class RingStep:
         self.ring = kv.KvRing(self.lay, R, _bank(torch, R * self.slot), _bank(torch, R * self.slot),
                               self.ring_host, copy_stream=self.s["d2h"], transport=transport)
         self.ring.set_gather(RING_GATHER)
+        if out_engines is None:
+            out_engines = default_out_engines(w.name)
+        if out_engines and transport == TRANSPORTS["engine"]:
+            self.ring.set_option(kv.KV_OPT_DMA_ENGINE, out_engines[0])
 
     def link_bytes(self):
         return self.link_bytes_out() + self.link_bytes_in()
@@ -528,6 +534,8 @@ class SwapStep:
         self.eng_o = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb, self.s["d2h"],
                                transport)
         self.eng_out = [self.eng_o]
+        if out_engines is None:
+            out_engines = default_out_engines(w.name)
         if out_engines and transport == TRANSPORTS["engine"]:
             self.eng_o.set_option(kv.KV_OPT_DMA_ENGINE, out_engines[0])
             for e in out_engines[1:]:
@@ -835,8 +843,9 @@ STEPS = {"gpt2-small-tiny": StreamStep, "gpt2-1.5b": StreamStep, "opt-66b-16l": 
 # kernels more of HBM).  GPT-2-1.5B: with the named-engine device->host leg
 # the step takes 107-110 ms against 108-115 ms with the link-copy kernel
 # (alternating runs on one box), with the tile kernels at 0.63-0.66 of peak
-# instead of 0.54-0.56; the OPT-66B ring runs 7% faster and the BLOOM step
-# 2-3% faster with the link-copy kernel.  The 100K-context step streams its
+# instead of 0.54-0.56; the BLOOM step runs 2-3% faster with the link-copy
+# kernel, and the OPT-66B ring keeps the link-copy kernel too: pinned to one
+# engine it matched it on one box (below) and took 15.7 ms on another.  The 100K-context step streams its
 # prompt on DMA engine 0 through two handles (the next chunk's copy is
 # queued on the engine while the other runs) and swaps its row with the
 # link-copy kernel from 16 workgroups, through banks that hold the whole row
@@ -855,9 +864,19 @@ DEFAULT_ROW_TRANSPORT = {"gqa-100k": "auto"}
 # (97.5-98.0 GB/s) with its unpacks at 0.61 of HBM peak in the step, against
 # 297 ms (92.6 GB/s) and 0.44 with 256 MiB banks (6 row groups per layer)
 DEFAULT_SWAP_BANK_MIB = {"bloom-176b-10l": 0}
-# DMA engines of the GPT-2 step's device->host handles (prompt, ring,
-# swap-out) with the engine transport; absent: an idle engine at each copy
-DEFAULT_OUT_ENGINES = {}
+# DMA engines of the device->host handles when a step runs with the engine
+# transport (the GPT-2 steps: prompt, ring, swap-out; the OPT-66B ring: its
+# flushes; the BLOOM step: its swap-out handles); absent: an idle engine at
+# each copy.  The OPT-66B ring pinned to engine 0 took 11.04-11.05 ms with
+# its gather kernel at 0.45 of HBM peak on one box (11.0-11.05 ms and
+# 0.40-0.43 with the link-copy kernel, 11.85 ms with an idle engine at each
+# copy) and 15.7 ms on another, so its default transport stays the kernel.
+DEFAULT_OUT_ENGINES = {"opt-66b-16l": "0"}
+
+
+def default_out_engines(name):
+    e = DEFAULT_OUT_ENGINES.get(name)
+    return [int(x) for x in e.split(",")] if e else None
 DEFAULT_PROMPT_ENGINES = {"gqa-100k": "0,0"}
 DEFAULT_ROW_LINK_BLOCKS = {"gqa-100k": 16}
 DEFAULT_ROW_ENGINES = {}
@@ -1396,6 +1415,10 @@ def main():
                         [int(x) for x in args.prompt_engines.split(",")], args.row_link_blocks,
                         [int(x) for x in args.row_engines.split(",")], bool(args.row_first),
                         args.row_bank_mib << 20)
+    elif STEPS[w.name] is RingStep:
+        step = RingStep(w, args.swap_bank_mib << 20, TRANSPORTS[args.transport],
+                        [int(x) for x in args.prompt_engines.split(",")]
+                        if args.prompt_engines else None)
     elif STEPS[w.name] is StreamStep:
         step = StreamStep(w, args.swap_bank_mib << 20, TRANSPORTS[args.transport],
                           [int(x) for x in args.prompt_engines.split(",")]
