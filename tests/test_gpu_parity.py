@@ -338,6 +338,17 @@ def test_ring_gather_at_flush_runs(kv, D, R, steps):
     run_ring(kv, dims, R, pos, seed=24, gather=1, caches=2)
 
 
+@pytest.mark.parametrize("D", [8, 24, 64, 128])
+def test_ring_gather_at_flush_many_units(kv, D):
+    """Gather at flush over 105 (layer, row, head) units at ragged row
+    positions: heads of 1, 3, 8 and 16 vectors, so a flush of 8 steps moves
+    8-128 vectors per unit and the gather groups several units per wave with
+    a partial last group; the 19 steps end in a partial bank of 3."""
+    dims = (3, 5, 7, D, 40)
+    pos = [[(7 * b) % 20 + j for b in range(5)] for j in range(19)]
+    run_ring(kv, dims, 8, pos, seed=26, gather=1)
+
+
 def test_ring_gather_at_flush_partial_flushes(kv):
     """Explicit flushes in the middle of a bank: the pending steps are gathered
     then, and later steps continue in the same bank."""
