@@ -111,27 +111,41 @@ def test_gpt2_stream_step(bench, transport):
 
 
 @pytest.mark.timeout(600)
-def test_opt66b_ring_step(bench):
+@pytest.mark.parametrize("duplex", [True, False])
+def test_opt66b_ring_step(bench, duplex):
     """The ragged decode ring of the OPT-66B slice: 64 pushes gathered at
-    flush, 4 flushes, restore into a second cache."""
+    flush, 4 flushes, restore into a second cache; duplex: two rings taking
+    turns, each step restoring the image the other flushed the step before
+    while its own flushes go out."""
     import synth
+    import torch
     w = synth.WORKLOADS["opt-66b-16l"]
-    note(f"bench step {w.name} dims={w.dims}")
-    step = bench.RingStep(w, 256 << 20, bench.TRANSPORTS[bench.DEFAULT_TRANSPORT[w.name]])
+    note(f"bench step {w.name} dims={w.dims} duplex={duplex}")
+    step = bench.RingStep(w, 256 << 20, bench.TRANSPORTS[bench.DEFAULT_TRANSPORT[w.name]],
+                          duplex=duplex)
     dims = w.dims
     L, B = w.L, w.B
-    for k in range(2):
-        note(f"bench step {w.name}: step {k}")
-        step.run()
     Ak, Av = (words(t) for t in step.A)
     slots = [oracle.pack(dims, Ak, Av, 0, L, p, [1] * B) for p in step.positions]
     ring = oracle.ring_host(slots)
-    assert np.array_equal(host_words(step.ring_host, ring.nbytes), ring), "ring host image"
     del Ak, Av
-    Dk, Dv = (words(t) for t in step.D)
-    for j, p in enumerate(step.positions):
-        assert np.array_equal(oracle.pack(dims, Dk, Dv, 0, L, p, [1] * B), slots[j]), \
-            f"restored decode step {j}"
+    for k in range(3):
+        note(f"bench step {w.name}: step {k}")
+        step.run()
+        if k == 0 and duplex:
+            continue   # nothing flushed before the first step: no restore yet
+        # every ring flushed so far holds the decode positions of A ...
+        for i, host in enumerate(step.ring_hosts[:k + 1]):
+            assert np.array_equal(host_words(host, ring.nbytes), ring), f"ring {i} host image"
+        # ... and D holds them after this step's restore
+        Dk, Dv = (words(t) for t in step.D)
+        for j, p in enumerate(step.positions):
+            assert np.array_equal(oracle.pack(dims, Dk, Dv, 0, L, p, [1] * B), slots[j]), \
+                f"step {k}: restored decode step {j}"
+        del Dk, Dv
+        step.D[0].fill_(0x3A3A)     # the next restore has to write every position again
+        step.D[1].fill_(0x3A3A)
+        torch.cuda.synchronize()    # the fills run on torch's stream, the restore on another
 
 
 def ptr_words(ptr, nbytes):
