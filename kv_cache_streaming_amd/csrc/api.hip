@@ -204,6 +204,7 @@ int enqueue_copy(bool pack, const kv_layout &lay, const void *k, const void *v, 
     g.nh = nh < 0 ? lay.H : nh;
     g.tiles_per_row = 0;
     g.tile_tokens = 0;
+    g.layer_wgs = 0;
     g.T = rt.off[lay.B];
     return launch_copy(pack, g, rt, max_count, s);
 }
@@ -235,6 +236,7 @@ int enqueue_steps(bool pack, const kv_layout &lay, const void *k, const void *v,
     g.nh = lay.H;
     g.tiles_per_row = 0;
     g.tile_tokens = 0;
+    g.layer_wgs = 0;
     g.T = lay.B;
     return launch_steps(pack, g, rt, n, slot_bytes / 16, s);
 }

@@ -315,6 +315,23 @@ __global__ __launch_bounds__(kThreads) void copy_steps_lds(Geometry g, RowTable 
     }
 }
 
+// The row owning workgroup q of a layer in a grid of the rows' own tiles:
+// the last i in [0, nb) with pre[i] <= q.  A row without tokens owns no
+// workgroups, so it is never the one found.  q is uniform across the
+// workgroup: the search runs on scalar loads of the kernel arguments.
+__device__ __forceinline__ int32_t tile_row(const RowTiles &rtl, int32_t nb, int32_t q)
+{
+    int32_t lo = 0, hi = nb;
+    while (hi - lo > 1) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (rtl.pre[mid] <= q)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
 // The tile kernel (many tokens per row: prompt layers, chunks, swaps).  Split
 // roles: a row's first g.k_tiles workgroups move K only -- a tile of TTK =
 // 256 * KPER / C tokens of every chunk row, loaded chunk-major (each wave
@@ -330,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void copy_steps_lds(Geometry g, RowTable 
 // 0.76-0.77.  Larger tiles (2 or 4 vectors per thread for K, V or both)
 // were slower on 8- and 16-vector heads.
 template <int CT, int KPER, int VPER, bool kPack>
-__global__ __launch_bounds__(kThreads) void copy_split(Geometry g, RowTable rt)
+__global__ __launch_bounds__(kThreads) void copy_split(Geometry g, RowTable rt, RowTiles rtl)
 {
     constexpr int TVK = kThreads * KPER;
     constexpr int TVV = kThreads * VPER;
@@ -338,13 +355,33 @@ __global__ __launch_bounds__(kThreads) void copy_split(Geometry g, RowTable rt)
     const int32_t C = CT ? CT : g.C;
     const int32_t TTK = CT ? TVK / (CT ? CT : 1) : g.tile_tokens;
 
-    int32_t bid = blockIdx.x;
-    const int32_t tile = bid % g.tiles_per_row;
-    bid /= g.tiles_per_row;
-    const int32_t h = bid % g.nh;     // head within the moved range
-    bid /= g.nh;
-    const int32_t b = g.b0 + bid % g.nb;
-    const int32_t li = bid / g.nb;
+    // block -> (layer, row, head, tile); within a layer rows, then heads, then
+    // tiles, as the cache and the packed buffer lay them out
+    int32_t b, h, tile, li, k_tiles;
+    if (g.tiles_per_row > 0) {
+        // dense: every row of the span has the longest row's tiles (those
+        // past a short row's end exit at once)
+        int32_t bid = blockIdx.x;
+        tile = bid % g.tiles_per_row;
+        bid /= g.tiles_per_row;
+        h = bid % g.nh;               // head within the moved range
+        bid /= g.nh;
+        b = g.b0 + bid % g.nb;
+        li = bid / g.nb;
+        k_tiles = g.k_tiles;
+    } else {
+        // the rows' own tiles only
+        const int32_t q = (int32_t)blockIdx.x % g.layer_wgs;
+        li = (int32_t)blockIdx.x / g.layer_wgs;
+        const int32_t row = tile_row(rtl, g.nb, q);
+        b = g.b0 + row;
+        const int32_t n = rt.off[b + 1] - rt.off[b];
+        k_tiles = (n + TTK - 1) / TTK;
+        const int32_t row_tiles = k_tiles + (n * C + TVV - 1) / TVV;
+        const int32_t r = q - rtl.pre[row];
+        h = r / row_tiles;
+        tile = r - h * row_tiles;
+    }
 
     const int32_t off = rt.off[b];
     const int32_t cnt = rt.off[b + 1] - off;
@@ -354,8 +391,8 @@ __global__ __launch_bounds__(kThreads) void copy_split(Geometry g, RowTable rt)
                                ((int64_t)g.nh * off + (int64_t)h * cnt) * C);
     const int tid = threadIdx.x;
 
-    if (tile >= g.k_tiles) {
-        const int32_t v0 = (tile - g.k_tiles) * TVV;
+    if (tile >= k_tiles) {
+        const int32_t v0 = (tile - k_tiles) * TVV;
         const int32_t nv = cnt * C;
         if (v0 >= nv)
             return;
@@ -854,34 +891,34 @@ hipError_t launch_paged_tiles(const PagedGeometry &g, const RowTable &rt, int64_
 }
 
 template <int CT, bool kPack>
-hipError_t launch_split_c(const SplitMode &m, const Geometry &g, const RowTable &rt, dim3 grid,
-                          hipStream_t s, const LaunchTimer &t)
+hipError_t launch_split_c(const SplitMode &m, const Geometry &g, const RowTable &rt,
+                          const RowTiles &rtl, dim3 grid, hipStream_t s, const LaunchTimer &t)
 {
     const dim3 block(kThreads);
     if constexpr (CT == 0 || CT <= 32)
         if (m.kper == 1 && m.vper == 1)
-            return launch(copy_split<CT, 1, 1, kPack>, grid, block, 0, s, t, g, rt);
+            return launch(copy_split<CT, 1, 1, kPack>, grid, block, 0, s, t, g, rt, rtl);
     if constexpr (CT == 0 || CT > 32)
         if (m.kper == 4 && m.vper == 1)
-            return launch(copy_split<CT, 4, 1, kPack>, grid, block, 0, s, t, g, rt);
+            return launch(copy_split<CT, 4, 1, kPack>, grid, block, 0, s, t, g, rt, rtl);
     return hipErrorInvalidValue;
 }
 
 template <bool kPack>
-hipError_t launch_split(const SplitMode &m, const Geometry &g, const RowTable &rt, int64_t blocks,
-                        hipStream_t s, const LaunchTimer &t)
+hipError_t launch_split(const SplitMode &m, const Geometry &g, const RowTable &rt,
+                        const RowTiles &rtl, int64_t blocks, hipStream_t s, const LaunchTimer &t)
 {
     const dim3 grid((unsigned)blocks);
     switch (g.C) {
-    case 1: return launch_split_c<1, kPack>(m, g, rt, grid, s, t);
-    case 2: return launch_split_c<2, kPack>(m, g, rt, grid, s, t);
-    case 4: return launch_split_c<4, kPack>(m, g, rt, grid, s, t);
-    case 8: return launch_split_c<8, kPack>(m, g, rt, grid, s, t);
-    case 16: return launch_split_c<16, kPack>(m, g, rt, grid, s, t);
-    case 32: return launch_split_c<32, kPack>(m, g, rt, grid, s, t);
-    case 64: return launch_split_c<64, kPack>(m, g, rt, grid, s, t);
-    case 128: return launch_split_c<128, kPack>(m, g, rt, grid, s, t);
-    default: return launch_split_c<0, kPack>(m, g, rt, grid, s, t);
+    case 1: return launch_split_c<1, kPack>(m, g, rt, rtl, grid, s, t);
+    case 2: return launch_split_c<2, kPack>(m, g, rt, rtl, grid, s, t);
+    case 4: return launch_split_c<4, kPack>(m, g, rt, rtl, grid, s, t);
+    case 8: return launch_split_c<8, kPack>(m, g, rt, rtl, grid, s, t);
+    case 16: return launch_split_c<16, kPack>(m, g, rt, rtl, grid, s, t);
+    case 32: return launch_split_c<32, kPack>(m, g, rt, rtl, grid, s, t);
+    case 64: return launch_split_c<64, kPack>(m, g, rt, rtl, grid, s, t);
+    case 128: return launch_split_c<128, kPack>(m, g, rt, rtl, grid, s, t);
+    default: return launch_split_c<0, kPack>(m, g, rt, rtl, grid, s, t);
     }
 }
 
@@ -967,6 +1004,25 @@ bool row_span(const RowTable &rt, int32_t B, int32_t *b0, int32_t *nb)
     return hi > lo;
 }
 
+// Prefix of the workgroups of rows [b0, b0 + nb) of one layer into
+// rtl->pre: each of the nh heads of row b has ceil(count_b / ttk) K tiles
+// and ceil(count_b * C / tvv) V runs.  Returns the layer's total, or -1
+// when it does not fit a grid.
+int64_t row_tile_prefix(const RowTable &rt, int32_t b0, int32_t nb, int32_t nh, int32_t ttk,
+                        int32_t C, int32_t tvv, RowTiles *rtl)
+{
+    int64_t total = 0;
+    rtl->pre[0] = 0;
+    for (int32_t i = 0; i < nb; ++i) {
+        const int64_t cnt = rt.off[b0 + i + 1] - rt.off[b0 + i];
+        total += nh * ((cnt + ttk - 1) / ttk + (cnt * C + tvv - 1) / tvv);
+        if (total > 0x7fffffffLL)
+            return -1;
+        rtl->pre[i + 1] = (int32_t)total;
+    }
+    return total;
+}
+
 }  // namespace
 
 int launch_copy(bool pack, const Geometry &g0, const RowTable &rt, int32_t max_count,
@@ -979,6 +1035,7 @@ int launch_copy(bool pack, const Geometry &g0, const RowTable &rt, int32_t max_c
     if (!row_span(rt, g.B, &g.b0, &g.nb))
         return KV_OK;
     int64_t per_layer;
+    RowTiles rtl{};
     if (small) {
         per_layer = ((int64_t)g.nb * g.nh * g.C + kThreads - 1) / kThreads;
     } else {
@@ -988,6 +1045,16 @@ int launch_copy(bool pack, const Geometry &g0, const RowTable &rt, int32_t max_c
         const int32_t tvv = kThreads * m.vper;
         g.tiles_per_row = g.k_tiles + (int32_t)(((int64_t)max_count * g.C + tvv - 1) / tvv);
         per_layer = (int64_t)g.nb * g.nh * g.tiles_per_row;
+        // ragged rows: a grid of the rows' own tiles when the dense one would
+        // be a fifth or more empty workgroups (finding its row costs a
+        // workgroup a few dependent loads before its first access, which
+        // lost 7% on uniform 4 KiB tiles)
+        const int64_t own = row_tile_prefix(rt, g.b0, g.nb, g.nh, g.tile_tokens, g.C, tvv, &rtl);
+        if (own >= 0 && own * 5 <= per_layer * 4) {
+            g.tiles_per_row = 0;
+            g.layer_wgs = (int32_t)own;
+            per_layer = own;
+        }
     }
     // A launch covers whole layers.  Keep every grid within 2^31-1 blocks and,
     // for the small kernel, its flat thread id within 2^31.
@@ -1016,8 +1083,8 @@ int launch_copy(bool pack, const Geometry &g0, const RowTable &rt, int32_t max_c
         } else {
             const int64_t blocks = (int64_t)gl.nl * per_layer;
             const SplitMode m = split_mode(g.C);
-            e = pack ? launch_split<true>(m, gl, rt, blocks, s, t)
-                     : launch_split<false>(m, gl, rt, blocks, s, t);
+            e = pack ? launch_split<true>(m, gl, rt, rtl, blocks, s, t)
+                     : launch_split<false>(m, gl, rt, rtl, blocks, s, t);
         }
         profile_commit(t, name, 2 * payload, e == hipSuccess);
         if (e != hipSuccess)

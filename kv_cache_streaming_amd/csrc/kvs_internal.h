@@ -27,11 +27,21 @@ struct Geometry {
     int32_t B, H, C, Smax;  // C = D/8 vectors per head row; H = heads of the cache
     int32_t l0, nl;         // layer range
     int32_t h0, nh;         // head range [h0, h0 + nh) moved; the packed format has nh heads
-    int32_t tiles_per_row;  // tile kernel: tiles per row (ceil(max count / tile tokens))
+    int32_t tiles_per_row;  // tile kernel: tiles per (row, head) of a dense grid (the longest
+                            // row's), or 0 for a grid of the rows' own tiles (RowTiles)
     int32_t tile_tokens;    // tile kernel: tokens per tile
-    int32_t k_tiles;        // split tile kernel: the first k_tiles tiles of a row move K, the rest V
+    int32_t k_tiles;        // dense split tile grid: the first k_tiles tiles of a row move K, the rest V
+    int32_t layer_wgs;      // grid of the rows' own tiles: workgroups per layer
     int32_t b0, nb;         // pack/unpack grids cover rows [b0, b0 + nb) (set by the launcher)
     int64_t T;              // sum of counts
+};
+
+// Workgroups of the rows [b0, b0 + nb) of one layer in a grid that holds
+// only the tiles each row has: row b0 + i owns workgroups [pre[i], pre[i + 1])
+// of the layer, head after head, each head's K tiles first and then its V
+// runs.
+struct RowTiles {
+    int32_t pre[kMaxRows + 1];
 };
 
 // Geometry of one launch on a paged pool: key [L, NB, H, D/8, P, 8], value

@@ -130,6 +130,16 @@ def test_empty_rows_around_the_moved_ones(kv):
     check_pack_unpack(kv, dims, 2, 1, z[:4] + [60] + z[5:], z[:4] + [20] + z[5:], seed=35)
 
 
+@pytest.mark.parametrize("D", [16, 24, 128, 1024])
+def test_ragged_rows_both_tile_grids(kv, D):
+    """Rows of very different lengths (a grid of the rows' own tiles: one row
+    of 2000 tokens beside rows of 10-40 and an empty one) and nearly equal
+    ones (the dense grid), over several layers and head dims."""
+    dims = (3, 5, 3, D, 2100)
+    check_pack_unpack(kv, dims, 0, 3, [50, 7, 0, 300, 2000], [2000, 10, 0, 40, 17], seed=41)
+    check_pack_unpack(kv, dims, 1, 2, [0, 3, 9, 1, 2], [1500, 1490, 1497, 1500, 1466], seed=42)
+
+
 def test_maximum_rows(kv):
     """KV_MAX_ROWS = 256 rows in one call (the row table travels in the kernel
     arguments): ragged and empty rows with the tile kernel, one token per row
