@@ -140,6 +140,49 @@ def test_ragged_rows_both_tile_grids(kv, D):
     check_pack_unpack(kv, dims, 1, 2, [0, 3, 9, 1, 2], [1500, 1490, 1497, 1500, 1466], seed=42)
 
 
+@pytest.mark.parametrize("S", [512, 520])
+@pytest.mark.parametrize("base", [0, 1664])
+def test_value_runs_on_cache_pages(kv, S, base):
+    """Rows that start in mid-page of the value cache: rows a whole number
+    of 4 KiB pages long (Smax = 512, D = 128) or with the page offset moving
+    from head to head (Smax = 520), a value cache that is a view based on a
+    page boundary or 1664 bytes past one, dense and ragged grids; pack and
+    unpack against the oracle, and nothing outside the cache view written."""
+    import torch
+    dims = (2, 4, 3, 128, S)
+    L, B, H, D, _ = dims
+    lay = kv.kv_layout_init(L, B, H, D, S, 0)
+    for seed, start, count in ((51, [5, 100, 17, 0], [400, 300, 411, 500]),
+                               (52, [3, 0, 250, 9], [500, 0, 7, 260])):
+        note(f"value runs S={S} base={base} start={start} count={count}")
+        K, V = synth.cache_pair(dims, seed)
+        want = oracle.pack(dims, K, V, 0, L, start, count)
+        dk = dev(K)
+        # the value cache as a view starting `base` bytes past a 4 KiB boundary
+        vbuf = torch.empty(V.size + 4096, dtype=torch.int16, device="cuda")
+        off = ((base - vbuf.data_ptr()) % 4096) // 2     # int16 words
+        assert (vbuf.data_ptr() + 2 * off) % 4096 == base
+        dv = vbuf[off:off + V.size]
+        dv.copy_(torch.from_numpy(V.view(np.int16)))
+        st = empty(want.size, CANARY)
+        kv.kv_pack_tokens(lay, dk, dv, 0, L, start, count, st, want.nbytes)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(st)[:want.size], want), "pack differs from the oracle"
+        sk, sv = np.full(K.size, 0xC3C3, np.uint16), np.full(V.size, 0x3C3C, np.uint16)
+        ek, ev = sk.copy(), sv.copy()
+        oracle.unpack(dims, ek, ev, 0, L, start, count, want)
+        dk2 = dev(sk)
+        vbuf.fill_(0x3C3C)
+        kv.kv_unpack_tokens(lay, dk2, vbuf[off:off + V.size], 0, L, start, count, st,
+                            want.nbytes)
+        torch.cuda.synchronize()
+        got_v = host(vbuf)
+        assert np.array_equal(host(dk2), ek), "unpack: key cache differs"
+        assert np.array_equal(got_v[off:off + V.size], ev), "unpack: value cache differs"
+        assert np.all(got_v[:off] == 0x3C3C) and np.all(got_v[off + V.size:] == 0x3C3C), \
+            "unpack wrote outside the value cache"
+
+
 def test_maximum_rows(kv):
     """KV_MAX_ROWS = 256 rows in one call (the row table travels in the kernel
     arguments): ragged and empty rows with the tile kernel, one token per row
