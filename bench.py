@@ -1,43 +1,39 @@
 """Benchmark of the KV buffered-copy path on one MI355X.
 
 By default one step is one pass of the whole path over one batch of the
-GPT-2-1.5B-shaped workload (L=48, B=8, H=25, D=64, Smax=1024, fp16; prompt
-length 1000; 24 decode steps; staging ring of 8 slots).  It follows the
-dataflow of the DejaVu workers, emulated on one GPU:
+100K-context workload (LongStep below: 60 layers, 4 rows of U{20000..99936}
+tokens, 8 KV heads, D=128, bf16, Smax=100000; 98.3 GB of caches):
 
-  1. prompt streaming (prompt worker): the 48 prompt layers of cache A are
-     packed layer by layer and copied to pinned host memory;
-  2. prompt load (token worker): the prompt image streamed in the previous
-     step -- a different request, already in host memory -- is copied back
-     through the banks and unpacked into cache B layer by layer, while (1)
-     runs: the two link directions carry independent data;
-  3. decode: 24 single-token packs of cache B (positions 1000..1023) into the
-     staging ring, flushed to pinned host memory every 8 steps (replication);
-  4. restore: the ring's host image is unpacked into cache D (recovery on a
-     fresh worker);
-  5. microbatch swap: cache B (microbatch x-1, all 1024 positions) is swapped
-     out layer by layer while microbatch x+1 is swapped in to cache C from
-     its host image, duplex.
+  1. row swap: the row with the longest context is packed and swapped out
+     to pinned host memory while that row's previous image is swapped into a
+     free one-row slot (both link directions at once);
+  2. prompt streaming: every row's prompt leaves layer by layer in
+     4096-token chunks, each chunk packed into a staging bank and copied to
+     pinned host memory while the next chunk is packed;
+  3. decode: 64 single-token packs at each row's own position into a
+     16-slot staging ring gathered at flush, flushed to pinned host memory
+     when full, then restored into the cache.
 
 Host images are double-buffered across steps, so each step's inbound
 transfers read what an earlier step wrote.  Each workload's step runs with
-the transport listed in DEFAULT_TRANSPORT (this one: device-to-host copies
-on named DMA engines) unless --transport names another.  Inputs are resident in HBM
-before the timed region.  `value` is the KV payload the step moves across
-the host link (both directions) per second.  `roofline` describes the
-pack/unpack kernel with the most GPU time: algorithmic bytes (payload read +
-payload written) per launch over its average duration, both measured live
-with hipEvents bound to every launch's dispatch (the kernel's own begin and
-end timestamps).  `cpu_baseline`
-is the oracle on a bounded sample of the same step (single-threaded; its
+the transport listed in DEFAULT_TRANSPORT unless --transport names another.
+Inputs are resident in HBM before the timed region.  `value` is the KV
+payload the step moves across the host link (both directions) per second.
+`roofline` describes the pack/unpack kernel with the most GPU time:
+algorithmic bytes (payload read + payload written) per launch over its
+average duration, both measured live with hipEvents bound to every launch's
+dispatch (the kernel's own begin and end timestamps).  `cpu_baseline` is the
+oracle on a bounded sample of the same step (single-threaded; its
 `all_cores` entry runs the same calls in pieces over the host's cores).
 
 `--workload` selects the other shapes, each with the step its class below
-describes: opt-66b-16l (RingStep: the decode ring of a 16-layer OPT-66B
-stage), bloom-176b-10l (SwapStep: duplex microbatch swapping on a 10-layer
-BLOOM-176B stage, plus the steady-state schedule against its Appendix E
-prediction), gqa-100k (LongStep: 100K-token contexts), gpt2-small-tiny (the
-default step at GPT-2-small size).
+describes: gpt2-1.5b (StreamStep: prompt streaming of 48 layers beside the
+load of an earlier prompt image, 24 ring pushes with 3 flushes and a ring
+restore, and a microbatch swap-out beside a swap-in), opt-66b-16l (RingStep:
+the decode ring of a 16-layer OPT-66B stage), bloom-176b-10l (SwapStep:
+duplex microbatch swapping on a 10-layer BLOOM-176B stage, plus the
+steady-state schedule against its Appendix E prediction), gpt2-small-tiny
+(the GPT-2-1.5B step at GPT-2-small size).
 """
 from __future__ import annotations
 
@@ -140,7 +136,23 @@ def parse_args():
 
 class StreamStep:
     """Prompt streaming, decode ring and microbatch swap of a uniform-prompt
-    workload (the GPT-2 shapes): the five phases listed at the top."""
+    workload (the GPT-2 shapes), following the DejaVu workers' dataflow:
+
+      1. prompt streaming (prompt worker): the prompt layers of cache A are
+         packed layer by layer and copied to pinned host memory;
+      2. prompt load (token worker): the prompt image streamed in the
+         previous step -- a different request, already in host memory -- is
+         copied back through the banks and unpacked into cache B layer by
+         layer, while (1) runs: the two link directions carry independent
+         data;
+      3. decode: single-token packs of cache B at the positions after the
+         prompt into the staging ring, flushed to pinned host memory when
+         full (replication);
+      4. restore: the ring's host image is unpacked into cache D (recovery
+         on a fresh worker);
+      5. microbatch swap: cache B (microbatch x-1, every position) is
+         swapped out layer by layer while microbatch x+1 is swapped in to
+         cache C from its host image, duplex."""
 
     def __init__(self, w, swap_bank_bytes, transport=0, out_engines=None):
         """out_engines: with the engine transport, the DMA engines of the
