@@ -68,6 +68,15 @@ RING_GATHER = 1   # kv_ring_gather of the rings the steps use (set from --ring-g
 WHOLE_CALLS = True   # swaps of complete images as one call each (set from --swap-calls)
 
 
+_T0 = time.perf_counter()
+
+
+def progress(msg):
+    """One line on stderr as each phase of the run ends (stdout holds only the
+    result line)."""
+    print(f"[bench {time.perf_counter() - _T0:7.1f} s] {msg}", file=sys.stderr, flush=True)
+
+
 def counters_file(workload, kernel_name):
     return os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_{workload}.txt")
 
@@ -109,6 +118,11 @@ def parse_args():
                     help="gqa-100k: banks of the row swap (0: the whole row image)")
     ap.add_argument("--row-first", type=int, choices=(0, 1), default=None,
                     help="gqa-100k: the prompt's copies wait for the row swap-out's (1)")
+    ap.add_argument("--row-in-transport", choices=("auto", "kernel", "runtime", "dma", "dma_out",
+                                                   "engine"), default=None,
+                    help="gqa-100k: transport of the row swap-in (default: --row-transport)")
+    ap.add_argument("--row-in-after", type=int, choices=(0, 1), default=None,
+                    help="gqa-100k: the row swap-in's copies wait for the row swap-out's (1)")
     ap.add_argument("--row-link-blocks", type=int, default=None,
                     help="gqa-100k: link-copy workgroups of the row swap-out (KV_OPT_LINK_BLOCKS)")
     ap.add_argument("--ring-duplex", type=int, choices=(0, 1), default=None,
@@ -711,7 +725,8 @@ class LongStep:
     through a 16-slot staging ring restored into the cache."""
 
     def __init__(self, w, swap_bank_bytes, transport=0, row_transport=None, prompt_engines=None,
-                 row_link_blocks=None, row_engines=None, row_first=None, row_bank_bytes=None):
+                 row_link_blocks=None, row_engines=None, row_first=None, row_bank_bytes=None,
+                 row_in_transport=None, row_in_after=None):
         """row_transport: the row swap's kv_transport (None: the workload's
         default, else `transport`); prompt_engines: DMA engines of the
         prompt-streaming handles with the engine transport (None: the
@@ -723,7 +738,10 @@ class LongStep:
         are done (the two outgoing legs take the link one after the other);
         row_bank_bytes: the row swap's banks (None: the workload's default;
         0: the whole row image, packed in one pass before its copy and
-        unpacked in one pass after it)."""
+        unpacked in one pass after it); row_in_transport: the row swap-in's
+        kv_transport (None: the workload's default, else the row swap's);
+        row_in_after: the row swap-in's copies start once the row swap-out's
+        copies are done."""
         import torch
 
         import kv_cache_streaming_amd as kv
@@ -739,6 +757,9 @@ class LongStep:
         if row_engines is None:
             row_engines = [int(x) for x in DEFAULT_ROW_ENGINES.get(w.name, "-1").split(",")]
         self.row_first = DEFAULT_ROW_FIRST.get(w.name, False) if row_first is None else row_first
+        self.row_in_after = bool(row_in_after)
+        if row_in_transport is None:
+            row_in_transport = row_transport
         if row_bank_bytes is None:
             row_bank_bytes = DEFAULT_ROW_BANK_MIB.get(w.name, swap_bank_bytes >> 20) << 20
         self.row_done = torch.cuda.Event()
@@ -798,7 +819,7 @@ class LongStep:
         self.slot1 = (torch.empty(n1, dtype=torch.int16, device="cuda"),
                       torch.empty(n1, dtype=torch.int16, device="cuda"))
         self.eng_i = kv.KvSwap(self.lay1, _bank(torch, ob), _bank(torch, ob), ob, self.s["h2d"],
-                               rt)
+                               row_in_transport)
         # the first step swaps in whatever the second image holds: its bytes
         # only have to be there, not to be a real row (no kernels at set-up,
         # so a counter run sees the steps' launches only)
@@ -836,10 +857,13 @@ class LongStep:
             h.swap_out(self.A[0], self.A[1], l0, l1 - l0, self.row_start, self.row_count,
                        self.row_host[out].data_ptr() + l0 * self.row_layer,
                        (l1 - l0) * self.row_layer, self.s["out"],
-                       self.row_done if (self.row_first and i == n - 1) else None)
+                       self.row_done if ((self.row_first or self.row_in_after) and i == n - 1)
+                       else None)
         if self.row_first:
             for cs in self.p_copy:
                 cs.wait_event(self.row_done)
+        if self.row_in_after:
+            self.s["h2d"].wait_event(self.row_done)
         self.eng_i.swap_in(self.slot1[0], self.slot1[1], 0, w.L, [0], [max(self.row_count)],
                            self.row_host[inn], self.row_image, self.s["in"])
         k, n = 0, len(self.eng_p)
@@ -1450,11 +1474,16 @@ def main():
             args.row_first = int(DEFAULT_ROW_FIRST.get(w.name, False))
         if args.row_bank_mib is None:
             args.row_bank_mib = DEFAULT_ROW_BANK_MIB.get(w.name, args.swap_bank_mib)
+        if args.row_in_transport is None:
+            args.row_in_transport = args.row_transport
+        if args.row_in_after is None:
+            args.row_in_after = 0
         step = LongStep(w, args.swap_bank_mib << 20, TRANSPORTS[args.transport],
                         TRANSPORTS[args.row_transport],
                         [int(x) for x in args.prompt_engines.split(",")], args.row_link_blocks,
                         [int(x) for x in args.row_engines.split(",")], bool(args.row_first),
-                        args.row_bank_mib << 20)
+                        args.row_bank_mib << 20, TRANSPORTS[args.row_in_transport],
+                        bool(args.row_in_after))
     elif STEPS[w.name] is RingStep:
         step = RingStep(w, args.swap_bank_mib << 20, TRANSPORTS[args.transport],
                         [int(x) for x in args.prompt_engines.split(",")]
@@ -1471,6 +1500,7 @@ def main():
     else:
         step = STEPS[w.name](w, args.swap_bank_mib << 20, TRANSPORTS[args.transport])
     torch.cuda.synchronize()
+    progress(f"{w.name}: caches, banks and host images ready")
 
     if args.calibrate_copy_mib:
         # a plain elementwise kernel that reads and writes exactly this many
@@ -1491,6 +1521,7 @@ def main():
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
+    progress(f"{args.warmup} warm-up steps done")
     if not args.no_profile:
         kv.kv_profile_begin()
     t0 = time.perf_counter()
@@ -1498,6 +1529,7 @@ def main():
         step.run()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    progress(f"{args.steps} timed steps done: {elapsed / args.steps * 1000:.1f} ms per step")
     stats = {} if args.no_profile else kv.kv_profile_end()
     window = None if args.no_profile else kv.kv_profile_last_window()
     ms = elapsed / args.steps * 1000
@@ -1558,6 +1590,7 @@ def main():
     detail["link_directions"] = directions
     if not args.no_profile and not args.no_detail:
         ceil = link_ceiling(step, kv, TRANSPORTS[args.transport])
+        progress("link ceiling measured")
         detail["link_ceiling_GBps"] = ceil
         for name in ("d2h", "h2d"):
             directions[name]["frac_of_ceiling"] = round(directions[name]["GBps"] / ceil[name], 4)
@@ -1579,10 +1612,12 @@ def main():
                                                   step.row_count)
         if isinstance(step, RingStep):
             detail["repartition_2x2"] = step.repartition(kv)
+        progress("detail measured")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = (cpu_baseline(step, args.cpu_baseline_seconds) if isinstance(step, StreamStep)
                else cpu_baseline_layer(step, args.cpu_baseline_seconds))
+        progress("oracle baseline timed")
 
     line = {"metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
@@ -1600,6 +1635,8 @@ def main():
                            "prompt_engines": args.prompt_engines,
                            "row_engines": args.row_engines,
                            "row_first": args.row_first,
+                           "row_in_transport": args.row_in_transport,
+                           "row_in_after": args.row_in_after,
                            "row_bank_mib": args.row_bank_mib,
                            "row_link_blocks": args.row_link_blocks}
                           if isinstance(step, LongStep) else {}),
