@@ -193,8 +193,21 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // instead of sitting there dirty until the kernel's end-of-launch
 // write-back.  Measured on one GPT-2-1.5B layer packed alone (102 MB read +
 // write): 17.9 us instead of 20.4 us; 16-token paged packs 6% faster.
-// Stores to the caches (unpack) and the ring's step gather stay ordinary:
-// write-through gained nothing there, or lost 3-8%.
+// The ring's step gather stores ordinarily: write-through gained nothing
+// there, or lost 3-8%.  The split-role tile kernel (copy_split) also loads
+// with the non-temporal hint in both directions and stores to the caches
+// (unpack) with it: every byte is touched once, so nothing is worth keeping
+// in the caches on the way.  Measured alone on cold data (median of 20):
+// 48 GPT-2-1.5B layers in one call 0.78/0.76 -> 0.79/0.80 of HBM peak
+// (pack/unpack), a BLOOM-176B layer 0.72/0.73 -> 0.75/0.78, a 100K-context
+// row layer 0.75/0.75 -> 0.77/0.78; inside the 100K-context step its packs
+// 0.62-0.63 -> 0.66, inside the BLOOM step 0.72 -> 0.75 (unpacks 0.60 ->
+// 0.62), step times unchanged.  Non-temporal packed-buffer stores in place
+// of write-through raised the isolated packs a little more (0.80, 0.76,
+// 0.77) but cost the 100K step's in-step packs (0.63).  A plain streaming
+// copy kernel (one 16-byte vector per thread, 256 threads per workgroup,
+// 2 GiB) moves 6.08 TB/s (read + write) with ordinary and 6.46 TB/s with
+// non-temporal loads and stores on this GPU: the practical copy ceiling.
 constexpr int kWriteThrough = 1 | 16;   // sc0 | sc1
 
 // Buffer resource over `bytes` (< 2^31) of packed buffer from `base`.
@@ -345,7 +358,8 @@ __device__ __forceinline__ int32_t tile_row(const RowTiles &rtl, int32_t nb, int
 // unpacked, a 99,000-token 100K-context row layer 0.71 -> 0.74-0.76 both
 // ways, 48 GPT-2-1.5B layers in one call 0.75 -> 0.78 and 0.73-0.77 ->
 // 0.76-0.77.  Larger tiles (2 or 4 vectors per thread for K, V or both)
-// were slower on 8- and 16-vector heads.
+// were slower on 8- and 16-vector heads.  Loads, and the cache stores of
+// unpack, carry the non-temporal hint (the cache policy note above).
 template <int CT, int KPER, int VPER, bool kPack>
 __global__ __launch_bounds__(kThreads) void copy_split(Geometry g, RowTable rt, RowTiles rtl)
 {
@@ -406,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void copy_split(Geometry g, RowTable rt, 
             for (int p = 0; p < VPER; ++p) {
                 const int e = tid + p * kThreads;
                 if (e < n)
-                    r[p] = vc[e];
+                    r[p] = __builtin_nontemporal_load(vc + e);
             }
 #pragma unroll
             for (int p = 0; p < VPER; ++p) {
@@ -419,13 +433,13 @@ __global__ __launch_bounds__(kThreads) void copy_split(Geometry g, RowTable rt, 
             for (int p = 0; p < VPER; ++p) {
                 const int e = tid + p * kThreads;
                 if (e < n)
-                    r[p] = vs[e];
+                    r[p] = __builtin_nontemporal_load(vs + e);
             }
 #pragma unroll
             for (int p = 0; p < VPER; ++p) {
                 const int e = tid + p * kThreads;
                 if (e < n)
-                    vc[e] = r[p];
+                    __builtin_nontemporal_store(r[p], vc + e);
             }
         }
         return;
@@ -445,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void copy_split(Geometry g, RowTable rt, 
         for (int p = 0; p < KPER; ++p) {
             const int e = tid + p * kThreads, c = e / TTK, i = e % TTK;
             if (c < C && i < nt)
-                kr[p] = kc[(int64_t)c * g.Smax + i];
+                kr[p] = __builtin_nontemporal_load(kc + (int64_t)c * g.Smax + i);
         }
 #pragma unroll
         for (int p = 0; p < KPER; ++p) {
@@ -465,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void copy_split(Geometry g, RowTable rt, 
         for (int p = 0; p < KPER; ++p) {
             const int e = tid + p * kThreads;
             if (e < nvec)
-                kr[p] = ks[e];
+                kr[p] = __builtin_nontemporal_load(ks + e);
         }
 #pragma unroll
         for (int p = 0; p < KPER; ++p) {
@@ -478,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void copy_split(Geometry g, RowTable rt, 
         for (int p = 0; p < KPER; ++p) {
             const int e = tid + p * kThreads, c = e / TTK, i = e % TTK;
             if (c < C && i < nt)
-                kc[(int64_t)c * g.Smax + i] = lds[lds_slot<CT>(i, c, C)];
+                __builtin_nontemporal_store(lds[lds_slot<CT>(i, c, C)], kc + (int64_t)c * g.Smax + i);
         }
     }
 }
