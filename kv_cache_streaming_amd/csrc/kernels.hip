@@ -208,6 +208,15 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // copy kernel (one 16-byte vector per thread, 256 threads per workgroup,
 // 2 GiB) moves 6.08 TB/s (read + write) with ordinary and 6.46 TB/s with
 // non-temporal loads and stores on this GPU: the practical copy ceiling.
+// The paged kernels take the same hints (pool reads of the pack, packed
+// reads and pool writes of the unpack): 48 GPT-2-1.5B layers from 16-token
+// pages 0.68 -> 0.76 of peak packed, 0.70 -> 0.71 unpacked; 256-token
+// chunks 0.67 -> 0.69 and 0.71 -> 0.72.  The ring's step gather loads the
+// cache non-temporally when it packs: in the OPT-66B ring step its packs
+// run at 0.49 of peak beside the flushes instead of 0.38, though 24
+// GPT-2-1.5B steps packed alone take 0.90 us per step instead of 0.84.  It
+// keeps ordinary accesses when it unpacks (non-temporal there: OPT-66B
+// in-step unpacks 0.37 -> 0.33).
 constexpr int kWriteThrough = 1 | 16;   // sc0 | sc1
 
 // Buffer resource over `bytes` (< 2^31) of packed buffer from `base`.
@@ -268,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void copy_steps_lds(Geometry g, RowTable 
                 for (int j = 0; j < kB; ++j) {
                     const int32_t e = e0 + 64 * j, c = e / n, t = e - c * n;
                     if (e < nv)
-                        r[j] = kc[(int64_t)c * g.Smax + t];
+                        r[j] = __builtin_nontemporal_load(kc + (int64_t)c * g.Smax + t);
                 }
 #pragma unroll
                 for (int j = 0; j < kB; ++j) {
@@ -282,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void copy_steps_lds(Geometry g, RowTable 
 #pragma unroll
                 for (int j = 0; j < kB; ++j)
                     if (e0 + 64 * j < nv)
-                        r[j] = vc[e0 + 64 * j];
+                        r[j] = __builtin_nontemporal_load(vc + e0 + 64 * j);
 #pragma unroll
                 for (int j = 0; j < kB; ++j) {
                     const int32_t e = e0 + 64 * j, t = e / C, c = e - t * C;
@@ -640,13 +649,13 @@ __global__ __launch_bounds__(kThreads) void copy_paged_tiles(PagedGeometry g, Ro
                 uint32_t slot;
                 const int64_t u = unit_of(i, slot);
                 if (u >= 0)
-                    kr[p] = kpool[u + (int64_t)c * g.P + slot];
+                    kr[p] = __builtin_nontemporal_load(kpool + u + (int64_t)c * g.P + slot);
             }
             if (e < nvec) {
                 uint32_t slot;
                 const int64_t u = unit_of(e / C, slot);
                 if (u >= 0)
-                    vr[p] = vpool[u + (int64_t)slot * C + e % C];
+                    vr[p] = __builtin_nontemporal_load(vpool + u + (int64_t)slot * C + e % C);
             }
         }
 #pragma unroll
@@ -770,7 +779,7 @@ __global__ __launch_bounds__(kThreads) void unpack_paged_split(PagedGeometry g, 
         for (int p = 0; p < VPER; ++p) {
             const int e = tid + p * kThreads;
             if (e < n)
-                r[p] = vs[e];
+                r[p] = __builtin_nontemporal_load(vs + e);
         }
 #pragma unroll
         for (int p = 0; p < VPER; ++p) {
@@ -781,7 +790,7 @@ __global__ __launch_bounds__(kThreads) void unpack_paged_split(PagedGeometry g, 
                 paged_split(g, (uint32_t)(rt.start[b] + tok), q, slot);
                 const int32_t id = trow[q];
                 if (id >= 0 && id < g.NB)
-                    vpool[((layer * g.NB + id) * g.H + h) * CP + (int64_t)slot * C + c] = r[p];
+                    __builtin_nontemporal_store(r[p], vpool + ((layer * g.NB + id) * g.H + h) * CP + (int64_t)slot * C + c);
             }
         }
         return;
@@ -807,7 +816,7 @@ __global__ __launch_bounds__(kThreads) void unpack_paged_split(PagedGeometry g, 
     for (int p = 0; p < KPER; ++p) {
         const int e = tid + p * kThreads;
         if (e < nvec)
-            kr[p] = ks[e];
+            kr[p] = __builtin_nontemporal_load(ks + e);
     }
 #pragma unroll
     for (int p = 0; p < KPER; ++p) {
@@ -825,8 +834,8 @@ __global__ __launch_bounds__(kThreads) void unpack_paged_split(PagedGeometry g, 
             paged_split(g, o0 + (uint32_t)i, q, slot);
             const int32_t id = ids[q];
             if (id >= 0)
-                kw[((layer * g.NB + id) * g.H + h) * CP + (int64_t)c * g.P + slot] =
-                    lds[lds_slot<CT>(i, c, C)];
+                __builtin_nontemporal_store(lds[lds_slot<CT>(i, c, C)],
+                    kw + ((layer * g.NB + id) * g.H + h) * CP + (int64_t)c * g.P + slot);
         }
     }
 }
