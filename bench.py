@@ -932,9 +932,6 @@ DEFAULT_SWAP_BANK_MIB = {"bloom-176b-10l": 0}
 DEFAULT_OUT_ENGINES = {"opt-66b-16l": "0"}
 
 
-def default_out_engines(name):
-    e = DEFAULT_OUT_ENGINES.get(name)
-    return [int(x) for x in e.split(",")] if e else None
 DEFAULT_PROMPT_ENGINES = {"gqa-100k": "0,0"}
 # the OPT-66B ring step restores the previous step's image while it flushes:
 # 6.53 ms (92.4 GB/s across the link, both directions at 46.2 GB/s) against
@@ -946,6 +943,12 @@ DEFAULT_ROW_LINK_BLOCKS = {"gqa-100k": 16}
 DEFAULT_ROW_ENGINES = {}
 DEFAULT_ROW_FIRST = {"gqa-100k": True}
 DEFAULT_ROW_BANK_MIB = {"gqa-100k": 0}
+
+
+def default_out_engines(name):
+    e = DEFAULT_OUT_ENGINES.get(name)
+    return [int(x) for x in e.split(",")] if e else None
+
 
 def link_ceiling(step, kv, transport, target_bytes=4 << 30, reps=3):
     """GB/s the host link reaches through this library with `transport`, each
