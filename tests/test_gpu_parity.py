@@ -67,9 +67,12 @@ def check_pack_unpack(kv, dims, l0, nl, start, count, seed, bits=True, dtype=0):
     assert np.array_equal(host(st)[:want.size], want), "unpack wrote its staging input"
 
 
-@pytest.mark.parametrize("D", [8, 16, 24, 32, 64, 128, 256, 512, 1024])
+@pytest.mark.parametrize("D", [8, 16, 24, 32, 64, 72, 96, 128, 200, 256, 320, 512, 776, 1024])
 def test_tiled_ranges_every_head_dim(kv, D):
-    """Multi-token ranges (tile kernel), several tiles and a ragged tail per row."""
+    """Multi-token ranges (tile kernel), several tiles and a ragged tail per row.
+    Head sizes of 9, 12, 25, 40 and 97 vectors take the kernels' generic
+    variants (one vector per thread up to 32 vectors, four above), whose
+    tiles do not divide 256 or 1024 vectors evenly."""
     rng = np.random.default_rng(D)
     C = D // 8
     tile = max(1, 1024 // C)
@@ -85,7 +88,7 @@ def test_tiled_ranges_every_head_dim(kv, D):
         check_pack_unpack(kv, dims, 0, 3, st, ct, seed=D * 10 + it)
 
 
-@pytest.mark.parametrize("D", [8, 16, 24, 64, 128, 1024])
+@pytest.mark.parametrize("D", [8, 16, 24, 64, 96, 128, 320, 1024])
 def test_few_tokens_every_head_dim(kv, D):
     """Decode-like ranges (at most 8 tokens per row: the small kernel)."""
     rng = np.random.default_rng(100 + D)

@@ -46,7 +46,8 @@ SMALL_DESTS = [(0, 10, 0, 10, 0, 20),     # holds all of the source
 
 
 @pytest.mark.parametrize("D,S,counts", [(64, 700, "tiles"), (128, 300, "tiles"),
-                                        (24, 200, "tiles"), (64, 40, "decode")])
+                                        (24, 200, "tiles"), (320, 180, "tiles"),
+                                        (64, 40, "decode")])
 def test_pieces_and_merge_small(kv, D, S, counts):
     import torch
     src = (2, 3, 1, 3, 10, 3)
