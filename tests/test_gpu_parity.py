@@ -394,6 +394,18 @@ def test_ring_gather_at_flush_runs(kv, D, R, steps):
     run_ring(kv, dims, R, pos, seed=24, gather=1, caches=2)
 
 
+@pytest.mark.parametrize("gather", [0, 1])
+@pytest.mark.parametrize("D,R,steps", [(1024, 16, 21), (512, 20, 23)])
+def test_ring_wide_units_past_the_lds_pass(kv, D, R, steps, gather):
+    """Runs of steps whose unit holds more than 1024 vectors (16 steps of a
+    128-vector head, 20 of a 64-vector one) take the per-vector step kernel
+    instead of the LDS pass: gathered at flush, and unpacked in runs by the
+    restore in both gather modes."""
+    dims = (2, 3, 2, D, 48)
+    pos = [[j, 5 + j, 20 + j] for j in range(steps)]
+    run_ring(kv, dims, R, pos, seed=27 + D, gather=gather)
+
+
 @pytest.mark.parametrize("D", [8, 24, 64, 128])
 def test_ring_gather_at_flush_many_units(kv, D):
     """Gather at flush over 105 (layer, row, head) units at ragged row
