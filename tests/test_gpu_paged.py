@@ -44,6 +44,9 @@ CASES = [  # L, H, D, P, B, stride, ranges
     (3, 2, 24, 5, 3, 90, "tiles"),
     (2, 2, 96, 16, 3, 20, "tiles"),         # 12-vector heads: the generic one-vector tiles
     (2, 2, 320, 16, 3, 12, "tiles"),        # 40-vector heads: the generic four-vector tiles
+    (2, 3, 8, 16, 3, 10, "tiles"),          # 1-vector heads
+    (2, 2, 256, 16, 3, 8, "tiles"),         # 32-vector heads: four vectors per thread
+    (2, 1, 1024, 16, 2, 6, "tiles"),        # 128-vector heads
     (2, 2, 64, 1, 2, 300, "tiles"),
     (2, 3, 64, 16, 5, 8, "decode"),
     (2, 3, 64, 16, 6, 10, "span"),          # empty rows before, inside and after the moved ones
