@@ -995,22 +995,30 @@ def link_ceiling(step, kv, transport, target_bytes=4 << 30, reps=3):
     return res
 
 
-def hbm_copy_ceiling(torch, nbytes=1 << 30, reps=4):
-    """GB/s (read + write) of a plain 1 GiB device-to-device copy."""
-    a = torch.empty(4 * nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
+def hbm_copy_ceiling(torch, kv, nbytes=2 << 30, warm=5, reps=20):
+    """What HBM gives a plain copy on this GPU, read + write: the library's
+    kv_copy_packed (one 16-byte vector per thread, non-temporal loads and
+    stores) on 2 GiB, timed from its dispatches, median of `reps` after `warm`
+    (2 GiB each way is well past the 256 MB Infinity Cache); and torch's own
+    device-to-device copy of the same buffers, timed with events."""
+    a = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
     b = torch.empty_like(a)
-    n = nbytes // 2
-    b[:n].copy_(a[:n])
-    torch.cuda.synchronize()
-    e0, e1 = TimingEvent(), TimingEvent()
-    e0.record()
-    for r in range(reps):           # rotate over 4 GiB: more than the Infinity Cache
-        b[r % 4 * n:(r % 4 + 1) * n].copy_(a[r % 4 * n:(r % 4 + 1) * n])
-    e1.record()
-    torch.cuda.synchronize()
-    gbps = 2 * reps * nbytes / (e0.elapsed_time(e1) / 1000) / 1e9
+    s = torch.cuda.Stream()
+    secs = []
+    for i in range(warm + reps):
+        kv.kv_profile_begin()
+        kv.kv_copy_packed(b, a, nbytes, stream=s)
+        torch.cuda.synchronize()
+        stats = kv.kv_profile_end()
+        if i >= warm:
+            secs.append(stats["copy_packed"][1] / 1000)
+    out = {"bytes_each_way": nbytes}
+    rate_entry(out, "kv_copy_packed", secs, 2 * nbytes, HBM_PEAK_GBPS, "_GBps")
+    torch_secs = rep_seconds(torch, lambda: b.copy_(a), torch.cuda.current_stream(), warm=2,
+                             reps=5)
+    rate_entry(out, "torch_copy", torch_secs, 2 * nbytes, HBM_PEAK_GBPS, "_GBps")
     del a, b
-    return gbps
+    return out
 
 
 def rep_seconds(torch, fn, s=None, warm=5, reps=20):
@@ -1602,7 +1610,6 @@ def main():
                 step, kv, TRANSPORTS[args.row_transport])
         if isinstance(step, StreamStep):
             detail["decode_step_us"] = decode_step_us(step, kv)
-            detail["hbm_copy_ceiling_GBps"] = round(hbm_copy_ceiling(torch), 1)
             detail["large_slices"] = large_slices(step, kv)
             if step.w.B * step.w.Smax >= 4096:
                 detail["paged_slices"] = paged_slices(step, kv)
@@ -1615,6 +1622,7 @@ def main():
                                                   step.row_count)
         if isinstance(step, RingStep):
             detail["repartition_2x2"] = step.repartition(kv)
+        detail["hbm_copy_ceiling"] = hbm_copy_ceiling(torch, kv)
         progress("detail measured")
     cpu = None
     if not args.no_cpu_baseline:
@@ -1659,6 +1667,11 @@ def main():
         "pack_unpack_kernel": roofline["kernel"] if roofline else None,
         "pack_unpack_together_GBps": together["GBps"] if together else None,
         "pack_unpack_together_hbm_frac": together["frac_of_peak"] if together else None}
+    ceiling = detail.get("hbm_copy_ceiling")
+    if ceiling and roofline:
+        # the dominant kernel against what HBM gives a plain copy on this GPU
+        line["metric_parts"]["pack_unpack_frac_of_copy_ceiling"] = round(
+            roofline["achieved"] / ceiling["kv_copy_packed_GBps"], 4)
     print(json.dumps(line), flush=True)
 
 

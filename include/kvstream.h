@@ -261,6 +261,19 @@ int kv_stream_in(const kv_layout *lay, const kv_part *dst, void *k, void *v,
                  const kv_part *src, const int32_t *start, const int32_t *count,
                  const void *staging, int64_t staging_bytes, hipStream_t s);
 
+/* Move a packed block from one device buffer to another on the same GPU
+ * ([DV, Fast prompt KV transfer]: the prompt worker's packed KV goes to the
+ * token worker's buffer; Table 1: stream_out's pieces reach the workers
+ * that merge them).  When both workers share a GPU the move is a plain
+ * device-to-device copy: `bytes` (a multiple of 16) from `src` to `dst`, both
+ * 16-byte aligned device memory inside one allocation each, not
+ * overlapping (else KV_EINVAL; negative bytes KV_ESIZE; 0 bytes enqueues
+ * nothing).  Enqueued on `s`; every byte is read once and written once with
+ * the non-temporal hint, one 16-byte vector per thread -- the fastest plain
+ * copy measured on MI355X, so its rate is also the practical HBM ceiling
+ * the pack and unpack kernels are compared with. */
+int kv_copy_packed(void *dst, const void *src, int64_t bytes, hipStream_t s);
+
 /* ---------------------------------------------------------------------------
  * Swap engine: staged, layer-pipelined transfers between a cache and pinned
  * host memory ([DV, Microbatch swapping workflow, Fig 9]; flush/fetch in

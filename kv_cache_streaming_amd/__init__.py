@@ -118,6 +118,7 @@ _SIGNATURES = {
     "kv_stream_bytes": (_I64, [_LAY, _PART, _PART, _P]),
     "kv_stream_out": (ctypes.c_int, [_LAY, _PART, _P, _P, _PART, _P, _P, _P, _I64, _P]),
     "kv_stream_in": (ctypes.c_int, [_LAY, _PART, _P, _P, _PART, _P, _P, _P, _I64, _P]),
+    "kv_copy_packed": (ctypes.c_int, [_P, _P, _I64, _P]),
     "kv_swap_create": (ctypes.c_int, [ctypes.POINTER(_P), _LAY, _P, _P, _I64, _P, _I32]),
     "kv_swap_destroy": (ctypes.c_int, [_P]),
     "kv_swap_set_option": (ctypes.c_int, [_P, _I32, _I64]),
@@ -408,6 +409,13 @@ def kv_stream_in(lay, dst_part, k, v, src_part, start, count, staging, staging_b
     _check(_lib.kv_stream_in(ctypes.byref(lay), ctypes.byref(dst), _addr(k), _addr(v),
                              ctypes.byref(_part(src_part)), st.ptr, ct.ptr, _addr(staging), nb,
                              _stream(stream)), "kv_stream_in")
+
+
+def kv_copy_packed(dst, src, nbytes=None, stream=None) -> None:
+    """Device-to-device move of a packed block (``nbytes`` defaults to the
+    source's size)."""
+    nb = _nbytes(src) if nbytes is None else nbytes
+    _check(_lib.kv_copy_packed(_addr(dst), _addr(src), nb, _stream(stream)), "kv_copy_packed")
 
 
 # ---------------------------------------------------------------- swap engine

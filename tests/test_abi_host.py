@@ -142,6 +142,14 @@ def test_errors_before_any_hip_call(kv):
         kv.kv_pack_tokens(lay, fake, fake, 0, 1, None, None, fake, 1 << 20, stream=0)
     assert e.value.status == kv.KV_EINVAL
     assert "start" in kv.kv_last_error()
+    for dst, src, nbytes, status in ((fake, fake, 24, kv.KV_EINVAL),   # not whole vectors
+                                     (fake, fake, -16, kv.KV_ESIZE),
+                                     (0, fake, 64, kv.KV_EINVAL),      # NULL destination
+                                     (fake, 0, 64, kv.KV_EINVAL)):
+        with pytest.raises(kv.KvError) as e:
+            kv.kv_copy_packed(dst, src, nbytes, stream=0)
+        assert e.value.status == status
+    kv.kv_copy_packed(fake, fake, 0, stream=0)   # nothing to move: nothing enqueued
 
 
 def replay_plan(kv, dims, l0, nl, start, count, bank_bytes, seed):

@@ -244,6 +244,44 @@ def test_prompt_layer_chunks(kv):
             assert np.array_equal(host(dk2), ek) and np.array_equal(host(dv2), ev)
 
 
+@pytest.mark.parametrize("nbytes", [16, 4096, 4096 + 16, (1 << 20) + 48, 300 << 20])
+def test_copy_packed_moves_every_byte(kv, nbytes):
+    """kv_copy_packed is a plain copy: the destination equals the source
+    bit for bit, and nothing past the destination range is written
+    (sizes below, at and just past one workgroup's 4 KiB, and a 300 MiB
+    block of many workgroups)."""
+    import torch
+    note(f"copy_packed {nbytes} bytes")
+    words = nbytes // 2
+    src = dev(synth.random_bits(words, 600 + nbytes % 997))
+    dst = empty(words, extra=CANARY)
+    kv.kv_copy_packed(dst, src, nbytes)
+    torch.cuda.synchronize()
+    got = host(dst)
+    assert np.array_equal(got[:words], host(src)), "copy differs from its source"
+    assert np.all(got[words:] == 0x7A7A), "copy wrote past its destination"
+
+
+def test_copy_packed_refuses_bad_buffers(kv):
+    """Overlapping ranges, a misaligned address and pageable host memory are
+    refused before anything is enqueued (the range-inside-one-allocation
+    check is the one every entry point shares; its test is below)."""
+    import torch
+    a = empty(1024)
+    with pytest.raises(kv.KvError) as e:          # overlapping ranges of one buffer
+        kv.kv_copy_packed(a[256:], a, 1024)
+    assert e.value.status == kv.KV_EINVAL
+    with pytest.raises(kv.KvError) as e:          # misaligned destination
+        kv.kv_copy_packed(a.data_ptr() + 8, a.data_ptr() + 1024, 512)
+    assert e.value.status == kv.KV_EINVAL
+    h = np.zeros(512, np.uint16)                  # pageable host memory
+    with pytest.raises(kv.KvError) as e:
+        kv.kv_copy_packed(a, h.ctypes.data, 1024)
+    assert e.value.status == kv.KV_EINVAL
+    torch.cuda.synchronize()
+    assert np.all(host(a) == 0x7A7A), "a refused copy wrote"
+
+
 def test_error_paths(kv):
     import torch
     dims = (2, 2, 2, 16, 8)
