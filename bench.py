@@ -61,6 +61,12 @@ if int(os.environ.get("GPU_MAX_HW_QUEUES", "0") or 0) < 16:
     os.environ["GPU_MAX_HW_QUEUES"] = "16"
 
 METRIC = "KV pack/unpack GB/s (% HBM peak) + swap host-link GB/s, 1 MI355X"
+# The pages' own figures around this path (other hardware; context, not targets):
+# DejaVu's serving throughput over FasterTransformer, and the estimate of one
+# 2048-token OPT-175B prompt-KV transfer (9 GiB) over eight PCIe 5.0 x16 links.
+PAGES_THROUGHPUT_VS_FT = "1.88x (OPT-66B), 2x (BLOOM-176B): system throughput on A100-80GB / V100-16GB clusters"
+PAGES_OPT175B_KV_BYTES = 2048 * 4.5 * (1 << 20)   # 2048 tokens x 4.5 MiB
+PAGES_OPT175B_ESTIMATE_MS = 17.6                  # over 8 links of 64 GB/s
 HBM_PEAK_GBPS = 8000.0
 PCIE_PEAK_GBPS = 63.0          # PCIe 5.0 x16, per direction
 
@@ -1667,6 +1673,20 @@ def main():
         "pack_unpack_kernel": roofline["kernel"] if roofline else None,
         "pack_unpack_together_GBps": together["GBps"] if together else None,
         "pack_unpack_together_hbm_frac": together["frac_of_peak"] if together else None}
+    if roofline:
+        line["metric_parts"]["pack_unpack_payload_GBps"] = round(roofline["achieved"] / 2, 1)
+        if roofline["traffic"]:
+            line["metric_parts"]["pack_unpack_counter_traffic_GBps"] = round(
+                roofline["traffic"] / (roofline["avg_us"] * 1e3), 1)
+    # the pages' transfer estimate redone with this link's measured rate
+    d2h = detail.get("link_ceiling_GBps", {}).get("d2h") or directions["d2h"]["GBps"]
+    if d2h:
+        one = PAGES_OPT175B_KV_BYTES / (d2h * 1e9) * 1000
+        line["context"] = {"pages_throughput_vs_fastertransformer": PAGES_THROUGHPUT_VS_FT,
+                           "pages_opt175b_2048_token_kv_ms_estimate_8_links": PAGES_OPT175B_ESTIMATE_MS,
+                           "same_9_GiB_at_this_link_GBps": d2h,
+                           "same_9_GiB_ms_one_link": round(one, 1),
+                           "same_9_GiB_ms_8_links": round(one / 8, 1)}
     ceiling = detail.get("hbm_copy_ceiling")
     if ceiling and roofline:
         # the dominant kernel against what HBM gives a plain copy on this GPU
