@@ -131,6 +131,8 @@ def parse_args():
                     help="gqa-100k: the row swap-in's copies wait for the row swap-out's (1)")
     ap.add_argument("--row-link-blocks", type=int, default=None,
                     help="gqa-100k: link-copy workgroups of the row swap-out (KV_OPT_LINK_BLOCKS)")
+    ap.add_argument("--link-blocks", type=int, default=None,
+                    help="bloom-176b-10l: link-copy workgroups of the swap-out (KV_OPT_LINK_BLOCKS)")
     ap.add_argument("--ring-duplex", type=int, choices=(0, 1), default=None,
                     help="opt-66b-16l: restore the image the other ring flushed in the previous "
                          "step while this step's flushes go out (1), or flush and then restore "
@@ -562,10 +564,12 @@ class SwapStep:
     layer's unpack waiting only for that layer's pack (both link directions at
     once)."""
 
-    def __init__(self, w, swap_bank_bytes, transport=0, out_engines=None):
+    def __init__(self, w, swap_bank_bytes, transport=0, out_engines=None, link_blocks=None):
         """out_engines: with the engine transport, the DMA engines of the
         swap-out handles (layers alternate over them, each handle with its own
-        copy stream); None: one handle, an idle engine at each copy."""
+        copy stream); None: one handle, an idle engine at each copy.
+        link_blocks: workgroups of the swap-out's link-copy kernel
+        (KV_OPT_LINK_BLOCKS; None: the library's default)."""
         import torch
 
         import kv_cache_streaming_amd as kv
@@ -597,6 +601,9 @@ class SwapStep:
                               torch.cuda.Stream(), transport)
                 h.set_option(kv.KV_OPT_DMA_ENGINE, e)
                 self.eng_out.append(h)
+        if link_blocks:
+            for h in self.eng_out:
+                h.set_option(kv.KV_OPT_LINK_BLOCKS, link_blocks)
         self.eng_i = kv.KvSwap(self.lay, _bank(torch, sb), _bank(torch, sb), sb, self.s["h2d"],
                                transport)
         self.packed = [torch.cuda.Event() for _ in range(L)]
@@ -1513,7 +1520,7 @@ def main():
     elif STEPS[w.name] is SwapStep:
         step = SwapStep(w, args.swap_bank_mib << 20, TRANSPORTS[args.transport],
                         [int(x) for x in args.prompt_engines.split(",")]
-                        if args.prompt_engines else None)
+                        if args.prompt_engines else None, args.link_blocks)
     else:
         step = STEPS[w.name](w, args.swap_bank_mib << 20, TRANSPORTS[args.transport])
     torch.cuda.synchronize()
