@@ -147,8 +147,9 @@ def parse_args():
                          "slices, schedule): a kernel trace then holds the steps' launches only")
     ap.add_argument("--slices-only", action="store_true",
                     help="run only the isolated large-slice calls of the workload (the ones the "
-                         "70%%-of-peak bar applies to) and print their rates: a profiler run then "
-                         "holds those launches alone")
+                         "70%%-of-peak bar applies to; for gpt2-1.5b also the paged-pool calls, "
+                         "for opt-66b-16l the split/merge calls) and print their rates: a "
+                         "profiler run then holds those launches alone")
     ap.add_argument("--no-profile", action="store_true",
                     help="do not time launches with events (for external profilers)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -1137,14 +1138,21 @@ def layer_slices(step, kv, cache, start, count, warm=5, reps=20):
 
 def slices_only(step, kv):
     """The isolated large-slice calls of a workload (each moves 256 MiB of
-    payload or more): 48 GPT-2-1.5B layers in one call, a BLOOM-176B layer of
-    every row, one layer of the longest 100K-context row."""
+    payload or more): 48 GPT-2-1.5B layers in one call (and the same prompt
+    from paged pools of 16- and 256-token blocks), a BLOOM-176B layer of
+    every row, one layer of the longest 100K-context row, and the OPT-66B
+    slice's split into 2 stages x 2 ranks and its merge."""
     if isinstance(step, StreamStep):
-        return {"gpt2_48_layers": large_slices(step, kv)}
+        out = {"gpt2_48_layers": large_slices(step, kv)}
+        if step.w.B * step.w.Smax >= 4096:
+            out["paged"] = paged_slices(step, kv)
+        return out
     if isinstance(step, SwapStep):
         return {"bloom_layer": layer_slices(step, kv, step.slots[0], step.rows_start, step.rows)}
     if isinstance(step, LongStep):
         return {"long_row_layer": layer_slices(step, kv, step.A, step.row_start, step.row_count)}
+    if isinstance(step, RingStep):
+        return {"repartition_2x2": step.repartition(kv)}
     return {}
 
 
