@@ -1191,6 +1191,55 @@ def paged_slices(step, kv):
     return out
 
 
+def decode_loop(step, kv, cache, reps=5):
+    """A decode loop that packs each step as it comes: one kv_pack_tokens call
+    per step (one token per row at the workload's decode positions, every
+    layer) into that step's slot of a staging buffer.  Wall time per step of
+    the whole loop, events on its stream around it (best of `reps` after two
+    warm-up loops): issued from Python call by call, and captured once into a
+    HIP graph and replayed.  The replay's bytes are compared with the eager
+    loop's; the kernels' own time per step comes from their dispatches."""
+    torch, lay = step.torch, step.lay
+    positions = step.positions
+    n = len(positions)
+    slot = kv.kv_pack_bytes(lay, lay.L, None, 1)
+    st = torch.zeros(n * slot // 2, dtype=torch.int16, device="cuda")
+    base = st.data_ptr()
+    k, v = cache
+    s = torch.cuda.Stream()
+
+    def loop():
+        for j, pos in enumerate(positions):
+            kv.kv_pack_tokens(lay, k, v, 0, lay.L, pos, None, base + j * slot, slot, s)
+
+    eager = min(rep_seconds(torch, loop, s, warm=2, reps=reps))
+    kv.kv_profile_begin()
+    loop()
+    torch.cuda.synchronize()
+    kernel_ms = sum(x[1] for x in kv.kv_profile_end().values())
+    want = st.clone()
+    st.zero_()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s, capture_error_mode="relaxed"):
+        loop()
+    torch.cuda.synchronize()
+
+    def replay():
+        with torch.cuda.stream(s):
+            g.replay()
+
+    graph = min(rep_seconds(torch, replay, s, warm=2, reps=reps))
+    torch.cuda.synchronize()
+    same = bool(torch.equal(st, want))
+    del g, st, want
+    return {"steps": n, "bytes_per_step": slot,
+            "eager_us_per_step": round(eager / n * 1e6, 2),
+            "graph_us_per_step": round(graph / n * 1e6, 2),
+            "kernel_us_per_step": round(kernel_ms * 1000 / n, 2),
+            "graph_matches_eager": same}
+
+
 def decode_step_us(step, kv, reps=3):
     """GPU time per decode step of the workload's decode steps, with a ring of
     one bank holding them all (no bank reuse, so no wait for a flush copy):
@@ -1631,6 +1680,7 @@ def main():
                 step, kv, TRANSPORTS[args.row_transport])
         if isinstance(step, StreamStep):
             detail["decode_step_us"] = decode_step_us(step, kv)
+            detail["decode_loop"] = decode_loop(step, kv, step.caches["B"])
             detail["large_slices"] = large_slices(step, kv)
             if step.w.B * step.w.Smax >= 4096:
                 detail["paged_slices"] = paged_slices(step, kv)
@@ -1641,8 +1691,10 @@ def main():
         if isinstance(step, LongStep):
             detail["layer_slices"] = layer_slices(step, kv, step.A, step.row_start,
                                                   step.row_count)
+            detail["decode_loop"] = decode_loop(step, kv, step.A)
         if isinstance(step, RingStep):
             detail["repartition_2x2"] = step.repartition(kv)
+            detail["decode_loop"] = decode_loop(step, kv, step.A)
         detail["hbm_copy_ceiling"] = hbm_copy_ceiling(torch, kv)
         progress("detail measured")
     cpu = None
