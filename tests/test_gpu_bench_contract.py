@@ -48,3 +48,13 @@ def test_headline_line():
     assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0
     parts = d["metric_parts"]
     assert parts["swap_host_link_GBps"] == d["value"] and parts["pack_unpack_GBps"] == rf["achieved"]
+    assert abs(parts["pack_unpack_payload_GBps"] - rf["achieved"] / 2) <= 0.1
+    if rf["traffic"]:
+        assert abs(parts["pack_unpack_counter_traffic_GBps"] -
+                   rf["traffic"] / (rf["avg_us"] * 1e3)) <= 0.01 * rf["achieved"]
+    # the pages' context figures beside this link's measured rate
+    ctx = d["context"]
+    assert ctx["pages_opt175b_2048_token_kv_ms_estimate_8_links"] == 17.6
+    assert ctx["same_9_GiB_at_this_link_GBps"] == d["detail"]["link_directions"]["d2h"]["GBps"]
+    assert abs(ctx["same_9_GiB_ms_one_link"] - 9 * 2 ** 30 / (ctx["same_9_GiB_at_this_link_GBps"]
+                                                              * 1e9) * 1000) <= 0.1
