@@ -1,10 +1,11 @@
 /* A plain C99 user of kvstream.h on the GPU: device memory from the HIP
  * runtime's C API, every buffer handed to the library as a bare pointer.
  * It fills a small cache on the host, then runs through the C ABI a ragged
- * multi-token pack and its unpack, a staged swap-out to pinned host memory,
- * and a staging ring (push, flush, restore), and writes the caches it made
- * and every result to <dir>/<name>.bin for tests/test_gpu_c_abi.py to check
- * against the oracle.  Prints "<call> <status>" per library call and "done"
+ * multi-token pack, a move of the packed block to another device buffer,
+ * the pack's unpack, a staged swap-out to pinned host memory, and a staging
+ * ring (push, flush, restore), and writes the caches it made and every
+ * result to <dir>/<name>.bin for tests/test_gpu_c_abi.py to check against
+ * the oracle.  Prints "<call> <status>" per library call and "done"
  * at the end; exits non-zero at the first failure. */
 #include "kvstream.h"
 
@@ -111,6 +112,14 @@ int main(int argc, char **argv)
         !hip_ok(hipStreamSynchronize(s), "hipStreamSynchronize") ||
         !save_dev("pack", stage, (size_t)need))
         return 1;
+    /* the packed block moved to a second device buffer */
+    void *stage2;
+    if (!hip_ok(hipMalloc(&stage2, (size_t)need), "hipMalloc") ||
+        !lib_ok(kv_copy_packed(stage2, stage, need, s), "kv_copy_packed") ||
+        !hip_ok(hipStreamSynchronize(s), "hipStreamSynchronize") ||
+        !save_dev("copy", stage2, (size_t)need))
+        return 1;
+    (void)hipFree(stage2);
     if (!hip_ok(hipMemset(zk, 0, cache_bytes), "hipMemset") ||
         !hip_ok(hipMemset(zv, 0, cache_bytes), "hipMemset") ||
         !lib_ok(kv_unpack_tokens(&lay, zk, zv, 0, L_, start, count, stage, need, s),

@@ -1,9 +1,9 @@
 """The boundary on the GPU from C: a C99 program (tests/c_abi_device.c) that
 allocates device and pinned host memory with the HIP runtime's C API and
 drives the library through include/kvstream.h alone -- a ragged multi-token
-pack and unpack, a staged swap-out, and a staging ring's push, flush and
-restore.  Every result it writes must equal the oracle's on the caches the
-program itself generated."""
+pack, a move of the packed block and its unpack, a staged swap-out, and a
+staging ring's push, flush and restore.  Every result it writes must equal
+the oracle's on the caches the program itself generated."""
 import os
 import shutil
 import subprocess
@@ -51,7 +51,8 @@ def outputs(tmp_path_factory):
 
 def test_every_call_succeeds(outputs):
     calls, _ = outputs
-    for name in ("kv_layout_init", "kv_pack_tokens", "kv_unpack_tokens", "kv_swap_create",
+    for name in ("kv_layout_init", "kv_pack_tokens", "kv_copy_packed", "kv_unpack_tokens",
+                 "kv_swap_create",
                  "kv_swap_out", "kv_swap_destroy", "kv_ring_create", "kv_ring_push",
                  "kv_ring_flush", "kv_ring_restore", "kv_ring_destroy"):
         assert calls.get(name) == "0", (name, calls.get(name))
@@ -63,6 +64,7 @@ def test_pack_unpack_from_c(outputs):
     K, V = f["k"].reshape(L, B, H, D // 8, S, 8), f["v"].reshape(L, B, H, S, D)
     want = oracle.pack(DIMS, K, V, 0, L, START, COUNT)
     assert np.array_equal(f["pack"], want)
+    assert np.array_equal(f["copy"], want)          # kv_copy_packed of the packed block
     zk, zv = np.zeros_like(K), np.zeros_like(V)
     oracle.unpack(DIMS, zk, zv, 0, L, START, COUNT, want)
     assert np.array_equal(f["unpack_k"], zk.ravel())
