@@ -25,6 +25,13 @@ average duration, both measured live with hipEvents bound to every launch's
 dispatch (the kernel's own begin and end timestamps).  `cpu_baseline` is the
 oracle on a bounded sample of the same step (single-threaded; its
 `all_cores` entry runs the same calls in pieces over the host's cores).
+`metric_parts` sets the metric's two figures side by side (host-link rates
+per direction against PCIe peak; the dominant kernel's algorithmic, payload
+and counted-traffic rates against HBM peak and, with the detail, against
+the plain-copy ceiling); `context` puts the pages' own figures beside the
+measured link; `detail` holds every kernel's launches and rates and the
+isolated measurements (link and HBM copy ceilings, large slices, decode
+loops, the microbatch schedule, the 2 x 2 repartition).
 
 `--workload` selects the other shapes, each with the step its class below
 describes: gpt2-1.5b (StreamStep: prompt streaming of 48 layers beside the
