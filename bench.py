@@ -31,7 +31,8 @@ and counted-traffic rates against HBM peak and, with the detail, against
 the plain-copy ceiling); `context` puts the pages' own figures beside the
 measured link; `detail` holds every kernel's launches and rates and the
 isolated measurements (link and HBM copy ceilings, large slices, decode
-loops, the microbatch schedule, the 2 x 2 repartition).
+loops, a decode step sent buffered against one copy call per region, the
+microbatch schedule, the 2 x 2 repartition).
 
 `--workload` selects the other shapes, each with the step its class below
 describes: gpt2-1.5b (StreamStep: prompt streaming of 48 layers beside the
@@ -69,11 +70,14 @@ if int(os.environ.get("GPU_MAX_HW_QUEUES", "0") or 0) < 16:
 
 METRIC = "KV pack/unpack GB/s (% HBM peak) + swap host-link GB/s, 1 MI355X"
 # The pages' own figures around this path (other hardware; context, not targets):
-# DejaVu's serving throughput over FasterTransformer, and the estimate of one
-# 2048-token OPT-175B prompt-KV transfer (9 GiB) over eight PCIe 5.0 x16 links.
+# DejaVu's serving throughput over FasterTransformer, the estimate of one
+# 2048-token OPT-175B prompt-KV transfer (9 GiB) over eight PCIe 5.0 x16 links,
+# and the gain of buffered copies over one copy call per small region when
+# streaming a request's cache out (prompt 500, 500 new tokens).
 PAGES_THROUGHPUT_VS_FT = "1.88x (OPT-66B), 2x (BLOOM-176B): system throughput on A100-80GB / V100-16GB clusters"
 PAGES_OPT175B_KV_BYTES = 2048 * 4.5 * (1 << 20)   # 2048 tokens x 4.5 MiB
 PAGES_OPT175B_ESTIMATE_MS = 17.6                  # over 8 links of 64 GB/s
+PAGES_BUFFERED_GAIN = "95x: buffered copies over many small copy calls, streaming to remote CPU memory"
 HBM_PEAK_GBPS = 8000.0
 PCIE_PEAK_GBPS = 63.0          # PCIe 5.0 x16, per direction
 
@@ -1247,6 +1251,118 @@ def decode_loop(step, kv, cache, reps=5):
             "graph_matches_eager": same}
 
 
+def buffered_vs_naive(step, kv, cache, reps=3, max_copies=200_000, keep_image=False):
+    """One decode step's new keys and values (one token per row at the
+    workload's first decode positions, every layer) sent to pinned host
+    memory in two ways.  Buffered, as the library does it: one kv_pack_tokens
+    call into a staging slot, then one device-to-host copy of the slot.
+    Naive: one runtime copy per contiguous piece of the cache, straight to
+    that piece's place in the same host image.  "per_piece" issues one copy
+    per 16-byte key vector and one per value row.  "per_head" issues, per
+    head, one strided 2-D copy of its key vectors and one copy of its value
+    row.  The naive copies are issued from Python through ctypes.
+    `ctypes_us_per_call` is what that loop costs per call around a runtime
+    call that does no work.  Times are wall time from the first call to the
+    end of the stream, best of `reps`.  The three host images must be
+    byte-identical; `keep_image` returns the buffered one as `image`."""
+    torch, lay = step.torch, step.lay
+    L, B, H, D, S = lay.L, lay.B, lay.H, lay.D, lay.Smax
+    C, P = D // 8, 2
+    pos = [int(p) for p in step.positions[0]]
+    assert all(0 <= p < S for p in pos)
+    slot = kv.kv_pack_bytes(lay, L, None, 1)
+    k, v = cache
+    kb, vb = k.data_ptr(), v.data_ptr()
+    lib = kv._lib      # the HIP runtime the library and torch share
+    copy1 = lib.hipMemcpyAsync
+    copy1.restype = ctypes.c_int
+    copy1.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                      ctypes.c_void_p]
+    copy2 = lib.hipMemcpy2DAsync
+    copy2.restype = ctypes.c_int
+    copy2.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                      ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    noop = lib.hipPeekAtLastError
+    noop.restype, noop.argtypes = ctypes.c_int, []
+    d2h = 2                                   # hipMemcpyDeviceToHost
+    s = torch.cuda.Stream()
+    sh = s.cuda_stream
+    st = torch.empty(slot // 2, dtype=torch.int16, device="cuda")
+    hosts = {name: _pinned(torch, slot) for name in ("buffered", "per_piece", "per_head")}
+    for h_ in hosts.values():
+        h_.zero_()
+    # (host offset, cache address) of every head's key and value run; the
+    # packed place of (layer l, K|V, row b, head h) for one token per row
+    runs = []
+    for l in range(L):
+        for b in range(B):
+            for h in range(H):
+                unit = (l * B + b) * H + h
+                ko = ((2 * l) * H * B + H * b + h) * D * P
+                vo = ((2 * l + 1) * H * B + H * b + h) * D * P
+                runs.append((ko, kb + (unit * C * S + pos[b]) * 16,
+                             vo, vb + (unit * S + pos[b]) * D * P))
+    # every copy stays inside its buffers
+    assert max(r[2] for r in runs) + D * P <= slot and max(r[0] for r in runs) + D * P <= slot
+    assert max(r[1] for r in runs) + ((C - 1) * S + 1) * 16 <= kb + lay.k_bytes
+    assert min(r[1] for r in runs) >= kb and min(r[3] for r in runs) >= vb
+    assert max(r[3] for r in runs) + D * P <= vb + lay.v_bytes
+    n_piece, n_head = len(runs) * (C + 1), len(runs) * 2
+    torch.cuda.synchronize()
+
+    def buffered():
+        kv.kv_pack_tokens(lay, k, v, 0, L, pos, None, st, slot, s)
+        return copy1(hosts["buffered"].data_ptr(), st.data_ptr(), slot, d2h, sh)
+
+    def per_piece():
+        hb, bad = hosts["per_piece"].data_ptr(), 0
+        for ko, ks, vo, vs in runs:
+            for c in range(C):
+                bad |= copy1(hb + ko + c * 16, ks + c * S * 16, 16, d2h, sh)
+            bad |= copy1(hb + vo, vs, D * P, d2h, sh)
+        return bad
+
+    def per_head():
+        hb, bad = hosts["per_head"].data_ptr(), 0
+        for ko, ks, vo, vs in runs:
+            bad |= copy2(hb + ko, 16, ks, S * 16, 16, C, d2h, sh)
+            bad |= copy1(hb + vo, vs, D * P, d2h, sh)
+        return bad
+
+    out = {"bytes_per_step": slot, "copies_per_step": {"buffered": 1, "per_piece": n_piece,
+                                                       "per_head": n_head}}
+    for name, fn in (("buffered", buffered), ("per_piece", per_piece), ("per_head", per_head)):
+        if out["copies_per_step"][name] > max_copies:
+            continue
+        best = None
+        for _ in range(reps + 1):                  # the first pass warms up
+            t0 = time.perf_counter()
+            rc = fn()
+            t1 = time.perf_counter()
+            s.synchronize()
+            t2 = time.perf_counter()
+            if rc:
+                raise RuntimeError(f"buffered_vs_naive: a {name} copy failed (hipError {rc})")
+            if best is None or t2 - t0 < best[0]:
+                best = (t2 - t0, t1 - t0)
+        out[f"{name}_us"] = round(best[0] * 1e6, 1)
+        out[f"{name}_issue_us"] = round(best[1] * 1e6, 1)
+    t0 = time.perf_counter()
+    for _ in range(n_head):
+        noop()
+    out["ctypes_us_per_call"] = round((time.perf_counter() - t0) / n_head * 1e6, 3)
+    for name in ("per_piece", "per_head"):
+        if f"{name}_us" in out:
+            out[f"gain_over_{name}"] = round(out[f"{name}_us"] / out["buffered_us"], 1)
+            if not torch.equal(hosts[name], hosts["buffered"]):
+                raise RuntimeError(f"buffered_vs_naive: the {name} host image differs")
+    out["host_images_equal"] = True
+    if keep_image:
+        out["image"] = hosts["buffered"]
+    del st, hosts
+    return out
+
+
 def decode_step_us(step, kv, reps=3):
     """GPU time per decode step of the workload's decode steps, with a ring of
     one bank holding them all (no bank reuse, so no wait for a flush copy):
@@ -1688,6 +1804,7 @@ def main():
         if isinstance(step, StreamStep):
             detail["decode_step_us"] = decode_step_us(step, kv)
             detail["decode_loop"] = decode_loop(step, kv, step.caches["B"])
+            detail["buffered_vs_naive"] = buffered_vs_naive(step, kv, step.caches["B"])
             detail["large_slices"] = large_slices(step, kv)
             if step.w.B * step.w.Smax >= 4096:
                 detail["paged_slices"] = paged_slices(step, kv)
@@ -1699,9 +1816,11 @@ def main():
             detail["layer_slices"] = layer_slices(step, kv, step.A, step.row_start,
                                                   step.row_count)
             detail["decode_loop"] = decode_loop(step, kv, step.A)
+            detail["buffered_vs_naive"] = buffered_vs_naive(step, kv, step.A)
         if isinstance(step, RingStep):
             detail["repartition_2x2"] = step.repartition(kv)
             detail["decode_loop"] = decode_loop(step, kv, step.A)
+            detail["buffered_vs_naive"] = buffered_vs_naive(step, kv, step.A)
         detail["hbm_copy_ceiling"] = hbm_copy_ceiling(torch, kv)
         progress("detail measured")
     cpu = None
@@ -1761,6 +1880,13 @@ def main():
                            "same_9_GiB_at_this_link_GBps": d2h,
                            "same_9_GiB_ms_one_link": round(one, 1),
                            "same_9_GiB_ms_8_links": round(one / 8, 1)}
+        naive = detail.get("buffered_vs_naive")
+        if naive:
+            line["context"]["pages_buffered_copy_gain_over_naive_copies"] = PAGES_BUFFERED_GAIN
+            for name in ("per_piece", "per_head"):
+                if f"gain_over_{name}" in naive:
+                    line["context"][f"this_gpu_decode_step_gain_over_{name}_copies"] = \
+                        naive[f"gain_over_{name}"]
     ceiling = detail.get("hbm_copy_ceiling")
     if ceiling and roofline:
         # the dominant kernel against what HBM gives a plain copy on this GPU

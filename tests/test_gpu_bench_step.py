@@ -233,3 +233,26 @@ def test_gqa_100k_long_step(bench):
             want = oracle.pack(one, Kl, Vl, 0, 1, p, [1] * B)
             got = ring[j * slot_w + l * lw:j * slot_w + (l + 1) * lw]
             assert np.array_equal(got, want), f"ring slot {j}, layer {l}"
+
+
+@pytest.mark.timeout(300)
+def test_buffered_vs_naive_copies(bench):
+    """A decode step sent to pinned host memory buffered (one pack, one copy)
+    and with one runtime copy per cache region: both host images equal the
+    oracle's pack of that step, and the buffered send is the faster."""
+    import synth
+
+    import kv_cache_streaming_amd as kv
+    w = synth.WORKLOADS["gpt2-small-tiny"]
+    note(f"buffered vs naive copies {w.name} dims={w.dims}")
+    step = bench.StreamStep(w, bench.DEFAULT_SWAP_BANK_MIB.get(w.name, 256) << 20,
+                            bench.TRANSPORTS["auto"])
+    r = bench.buffered_vs_naive(step, kv, step.caches["B"], reps=1, keep_image=True)
+    L, B, H, D, S = w.dims
+    assert r["copies_per_step"] == {"buffered": 1, "per_piece": L * B * H * (D // 8 + 1),
+                                    "per_head": 2 * L * B * H}
+    Bk, Bv = (words(t) for t in step.caches["B"])
+    want = oracle.pack(w.dims, Bk, Bv, 0, L, step.positions[0], [1] * B)
+    assert np.array_equal(host_words(r["image"], want.nbytes), want)
+    assert r["host_images_equal"]
+    assert r["gain_over_per_piece"] > 1 and r["gain_over_per_head"] > 1, r
