@@ -31,7 +31,8 @@ and counted-traffic rates against HBM peak and, with the detail, against
 the plain-copy ceiling); `context` puts the pages' own figures beside the
 measured link; `detail` holds every kernel's launches and rates and the
 isolated measurements (link and HBM copy ceilings, large slices, decode
-loops, a decode step sent buffered against one copy call per region, the
+loops, a decode step sent buffered against one copy call per region,
+layer-by-layer prompt streaming against streaming after the prompt, the
 microbatch schedule, the 2 x 2 repartition).
 
 `--workload` selects the other shapes, each with the step its class below
@@ -72,12 +73,14 @@ METRIC = "KV pack/unpack GB/s (% HBM peak) + swap host-link GB/s, 1 MI355X"
 # The pages' own figures around this path (other hardware; context, not targets):
 # DejaVu's serving throughput over FasterTransformer, the estimate of one
 # 2048-token OPT-175B prompt-KV transfer (9 GiB) over eight PCIe 5.0 x16 links,
-# and the gain of buffered copies over one copy call per small region when
-# streaming a request's cache out (prompt 500, 500 new tokens).
+# the gain of buffered copies over one copy call per small region when
+# streaming a request's cache out (prompt 500, 500 new tokens), and the further
+# gain of streaming layer by layer and overlapping it with compute.
 PAGES_THROUGHPUT_VS_FT = "1.88x (OPT-66B), 2x (BLOOM-176B): system throughput on A100-80GB / V100-16GB clusters"
 PAGES_OPT175B_KV_BYTES = 2048 * 4.5 * (1 << 20)   # 2048 tokens x 4.5 MiB
 PAGES_OPT175B_ESTIMATE_MS = 17.6                  # over 8 links of 64 GB/s
 PAGES_BUFFERED_GAIN = "95x: buffered copies over many small copy calls, streaming to remote CPU memory"
+PAGES_OVERLAP_GAIN = "1.4x more: layer-by-layer prompt streaming and token streaming overlapped with compute"
 HBM_PEAK_GBPS = 8000.0
 PCIE_PEAK_GBPS = 63.0          # PCIe 5.0 x16, per direction
 
@@ -1363,6 +1366,65 @@ def buffered_vs_naive(step, kv, cache, reps=3, max_copies=200_000, keep_image=Fa
     return out
 
 
+def prompt_overlap(step, kv, reps=2):
+    """Layer-by-layer prompt streaming against streaming once the prompt is
+    done.  The pages give no per-layer compute time, so a timed busy-wait of
+    t on a compute stream plays each layer's compute, with t set to fractions
+    of x, the per-layer transfer time measured alone.  Overlapped: layer l's
+    busy-wait, then kv_stream_prompt_layer(l) on the same stream; its pack
+    follows the layer's compute, and its copy runs on the copy stream while
+    layer l+1 computes.  After: all L busy-waits, then the L layers streamed.
+    Times are wall time from the first call until the last copy has landed,
+    best of `reps`.  `ideal_ms` is L*max(t, x) + min(t, x), a pipeline of L
+    stages."""
+    torch, w = step.torch, step.w
+    L, A, lp, eng = w.L, step.caches["A"], step.layer_prompt, step.eng_p
+    host = step.host_p[0].data_ptr()
+    c = torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(c):
+        torch.cuda._sleep(1000)
+        e0.record(c)
+        torch.cuda._sleep(2_000_000)
+        e1.record(c)
+    torch.cuda.synchronize()
+    cycles_per_ms = 2_000_000 / e0.elapsed_time(e1)
+
+    def stream(l):
+        eng.stream_prompt_layer(A[0], A[1], l, 0, step.prompt, None, host + l * lp, lp, c)
+
+    def run(t_ms, overlap):
+        cyc = int(t_ms * cycles_per_ms)
+        best = None
+        for _ in range(reps + 1):                  # the first pass warms up
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            with torch.cuda.stream(c):
+                for l in range(L):
+                    if cyc:
+                        torch.cuda._sleep(cyc)
+                    if overlap:
+                        stream(l)
+                if not overlap:
+                    for l in range(L):
+                        stream(l)
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) * 1000
+            best = dt if best is None else min(best, dt)
+        return best
+
+    x = run(0.0, True) / L
+    out = {"layers": L, "layer_bytes": lp, "transfer_ms_per_layer": round(x, 3), "rows": []}
+    for f in (0.5, 1.0, 2.0):
+        t = f * x
+        after, over = run(t, False), run(t, True)
+        out["rows"].append({"compute_ms_per_layer": round(t, 3), "after_ms": round(after, 2),
+                            "overlapped_ms": round(over, 2),
+                            "ideal_ms": round(L * max(t, x) + min(t, x), 2),
+                            "gain": round(after / over, 2)})
+    return out
+
+
 def decode_step_us(step, kv, reps=3):
     """GPU time per decode step of the workload's decode steps, with a ring of
     one bank holding them all (no bank reuse, so no wait for a flush copy):
@@ -1805,6 +1867,7 @@ def main():
             detail["decode_step_us"] = decode_step_us(step, kv)
             detail["decode_loop"] = decode_loop(step, kv, step.caches["B"])
             detail["buffered_vs_naive"] = buffered_vs_naive(step, kv, step.caches["B"])
+            detail["prompt_overlap"] = prompt_overlap(step, kv)
             detail["large_slices"] = large_slices(step, kv)
             if step.w.B * step.w.Smax >= 4096:
                 detail["paged_slices"] = paged_slices(step, kv)
@@ -1880,6 +1943,10 @@ def main():
                            "same_9_GiB_at_this_link_GBps": d2h,
                            "same_9_GiB_ms_one_link": round(one, 1),
                            "same_9_GiB_ms_8_links": round(one / 8, 1)}
+        lap = detail.get("prompt_overlap")
+        if lap:
+            line["context"]["pages_layer_streaming_and_overlap_gain"] = PAGES_OVERLAP_GAIN
+            line["context"]["this_gpu_prompt_overlap_gain_at_equal_compute"] = lap["rows"][1]["gain"]
         naive = detail.get("buffered_vs_naive")
         if naive:
             line["context"]["pages_buffered_copy_gain_over_naive_copies"] = PAGES_BUFFERED_GAIN

@@ -256,3 +256,26 @@ def test_buffered_vs_naive_copies(bench):
     assert np.array_equal(host_words(r["image"], want.nbytes), want)
     assert r["host_images_equal"]
     assert r["gain_over_per_piece"] > 1 and r["gain_over_per_head"] > 1, r
+
+
+@pytest.mark.timeout(600)
+def test_prompt_overlap(bench):
+    """Layer-by-layer prompt streaming of GPT-2-1.5B against streaming after
+    the prompt, with a busy-wait per layer as its compute: the streamed image
+    equals the oracle's layers, and at compute equal to the transfer the
+    overlap saves time."""
+    import synth
+
+    import kv_cache_streaming_amd as kv
+    w = synth.WORKLOADS["gpt2-1.5b"]
+    name = bench.DEFAULT_TRANSPORT[w.name]
+    note(f"prompt overlap {w.name} dims={w.dims} transport={name}")
+    step = bench.StreamStep(w, 256 << 20, bench.TRANSPORTS[name])
+    r = bench.prompt_overlap(step, kv, reps=1)
+    L = w.L
+    A = [words(t) for t in step.caches["A"]]
+    check_layers(w.dims, A[0], A[1], step.rows_prompt,
+                 host_words(step.host_p[0], L * step.layer_prompt), step.layer_prompt,
+                 "prompt streamed layer by layer")
+    equal = r["rows"][1]
+    assert equal["overlapped_ms"] < equal["after_ms"] / 1.3, r
