@@ -32,8 +32,9 @@ the plain-copy ceiling); `context` puts the pages' own figures beside the
 measured link; `detail` holds every kernel's launches and rates and the
 isolated measurements (link and HBM copy ceilings, large slices, decode
 loops, a decode step sent buffered against one copy call per region,
-layer-by-layer prompt streaming against streaming after the prompt, the
-microbatch schedule, the 2 x 2 repartition).
+layer-by-layer prompt streaming against streaming after the prompt, decode
+steps streamed through the ring beside compute against compute that waits
+for each flush, the microbatch schedule, the 2 x 2 repartition).
 
 `--workload` selects the other shapes, each with the step its class below
 describes: gpt2-1.5b (StreamStep: prompt streaming of 48 layers beside the
@@ -1425,6 +1426,76 @@ def prompt_overlap(step, kv, reps=2):
     return out
 
 
+def token_overlap(step, kv, cache, reps=2, keep_image=False):
+    """Decode steps streamed through the staging ring while the next steps
+    compute, against compute that waits for each bank's flush.  A timed
+    busy-wait of t on the compute stream plays each decode step's compute.
+    The pages give no step time, so t is set so that a bank's R steps take
+    ½, 1 and 2 times x, the flush of one bank measured alone.  Overlapped:
+    each step's busy-wait, then kv_ring_push; a full bank is packed and
+    copied out on the copy stream while the next bank's steps compute.
+    Waiting: the same calls, but after each full bank the compute stream
+    waits for that bank's copy to land.  Times are wall time until the host
+    image is complete, best of `reps`.  `ideal_ms` is n·max(R·t, x) + min(R·t, x)
+    over the n banks.  `keep_image` returns the host image as `image`."""
+    torch, w, lay = step.torch, step.w, step.lay
+    R, positions = w.ring_slots, step.positions
+    nsteps = len(positions)
+    banks = nsteps // R
+    slot = kv.kv_pack_bytes(lay, lay.L, None, 1)
+    k, v = cache
+    c, cs = torch.cuda.Stream(), torch.cuda.Stream()
+    hostbuf = _pinned(torch, nsteps * slot)
+    ring = kv.KvRing(lay, R, _bank(torch, R * slot), _bank(torch, R * slot), hostbuf,
+                     copy_stream=cs)
+    ring.set_gather(kv.KV_RING_GATHER_AT_FLUSH)
+    landed = torch.cuda.Event()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(c):
+        torch.cuda._sleep(1000)
+        e0.record(c)
+        torch.cuda._sleep(2_000_000)
+        e1.record(c)
+    torch.cuda.synchronize()
+    cycles_per_ms = 2_000_000 / e0.elapsed_time(e1)
+
+    def run(t_ms, wait):
+        cyc = int(t_ms * cycles_per_ms)
+        best = None
+        for _ in range(reps + 1):                  # the first pass warms up
+            ring.reset()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            with torch.cuda.stream(c):
+                for j, pos in enumerate(positions[:banks * R]):
+                    if cyc:
+                        torch.cuda._sleep(cyc)
+                    ring.push(k, v, pos, c)
+                    if wait and (j + 1) % R == 0:
+                        ring.flush(c, landed)      # nothing left to copy: marks the bank's copy
+                        c.wait_event(landed)
+                ring.flush(c)
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) * 1000
+            best = dt if best is None else min(best, dt)
+        return best
+
+    x = run(0.0, True) / banks
+    out = {"steps": banks * R, "ring_slots": R, "bank_bytes": R * slot,
+           "flush_ms_per_bank": round(x, 3), "rows": []}
+    for f in (0.5, 1.0, 2.0):
+        t = f * x / R
+        waiting, over = run(t, True), run(t, False)
+        out["rows"].append({"compute_ms_per_step": round(t, 4), "waiting_ms": round(waiting, 2),
+                            "overlapped_ms": round(over, 2),
+                            "ideal_ms": round(banks * max(R * t, x) + min(R * t, x), 2),
+                            "gain": round(waiting / over, 2)})
+    ring.close()
+    if keep_image:
+        out["image"] = hostbuf
+    return out
+
+
 def decode_step_us(step, kv, reps=3):
     """GPU time per decode step of the workload's decode steps, with a ring of
     one bank holding them all (no bank reuse, so no wait for a flush copy):
@@ -1868,6 +1939,7 @@ def main():
             detail["decode_loop"] = decode_loop(step, kv, step.caches["B"])
             detail["buffered_vs_naive"] = buffered_vs_naive(step, kv, step.caches["B"])
             detail["prompt_overlap"] = prompt_overlap(step, kv)
+            detail["token_overlap"] = token_overlap(step, kv, step.caches["B"])
             detail["large_slices"] = large_slices(step, kv)
             if step.w.B * step.w.Smax >= 4096:
                 detail["paged_slices"] = paged_slices(step, kv)
@@ -1880,10 +1952,12 @@ def main():
                                                   step.row_count)
             detail["decode_loop"] = decode_loop(step, kv, step.A)
             detail["buffered_vs_naive"] = buffered_vs_naive(step, kv, step.A)
+            detail["token_overlap"] = token_overlap(step, kv, step.A)
         if isinstance(step, RingStep):
             detail["repartition_2x2"] = step.repartition(kv)
             detail["decode_loop"] = decode_loop(step, kv, step.A)
             detail["buffered_vs_naive"] = buffered_vs_naive(step, kv, step.A)
+            detail["token_overlap"] = token_overlap(step, kv, step.A)
         detail["hbm_copy_ceiling"] = hbm_copy_ceiling(torch, kv)
         progress("detail measured")
     cpu = None
@@ -1947,6 +2021,10 @@ def main():
         if lap:
             line["context"]["pages_layer_streaming_and_overlap_gain"] = PAGES_OVERLAP_GAIN
             line["context"]["this_gpu_prompt_overlap_gain_at_equal_compute"] = lap["rows"][1]["gain"]
+        tok = detail.get("token_overlap")
+        if tok:
+            line["context"]["pages_layer_streaming_and_overlap_gain"] = PAGES_OVERLAP_GAIN
+            line["context"]["this_gpu_token_overlap_gain_at_equal_compute"] = tok["rows"][1]["gain"]
         naive = detail.get("buffered_vs_naive")
         if naive:
             line["context"]["pages_buffered_copy_gain_over_naive_copies"] = PAGES_BUFFERED_GAIN

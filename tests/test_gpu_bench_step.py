@@ -259,11 +259,12 @@ def test_buffered_vs_naive_copies(bench):
 
 
 @pytest.mark.timeout(600)
-def test_prompt_overlap(bench):
+def test_prompt_and_token_overlap(bench):
     """Layer-by-layer prompt streaming of GPT-2-1.5B against streaming after
-    the prompt, with a busy-wait per layer as its compute: the streamed image
-    equals the oracle's layers, and at compute equal to the transfer the
-    overlap saves time."""
+    the prompt, and its decode steps streamed through the ring against
+    compute that waits for each flush, with busy-waits as the compute: the
+    streamed images equal the oracle's, and at compute equal to the transfer
+    the overlap saves time."""
     import synth
 
     import kv_cache_streaming_amd as kv
@@ -279,3 +280,13 @@ def test_prompt_overlap(bench):
                  "prompt streamed layer by layer")
     equal = r["rows"][1]
     assert equal["overlapped_ms"] < equal["after_ms"] / 1.3, r
+    del A
+    note(f"token overlap {w.name}")
+    t = bench.token_overlap(step, kv, step.caches["B"], reps=1, keep_image=True)
+    Bk, Bv = (words(x) for x in step.caches["B"])
+    n = t["steps"]
+    slots = [oracle.pack(w.dims, Bk, Bv, 0, L, p, [1] * w.B) for p in step.positions[:n]]
+    ring = oracle.ring_host(slots)
+    assert np.array_equal(host_words(t["image"], ring.nbytes), ring), "ring host image"
+    equal = t["rows"][1]
+    assert equal["overlapped_ms"] < equal["waiting_ms"] / 1.2, t
