@@ -28,8 +28,9 @@ oracle on a bounded sample of the same step (single-threaded; its
 `metric_parts` sets the metric's two figures side by side (host-link rates
 per direction against PCIe peak; the dominant kernel's algorithmic, payload
 and counted-traffic rates against HBM peak and, with the detail, against
-the plain-copy ceiling); `context` puts the pages' own figures beside the
-measured link; `detail` holds every kernel's launches and rates and the
+the plain-copy ceiling); `context` puts the pages' own figures beside what
+is measured here (the link's rate, and with the detail the gains of
+buffered copies and of streaming beside compute); `detail` holds every kernel's launches and rates and the
 isolated measurements (link and HBM copy ceilings, large slices, decode
 loops, a decode step sent buffered against one copy call per region,
 layer-by-layer prompt streaming against streaming after the prompt, decode
