@@ -169,3 +169,91 @@ def test_long_context_defaults(bench):
     finally:
         sys.argv = args
     assert a.workload == w and a.gpus == 1
+
+
+@pytest.mark.parametrize("workload", ["gpt2-small-tiny", "opt-66b-16l"])
+def test_naive_copies_land_where_the_pack_puts_them(bench, monkeypatch, workload):
+    """The naive side of buffered_vs_naive on the CPU: the runtime's copies
+    become memmoves between host tensors and the library's pack becomes the
+    oracle's, so every per-piece and per-head copy must stay inside its
+    buffers and the three host images must equal the oracle's pack of the
+    step (OPT-66B: the full-size shape, 156,672 copies)."""
+    import ctypes
+    import types
+
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    w = synth.WORKLOADS[workload]
+    L, B, H, D, S = w.dims
+    rng = np.random.default_rng(5)
+    n = L * B * H * D * S
+    K = rng.integers(0, 1 << 16, size=n, dtype=np.uint16)
+    V = rng.integers(0, 1 << 16, size=n, dtype=np.uint16)
+    k, v = torch.from_numpy(K.view(np.int16)), torch.from_numpy(V.view(np.int16))
+    live = [k, v]
+
+    def inside(p, nb):
+        return any(t.data_ptr() <= p and p + nb <= t.data_ptr() + t.numel() * 2 for t in live)
+
+    def copy1(dst, src, nb, kind, s):
+        assert kind == 2 and inside(src, nb) and inside(dst, nb)
+        ctypes.memmove(dst, src, nb)
+        return 0
+
+    def copy2(dst, dpitch, src, spitch, width, height, kind, s):
+        assert kind == 2
+        for i in range(height):
+            assert inside(src + i * spitch, width) and inside(dst + i * dpitch, width)
+            ctypes.memmove(dst + i * dpitch, src + i * spitch, width)
+        return 0
+
+    class Fn:                     # accepts the restype/argtypes the bench sets
+        def __init__(self, f):
+            self.f = f
+
+        def __call__(self, *a):
+            return self.f(*a)
+
+    class FakeStream:
+        cuda_stream = 1
+
+        def synchronize(self):
+            pass
+
+    class FakeTorch:
+        cuda = types.SimpleNamespace(Stream=FakeStream, synchronize=lambda: None)
+
+        def __getattr__(self, name):
+            return getattr(torch, name)
+
+        @staticmethod
+        def empty(*a, **kw):
+            kw.pop("device", None)
+            kw.pop("pin_memory", None)
+            t = torch.empty(*a, **kw)
+            live.append(t)
+            return t
+
+    pos = [int(p) for p in rng.integers(0, S, size=B)]
+    want = oracle.pack(w.dims, K.reshape(L, B, H, D // 8, S, 8), V.reshape(L, B, H, S, D),
+                       0, L, pos, [1] * B)
+
+    def pack(lay, k_, v_, l0, nl, start, count, st, nbytes, s):
+        st.numpy().view(np.uint16)[:] = want
+
+    lay = types.SimpleNamespace(L=L, B=B, H=H, D=D, Smax=S, k_bytes=2 * n, v_bytes=2 * n)
+    fkv = types.SimpleNamespace(
+        _lib=types.SimpleNamespace(hipMemcpyAsync=Fn(copy1), hipMemcpy2DAsync=Fn(copy2),
+                                   hipPeekAtLastError=Fn(lambda: 0)),
+        kv_pack_tokens=pack, kv_pack_bytes=lambda lay_, nl, c, u: 2 * nl * B * H * D * 2 * u)
+    monkeypatch.setattr(bench, "_pinned", lambda t, nb: FakeTorch.empty((nb + 1) // 2,
+                                                                        dtype=torch.int16))
+    step = types.SimpleNamespace(torch=FakeTorch(), lay=lay, positions=[pos])
+    r = bench.buffered_vs_naive(step, fkv, (k, v), reps=1, keep_image=True)
+    assert r["copies_per_step"] == {"buffered": 1, "per_piece": L * B * H * (D // 8 + 1),
+                                    "per_head": 2 * L * B * H}
+    assert r["host_images_equal"]
+    assert np.array_equal(r["image"].numpy().view(np.uint16), want)
